@@ -1,0 +1,185 @@
+"""Exact-attention oracle (fp64, CPU).
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the benchmark's
+CPU-baseline leg are the only users; the product path never imports this
+package, and this package imports nothing from the product.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, IEEE double, no
+fast-math).  This module only marshals arguments: it hands the raw 16-bit
+patterns of bf16/fp16 tensors and the mask's broadcast strides to the C code
+and returns numpy float64 arrays.
+
+What is computed (ffpa-attn "API Reference", ``ffpa_attn_func``): for every
+query row r of batch b and query head h, with kv head ``h // (Hq // Hkv)``,
+
+    logit_k = scale * <q_r, k_k> + bias(b, h, r, k)     (bias after scaling)
+    logit_k = -inf  if causal and k > r + (Nkv - Nq)     (tail-aligned causal)
+    LSE     = log(sum_k exp(logit_k))                     (natural log)
+    O_r     = sum_k exp(logit_k - LSE) * v_k
+
+``scale=None`` means 1/sqrt(D).  A boolean mask excludes keys whose entry is
+false.  A row with every key excluded gets O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+MASK_NONE, MASK_BOOL_U8, MASK_ADD_F32, MASK_ADD_BF16, MASK_ADD_FP16 = 0, 1, 2, 3, 4
+DT_BF16, DT_FP16 = 0, 1
+
+# Planted-mistake switches (only for the tests proving the pins discriminate).
+FAULT_NONE = 0
+FAULT_TOPLEFT_CAUSAL = 1
+FAULT_HEAD_MODULO = 2
+FAULT_MASK_BEFORE_SCALE = 3
+FAULT_LSE_LOG2 = 4
+FAULT_DROP_LAST_KEY = 5
+FAULT_V_TRANSPOSED = 6
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``attn_oracle.c`` into ``liboracle.so`` with gcc (no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_attn_rows.restype = ctypes.c_int
+    lib.oracle_attn_rows.argtypes = [p, p, p, p, ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                     ctypes.c_double, ctypes.c_int, ctypes.c_int, p, i64, p, p, p, ctypes.c_int,
+                                     ctypes.c_int]
+    lib.oracle_causal_visible.restype = i64
+    lib.oracle_causal_visible.argtypes = [i64, i64, i64]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def causal_visible(r: int, nq: int, nkv: int) -> int:
+    """Number of keys query row r sees under the tail-aligned causal rule."""
+    return int(_load().oracle_causal_visible(r, nq, nkv))
+
+
+def _bits16(t) -> np.ndarray:
+    """Raw 16-bit patterns of a bf16/fp16 torch tensor (or a uint16 numpy array)."""
+    if isinstance(t, np.ndarray):
+        if t.dtype != np.uint16:
+            raise TypeError("numpy inputs must hold raw uint16 bit patterns")
+        return np.ascontiguousarray(t)
+    import torch
+
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"oracle inputs must be bf16 or fp16, got {t.dtype}")
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if isinstance(t, np.ndarray):
+        raise TypeError("pass dtype= with numpy inputs")
+    return DT_FP16 if t.dtype == torch.float16 else DT_BF16
+
+
+def _mask_args(mask, B, Hq, Nq, Nkv):
+    """(array, kind, strides) for a torch mask broadcastable to [B, Hq, Nq, Nkv]."""
+    import torch
+
+    if mask is None:
+        return None, MASK_NONE, (0, 0, 0, 0)
+    m = mask.detach().cpu()
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    if m.dim() != 4:
+        raise ValueError("mask must have at most 4 dims")
+    for have, want in zip(m.shape, (B, Hq, Nq, Nkv)):
+        if have not in (1, want):
+            raise ValueError(f"mask shape {tuple(mask.shape)} does not broadcast to {(B, Hq, Nq, Nkv)}")
+    m = m.contiguous()
+    strides = [0 if m.shape[i] == 1 else m.stride(i) for i in range(4)]
+    if m.dtype == torch.bool:
+        arr, kind = m.to(torch.uint8).numpy(), MASK_BOOL_U8
+    elif m.dtype == torch.float32:
+        arr, kind = m.numpy(), MASK_ADD_F32
+    elif m.dtype == torch.bfloat16:
+        arr, kind = m.view(torch.int16).numpy().view(np.uint16), MASK_ADD_BF16
+    elif m.dtype == torch.float16:
+        arr, kind = m.view(torch.int16).numpy().view(np.uint16), MASK_ADD_FP16
+    else:
+        raise TypeError(f"unsupported mask dtype {m.dtype}")
+    return np.ascontiguousarray(arr), kind, tuple(strides)
+
+
+def attention_rows(q, k, v, rows: Sequence[int], mask=None, scale: Optional[float] = None, is_causal: bool = False,
+                   want_probs: bool = False, threads: int = 0, fault: int = FAULT_NONE):
+    """Selected rows of exact attention in fp64.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D] (torch bf16/fp16, any device).
+    rows: flat row indices ``(b * Hq + h) * Nq + r``.
+    Returns (O [n, D] float64, LSE [n] float64) or, with want_probs, also P [n, Nkv].
+    """
+    lib = _load()
+    B, Hq, Nq, D = (int(x) for x in q.shape)
+    Bk, Hkv, Nkv, Dk = (int(x) for x in k.shape)
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("q/k/v shapes are inconsistent")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    qb, kb, vb = _bits16(q), _bits16(k), _bits16(v)
+    dtype = _dtype_code(q)
+    if scale is None or (isinstance(scale, float) and math.isnan(scale)):
+        scale = 1.0 / math.sqrt(D)
+    marr, mkind, ms = _mask_args(mask, B, Hq, Nq, Nkv)
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows_arr.size
+    if n and (rows_arr.min() < 0 or rows_arr.max() >= B * Hq * Nq):
+        raise ValueError("row index out of range")
+    O = np.zeros((n, D), dtype=np.float64)
+    L = np.zeros((n,), dtype=np.float64)
+    P = np.zeros((n, Nkv), dtype=np.float64) if want_probs else None
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.oracle_attn_rows(ptr(qb), ptr(kb), ptr(vb), ptr(marr), mkind, ms[0], ms[1], ms[2], ms[3], B, Hq, Hkv,
+                              Nq, Nkv, D, float(scale), int(bool(is_causal)), dtype, ptr(rows_arr), n, ptr(O), ptr(L),
+                              ptr(P), int(threads), int(fault))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_rows failed with code {rc}")
+    return (O, L, P) if want_probs else (O, L)
+
+
+def attention(q, k, v, mask=None, scale: Optional[float] = None, is_causal: bool = False, threads: int = 0,
+              fault: int = FAULT_NONE):
+    """All rows: returns O [B, Hq, Nq, D] and LSE [B, Hq, Nq] as float64 numpy arrays."""
+    B, Hq, Nq, D = (int(x) for x in q.shape)
+    O, L = attention_rows(q, k, v, np.arange(B * Hq * Nq), mask=mask, scale=scale, is_causal=is_causal,
+                          threads=threads, fault=fault)
+    return O.reshape(B, Hq, Nq, D), L.reshape(B, Hq, Nq)
