@@ -1,0 +1,167 @@
+"""MI355X (gfx950) exact large-head-dim attention forward.
+
+``attn`` computes O = softmax(scale * Q K^T + mask) V and, on request, the fp32 natural-log LSE,
+with the semantics of ffpa_attn_func on the ffpa-attn "API Reference" page: SDPA-style layout
+[B, H, N, D], GQA/MQA through enable_gqa, cross-attention (Nq != Nkv), tail-aligned causal masking
+(row r sees keys k <= r + Nkv - Nq, requiring Nkv >= Nq), boolean masks (True takes part) and
+additive floating masks, and scale = 1/sqrt(D) by default.
+
+Everything here is argument marshalling around the C ABI of ``libffpa.so`` (include/ffpa.h):
+tensors are passed by device pointer, outputs are allocated with torch, and the work is enqueued
+on torch's current HIP stream.  There is no fallback path: if the library is missing, importing
+works but every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["attn", "ffpa_fwd", "ffpa_check_args", "library", "rows_per_block", "FFPA_BF16", "FFPA_FP16",
+           "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libffpa.so")
+
+FFPA_BF16, FFPA_FP16 = 0, 1
+MASK_NONE, MASK_BOOL_U8, MASK_ADD_F32, MASK_ADD_BF16, MASK_ADD_FP16 = 0, 1, 2, 3, 4
+OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
+
+EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block")
+
+
+class MaskDesc(ctypes.Structure):
+    """ffpa_mask_t: element (b, h, r, k) at data + b*stride_b + h*stride_h + r*stride_q + k*stride_k."""
+    _fields_ = [("data", ctypes.c_void_p), ("kind", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libffpa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with exact_attention_head_amd/build.py "
+                           "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, p, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    args = [p, p, p, ctypes.POINTER(MaskDesc), p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32]
+    lib.ffpa_fwd.argtypes = args + [p]
+    lib.ffpa_fwd.restype = i32
+    lib.ffpa_check_args.argtypes = args
+    lib.ffpa_check_args.restype = i32
+    lib.ffpa_status_string.argtypes = [i32]
+    lib.ffpa_status_string.restype = ctypes.c_char_p
+    lib.ffpa_last_error_detail.argtypes = []
+    lib.ffpa_last_error_detail.restype = ctypes.c_char_p
+    lib.ffpa_rows_per_block.argtypes = [i64]
+    lib.ffpa_rows_per_block.restype = i32
+    _lib = lib
+    return lib
+
+
+def _raise(status: int) -> None:
+    lib = library()
+    detail = lib.ffpa_last_error_detail().decode()
+    name = lib.ffpa_status_string(status).decode()
+    msg = f"ffpa: {name}: {detail}" if detail else f"ffpa: {name}"
+    raise {ERR_TYPE: TypeError, ERR_VALUE: ValueError, ERR_UNSUPPORTED: NotImplementedError}.get(status,
+                                                                                                 RuntimeError)(msg)
+
+
+def ffpa_fwd(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype,
+             stream) -> int:
+    """The raw C entry point: pointers are integers (device addresses), returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_fwd(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale), int(is_causal),
+                              dtype, stream)
+
+
+def ffpa_check_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal,
+                    dtype) -> int:
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_check_args(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
+                                     int(is_causal), dtype)
+
+
+def rows_per_block(D: int) -> int:
+    return int(library().ffpa_rows_per_block(D))
+
+
+def _mask_desc(attn_mask, B, Hq, Nq, Nkv):
+    """MaskDesc for a torch mask broadcastable to [B, Hq, Nq, Nkv] (plus the tensor to keep alive)."""
+    import torch
+
+    kinds = {torch.bool: MASK_BOOL_U8, torch.float32: MASK_ADD_F32, torch.bfloat16: MASK_ADD_BF16,
+             torch.float16: MASK_ADD_FP16}
+    if attn_mask.dtype not in kinds:
+        raise TypeError(f"attn_mask dtype {attn_mask.dtype} is not bool, float32, bfloat16 or float16")
+    m = attn_mask
+    if m.dim() > 4:
+        raise ValueError("attn_mask has more than 4 dims")
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    for have, want in zip(m.shape, (B, Hq, Nq, Nkv)):
+        if have not in (1, want):
+            raise ValueError(f"attn_mask of shape {tuple(attn_mask.shape)} is not broadcastable to "
+                             f"{(B, Hq, Nq, Nkv)}")
+    if m.shape[3] != Nkv or m.stride(3) != 1:
+        # keys must be contiguous in memory: lay the mask out densely in its own (broadcast) shape
+        m = m.expand(m.shape[0], m.shape[1], m.shape[2], Nkv).contiguous()
+    strides = [0 if m.shape[i] == 1 else m.stride(i) for i in range(3)]
+    desc = MaskDesc(m.data_ptr(), kinds[m.dtype], strides[0], strides[1], strides[2], 1)
+    return desc, m
+
+
+def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False,
+         scale: Optional[float] = None, enable_gqa: bool = False, return_lse: bool = False, out=None):
+    """SDPA-aligned forward.  query [B, Hq, Nq, D]; key/value [B, Hkv, Nkv, D]; bf16 or fp16.
+
+    Returns O [B, Hq, Nq, D] (dtype of query), or (O, LSE [B, Hq, Nq] float32) with return_lse.
+    """
+    import torch
+
+    if dropout_p != 0.0:
+        raise NotImplementedError("attention dropout is not implemented (dropout_p must be 0)")
+    for name, t in (("query", query), ("key", key), ("value", value)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, H, N, D]")
+    if query.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"query dtype {query.dtype} is neither bfloat16 nor float16")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise TypeError("query, key and value must share one dtype")
+    if not (query.is_cuda and key.device == query.device and value.device == query.device):
+        raise ValueError("query, key and value must live on the same GPU")
+    B, Hq, Nq, D = query.shape
+    Bk, Hkv, Nkv, Dk = key.shape
+    if tuple(value.shape) != tuple(key.shape):
+        raise ValueError("key and value must share [B, Hkv, Nkv, D]")
+    if Bk != B or Dk != D:
+        raise ValueError("query and key disagree on batch or head dim")
+    if Hq != Hkv and not enable_gqa:
+        raise ValueError("Hq != Hkv needs enable_gqa=True")
+    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+    dtype = FFPA_BF16 if query.dtype == torch.bfloat16 else FFPA_FP16
+    if out is None:
+        o = torch.empty((B, Hq, Nq, D), dtype=query.dtype, device=query.device)
+    else:
+        if tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != query.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, Hq, Nq, D] tensor of the query dtype")
+        o = out
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=query.device) if return_lse else None
+    desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(query.device), B, Hq, Nq, Nkv)
+    sc = math.nan if scale is None else float(scale)
+    with torch.cuda.device(query.device):
+        stream = torch.cuda.current_stream(query.device).cuda_stream
+        st = ffpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(),
+                      lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal),
+                      dtype, stream)
+    del keep
+    if st != OK:
+        _raise(st)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,95 @@
+"""Builds libffpa.so in-tree: hipcc for gfx950, one object per (element type, head dim) kernel,
+compiled in parallel, plus the C-ABI object, linked into exact_attention_head_amd/libffpa.so."""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import re
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libffpa.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          # no packed-fp32 instructions in generated code
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-Wall", "-Wno-unused-result", "-I", os.path.join(PKG, "..", "include")]
+
+
+def head_dims() -> list[int]:
+    with open(os.path.join(CSRC, "ffpa_launch.hpp")) as f:
+        txt = f.read()
+    body = txt[txt.index("#define FFPA_FOR_EACH_D(X)"):]
+    body = body[:body.index("\n\n")]
+    return [int(x) for x in re.findall(r"X\((\d+)\)", body)]
+
+
+def _compile(src: str, obj: str, defines: list[str], remarks: bool) -> tuple[str, str]:
+    cmd = [HIPCC, *COMMON, *defines, "-c", src, "-o", obj]
+    if remarks:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {os.path.basename(obj)}:\n{r.stderr[-4000:]}")
+    return obj, r.stderr
+
+
+def resource_summary(stderr: str) -> dict:
+    """Parses -Rpass-analysis=kernel-resource-usage remarks (VGPRs, AGPRs, spills, LDS)."""
+    out = {}
+    for key, pat in [("vgpr", r"VGPRs: (\d+)"), ("agpr", r"AGPRs: (\d+)"), ("vgpr_spill", r"VGPRs Spill: (\d+)"),
+                     ("sgpr_spill", r"SGPRs Spill: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                     ("lds", r"LDS Size \[bytes/block\]: (\d+)"), ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")]:
+        m = re.search(pat, stderr)
+        if m:
+            out[key] = int(m.group(1))
+    return out
+
+
+def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -> str:
+    """Compiles every kernel and links libffpa.so; returns its path.  Always rebuilds."""
+    t0 = time.time()
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = jobs or max(1, min(16, os.cpu_count() or 4))
+    tasks = [(os.path.join(CSRC, "ffpa_api.hip"), os.path.join(BUILD, "ffpa_api.o"), [])]
+    for tag in ("Bf16", "Fp16"):
+        for d in head_dims():
+            tasks.append((os.path.join(CSRC, "ffpa_inst.hip"), os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}.o"),
+                          [f"-DFFPA_INST_T={tag}", f"-DFFPA_INST_D={d}"]))
+    # largest kernels first
+    tasks.sort(key=lambda t: -int(re.search(r"_d(\d+)", t[1]).group(1)) if "_d" in t[1] else 0)
+    resources = {}
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_compile, s, o, d, report) for s, o, d in tasks]
+        for f in cf.as_completed(futs):
+            obj, err = f.result()
+            if report and "_d" in obj:
+                resources[os.path.basename(obj)[:-2]] = resource_summary(err)
+    objs = [o for _, o, _ in tasks]
+    tmp = LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"[build] {LIB} ({len(objs)} objects, {time.time() - t0:.0f}s, {jobs} jobs)", flush=True)
+    if report:
+        for k in sorted(resources, key=lambda s: (s.split("_")[1], int(s.split("_d")[1]))):
+            print(f"[build] {k}: {resources[k]}", flush=True)
+    return LIB
+
+
+def clean() -> None:
+    shutil.rmtree(BUILD, ignore_errors=True)
+
+
+if __name__ == "__main__":
+    build(report="--report" in sys.argv)

@@ -1,0 +1,192 @@
+// C ABI of the attention forward (declared in include/ffpa.h): argument checking, the dispatch
+// to the per-head-dim kernels, and status reporting.  Argument rules follow the ffpa-attn "API
+// Reference" page, ffpa_attn_func: dtype fp16/bf16 (else TypeError), key/value sharing Nh_kv and
+// Nkv with Nh_q a multiple of Nh_kv, causal only with Nkv >= Nq (else ValueError), and a
+// NotImplementedError class for valid requests outside what the kernels cover.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ffpa.h"
+#include "ffpa_kernel.hpp"
+#include "ffpa_launch.hpp"
+
+namespace {
+
+thread_local char g_detail[256];
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t mask_elem_size(int kind) {
+  switch (kind) {
+    case FFPA_MASK_BOOL_U8: return 1;
+    case FFPA_MASK_ADD_F32: return 4;
+    case FFPA_MASK_ADD_BF16:
+    case FFPA_MASK_ADD_FP16: return 2;
+    default: return 0;
+  }
+}
+
+// Rows per workgroup of the kernel for head dim D, 0 if D has no kernel.
+int rows_for(int64_t D) {
+  switch (D) {
+#define FFPA_ROWS_CASE(Dv) \
+  case Dv: return ffpa::FwdKernel<ffpa::Bf16, Dv>::BR;
+    FFPA_FOR_EACH_D(FFPA_ROWS_CASE)
+#undef FFPA_ROWS_CASE
+    default: return 0;
+  }
+}
+
+int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o, const float* lse,
+          int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
+          int dtype) {
+  g_detail[0] = '\0';
+  if (dtype != FFPA_BF16 && dtype != FFPA_FP16) return fail(FFPA_ERR_TYPE, "dtype %d is neither bf16 nor fp16", dtype);
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
+    return fail(FFPA_ERR_VALUE, "every size must be >= 1 (B=%lld Hq=%lld Hkv=%lld Nq=%lld Nkv=%lld D=%lld)",
+                (long long)B, (long long)Hq, (long long)Hkv, (long long)Nq, (long long)Nkv, (long long)D);
+  if (Hq % Hkv != 0)
+    return fail(FFPA_ERR_VALUE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (is_causal != 0 && is_causal != 1) return fail(FFPA_ERR_VALUE, "is_causal must be 0 or 1");
+  if (is_causal && Nkv < Nq)
+    return fail(FFPA_ERR_VALUE, "causal attention needs Nkv >= Nq (Nq=%lld, Nkv=%lld)", (long long)Nq, (long long)Nkv);
+  if (std::isinf(scale)) return fail(FFPA_ERR_VALUE, "scale must be finite (NaN selects 1/sqrt(D))");
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(FFPA_ERR_VALUE, "q, k, v and o must be non-null");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
+  if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
+  if (D < 64 || D > 1024 || D % 64 != 0)
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
+  // grid size and 32-bit in-kernel indexing
+  const int br = rows_for(D);
+  const int64_t nqt = (Nq + br - 1) / br;
+  if (B * Hq * nqt > 0x7fffffffLL) return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
+  if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B * Hq > (1LL << 30) || B * Hkv > (1LL << 30))
+    return fail(FFPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit row indexing of the kernels");
+  if (Nq * D * 2 >= (1LL << 31) || Nkv * D * 2 >= (1LL << 31))
+    return fail(FFPA_ERR_UNSUPPORTED, "one head of Q or K/V must stay below 2 GiB (buffer addressing)");
+  const size_t esz = 2;
+  const size_t qbytes = (size_t)(B * Hq * Nq * D) * esz, kvbytes = (size_t)(B * Hkv * Nkv * D) * esz;
+  const size_t obytes = qbytes, lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kvbytes) ||
+      ranges_overlap(o, obytes, v, kvbytes) || ranges_overlap(o, obytes, lse, lbytes))
+    return fail(FFPA_ERR_VALUE, "o must not overlap q, k, v or lse");
+  if (lse != nullptr && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+                         ranges_overlap(lse, lbytes, v, kvbytes)))
+    return fail(FFPA_ERR_VALUE, "lse must not overlap q, k or v");
+  if (mask != nullptr) {
+    if (mask->kind == FFPA_MASK_NONE) {
+      // a descriptor that says "no mask"
+    } else {
+      const size_t msz = mask_elem_size(mask->kind);
+      if (msz == 0) return fail(FFPA_ERR_TYPE, "unknown mask kind %d", (int)mask->kind);
+      if (mask->data == nullptr) return fail(FFPA_ERR_VALUE, "mask data is null");
+      if (is_causal) return fail(FFPA_ERR_VALUE, "an explicit mask cannot be combined with is_causal");
+      if (mask->stride_k != 1) return fail(FFPA_ERR_UNSUPPORTED, "mask stride_k must be 1");
+      if (mask->stride_b < 0 || mask->stride_h < 0 || mask->stride_q < 0)
+        return fail(FFPA_ERR_VALUE, "mask strides must be >= 0");
+      if ((uintptr_t)mask->data % msz) return fail(FFPA_ERR_VALUE, "mask data misaligned for its element type");
+      const int64_t last = (B - 1) * mask->stride_b + (Hq - 1) * mask->stride_h + (Nq - 1) * mask->stride_q + Nkv;
+      if (last > (1LL << 62) / (int64_t)msz) return fail(FFPA_ERR_UNSUPPORTED, "mask too large");
+      const size_t mbytes = (size_t)last * msz;
+      if (ranges_overlap(o, obytes, mask->data, mbytes) || ranges_overlap(lse, lbytes, mask->data, mbytes))
+        return fail(FFPA_ERR_VALUE, "o and lse must not overlap the mask");
+    }
+  }
+  return FFPA_OK;
+}
+
+template <typename T>
+hipError_t dispatch(int64_t D, const ffpa::FwdArgs& a, hipStream_t s) {
+  switch (D) {
+#define FFPA_DISPATCH_CASE(Dv) \
+  case Dv: return ffpa::launch_fwd<T, Dv>(a, s);
+    FFPA_FOR_EACH_D(FFPA_DISPATCH_CASE)
+#undef FFPA_DISPATCH_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffpa_check_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                    const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                    float scale, int is_causal, int dtype) {
+  return check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+}
+
+int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse, int64_t B,
+             int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype,
+             void* stream) {
+  const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  ffpa::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.mask_kind = ffpa::kMaskNone;
+  if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
+    const size_t msz = mask_elem_size(mask->kind);
+    a.mask = mask->data;
+    a.mask_kind = mask->kind;  // the enum values match ffpa::MaskKind
+    a.msb = mask->stride_b;
+    a.msh = mask->stride_h;
+    a.msq = mask->stride_q;
+    // four consecutive keys form one aligned vector load when every row start is 4-element aligned
+    const bool aligned = ((uintptr_t)mask->data % (4 * msz)) == 0;
+    a.mask_vec = aligned && (a.msb % 4 == 0) && (a.msh % 4 == 0) && (a.msq % 4 == 0);
+  }
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Nq = (int)Nq;
+  a.Nkv = (int)Nkv;
+  a.group = (int)(Hq / Hkv);
+  const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.causal = is_causal;
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FFPA_OK;
+}
+
+const char* ffpa_status_string(int status) {
+  switch (status) {
+    case FFPA_OK: return "ok";
+    case FFPA_ERR_TYPE: return "type error";
+    case FFPA_ERR_VALUE: return "value error";
+    case FFPA_ERR_UNSUPPORTED: return "not supported";
+    case FFPA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ffpa_last_error_detail(void) { return g_detail; }
+
+int ffpa_rows_per_block(int64_t D) { return rows_for(D); }
+
+}  // extern "C"

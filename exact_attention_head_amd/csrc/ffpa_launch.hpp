@@ -1,0 +1,26 @@
+// Launchers of the forward kernel, one per (element type, head dim).  They are explicitly
+// instantiated in the ffpa_inst_*.hip files so the kernels compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace ffpa {
+
+struct FwdArgs;
+struct Bf16;
+struct Fp16;
+
+template <typename T, int D>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Head dims with a compiled kernel: 64, 128, ..., 1024.
+#define FFPA_FOR_EACH_D(X) \
+  X(64) X(128) X(192) X(256) X(320) X(384) X(448) X(512) X(576) X(640) X(704) X(768) X(832) X(896) X(960) X(1024)
+
+#define FFPA_DECLARE(Dv)                                                        \
+  extern template hipError_t launch_fwd<Bf16, Dv>(const FwdArgs&, hipStream_t); \
+  extern template hipError_t launch_fwd<Fp16, Dv>(const FwdArgs&, hipStream_t);
+FFPA_FOR_EACH_D(FFPA_DECLARE)
+#undef FFPA_DECLARE
+
+}  // namespace ffpa

@@ -1,0 +1,116 @@
+/*
+ * ffpa.h -- C ABI of the MI355X (gfx950) exact large-head-dim attention forward.
+ *
+ * The operation is the one the ffpa-attn "API Reference" (readthedocs) page
+ * defines for ffpa_attn_func, restated here:
+ *
+ *   O[b,h,r,:] = sum_k softmax_k( scale * <Q[b,h,r,:], K[b,g(h),k,:]> + mask[b,h,r,k] ) * V[b,g(h),k,:]
+ *   LSE[b,h,r] = log( sum_k exp( scale * <Q[b,h,r,:], K[b,g(h),k,:]> + mask[b,h,r,k] ) )
+ *
+ * with g(h) = h / (Hq / Hkv) (grouped-query and multi-query heads: page
+ * parameter "key", group_size = Nh_q / Nh_kv), the tail-aligned causal rule
+ * of parameter "is_causal" (row r sees key k only when k <= r + Nkv - Nq,
+ * which needs Nkv >= Nq), the mask of parameter "attn_mask" (a boolean entry
+ * that is true takes part, a false one is excluded; a floating entry is an
+ * additive bias, added after scaling), and scale = 1/sqrt(D) when not given
+ * (parameter "scale").  The natural-log LSE follows the fp32 log-sum-exp that
+ * the page's varlen entry returns.  A row whose keys are all excluded gets
+ * O = 0 and LSE = -inf.
+ *
+ * Every computation step runs in hand-written HIP kernels on the caller's
+ * stream.  The library allocates nothing, keeps no pointer after a call
+ * returns and needs no workspace; its only state is a thread-local error
+ * message, so calls from several host threads are safe.
+ */
+#ifndef FFPA_H_
+#define FFPA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum { FFPA_BF16 = 0, FFPA_FP16 = 1 } ffpa_dtype;
+
+/* Mask element types.  BOOL_U8: one byte per entry, nonzero = takes part.
+ * ADD_*: additive bias in the named floating type. */
+typedef enum {
+  FFPA_MASK_NONE = 0,
+  FFPA_MASK_BOOL_U8 = 1,
+  FFPA_MASK_ADD_F32 = 2,
+  FFPA_MASK_ADD_BF16 = 3,
+  FFPA_MASK_ADD_FP16 = 4
+} ffpa_mask_kind;
+
+/* A mask broadcastable to [B, Hq, Nq, Nkv] (page parameter "attn_mask").
+ * Entry (b, h, r, k) lives at data + b*stride_b + h*stride_h + r*stride_q
+ * + k*stride_k, in elements of the mask type.  A zero stride broadcasts that
+ * dimension.  stride_k must be 1.  `data` is a device pointer owned by the
+ * caller. */
+typedef struct {
+  const void* data;
+  int32_t kind; /* ffpa_mask_kind */
+  int64_t stride_b, stride_h, stride_q, stride_k;
+} ffpa_mask_t;
+
+/* Status codes.  The Python layer maps 1/2/3/4 to TypeError / ValueError /
+ * NotImplementedError / RuntimeError, the error classes the API page lists. */
+enum {
+  FFPA_OK = 0,
+  FFPA_ERR_TYPE = 1,        /* dtype not bf16/fp16, or unknown mask kind */
+  FFPA_ERR_VALUE = 2,       /* inconsistent shapes, causal with Nkv < Nq, bad scale, bad pointers */
+  FFPA_ERR_UNSUPPORTED = 3, /* a valid request outside what the kernels cover (e.g. D % 64 != 0) */
+  FFPA_ERR_HIP = 4          /* the HIP runtime refused the launch */
+};
+
+/*
+ * ffpa_fwd -- enqueue the attention forward on `stream`.
+ *
+ *   q    device, [B, Hq, Nq, D], contiguous row-major, dtype elements
+ *   k, v device, [B, Hkv, Nkv, D], contiguous row-major, dtype elements
+ *   mask NULL for none, else a host pointer to a descriptor of a device mask
+ *        (read during this call only); cannot be combined with is_causal
+ *   o    device, [B, Hq, Nq, D], contiguous, dtype elements; written
+ *   lse  device, [B, Hq, Nq] float32, natural log; written; NULL skips it
+ *   B, Hq, Hkv, Nq, Nkv >= 1; Hq % Hkv == 0; 64 <= D <= 1024 with D % 64 == 0
+ *   scale   finite, or NaN for the default 1/sqrt(D)
+ *   is_causal  0 or 1; 1 requires Nkv >= Nq
+ *   dtype   ffpa_dtype
+ *   stream  hipStream_t, NULL for the null stream
+ *
+ * q, k, v and o must be 16-byte aligned and o must not overlap q, k, v, mask
+ * or lse.  Arguments are checked on the host before any HIP call, so an
+ * error return means nothing was enqueued.  The call returns once the kernel
+ * is enqueued; faults during execution surface at the caller's next
+ * synchronisation.
+ */
+int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+             int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
+             int is_causal, int dtype, void* stream);
+
+/* The host-side argument check ffpa_fwd performs, without enqueuing anything
+ * and without touching the memory the pointers refer to. */
+int ffpa_check_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                    const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                    float scale, int is_causal, int dtype);
+
+/* A static, human-readable name of a status code.  Never NULL. */
+const char* ffpa_status_string(int status);
+
+/* The most specific description of the problem found by the calling
+ * thread's last failing ffpa_fwd / ffpa_check_args call ("" if none).  The
+ * text lives in thread-local storage and stays valid until that thread's
+ * next call into the library. */
+const char* ffpa_last_error_detail(void);
+
+/* Rows of Q handled by one workgroup for head dim D (the tiling the kernels
+ * use), or 0 for an unsupported D.  Host-only; for schedulers and tests. */
+int ffpa_rows_per_block(int64_t D);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFPA_H_ */

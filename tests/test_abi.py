@@ -1,0 +1,133 @@
+"""The C-ABI boundary on the host: the library loads, exports what include/ffpa.h declares, and
+checks arguments before any HIP call (these tests never touch a GPU)."""
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_head_amd as ffpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffpa.h")
+
+# fake, 16-byte aligned, non-overlapping "device addresses": ffpa_check_args never dereferences them
+Q, K, V, O, L, M = (0x10_0000_0000 * (i + 1) for i in range(6))
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffpa_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(ffpa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ffpa.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def check(B=1, Hq=2, Hkv=1, Nq=100, Nkv=130, D=512, scale=math.nan, causal=False, dtype=ffpa.FFPA_BF16,
+          mask=None, q=Q, k=K, v=V, o=O, lse=L):
+    return ffpa.ffpa_check_args(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, dtype)
+
+
+def detail():
+    return ffpa.library().ffpa_last_error_detail().decode()
+
+
+def test_valid_arguments_pass():
+    assert check() == ffpa.OK
+    assert detail() == ""
+    for D in range(64, 1025, 64):
+        assert check(D=D) == ffpa.OK, D
+    assert check(causal=True) == ffpa.OK
+    assert check(lse=None) == ffpa.OK
+    assert check(scale=0.125) == ffpa.OK
+    assert check(Hq=8, Hkv=8) == ffpa.OK
+    assert check(Nq=1, Nkv=1) == ffpa.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), ffpa.ERR_TYPE),
+    (dict(dtype=-1), ffpa.ERR_TYPE),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE),
+    (dict(B=0), ffpa.ERR_VALUE),
+    (dict(Nq=0), ffpa.ERR_VALUE),
+    (dict(Nkv=-5), ffpa.ERR_VALUE),
+    (dict(causal=True, Nq=131, Nkv=130), ffpa.ERR_VALUE),
+    (dict(scale=math.inf), ffpa.ERR_VALUE),
+    (dict(scale=-math.inf), ffpa.ERR_VALUE),
+    (dict(q=0), ffpa.ERR_VALUE),
+    (dict(o=0), ffpa.ERR_VALUE),
+    (dict(k=K + 8), ffpa.ERR_VALUE),
+    (dict(lse=L + 2), ffpa.ERR_VALUE),
+    (dict(o=Q), ffpa.ERR_VALUE),
+    (dict(o=Q + 1024), ffpa.ERR_VALUE),
+    (dict(lse=V + 64), ffpa.ERR_VALUE),
+    (dict(D=96), ffpa.ERR_UNSUPPORTED),
+    (dict(D=32), ffpa.ERR_UNSUPPORTED),
+    (dict(D=1088), ffpa.ERR_UNSUPPORTED),
+    (dict(D=2048), ffpa.ERR_UNSUPPORTED),
+])
+def test_argument_errors(kw, status):
+    assert check(**kw) == status
+    assert detail() != ""
+
+
+def mdesc(kind=ffpa.MASK_ADD_F32, data=M, sb=0, sh=0, sq=130, sk=1):
+    return ffpa.MaskDesc(data, kind, sb, sh, sq, sk)
+
+
+def test_mask_descriptor_rules():
+    assert check(mask=mdesc()) == ffpa.OK
+    assert check(mask=mdesc(kind=ffpa.MASK_BOOL_U8)) == ffpa.OK
+    assert check(mask=mdesc(kind=ffpa.MASK_ADD_BF16)) == ffpa.OK
+    assert check(mask=mdesc(kind=ffpa.MASK_ADD_FP16)) == ffpa.OK
+    assert check(mask=mdesc(kind=ffpa.MASK_NONE, data=0)) == ffpa.OK
+    assert check(mask=mdesc(kind=7)) == ffpa.ERR_TYPE
+    assert check(mask=mdesc(data=0)) == ffpa.ERR_VALUE
+    assert check(mask=mdesc(), causal=True) == ffpa.ERR_VALUE
+    assert check(mask=mdesc(sk=2)) == ffpa.ERR_UNSUPPORTED
+    assert check(mask=mdesc(sk=0)) == ffpa.ERR_UNSUPPORTED
+    assert check(mask=mdesc(sq=-130)) == ffpa.ERR_VALUE
+    assert check(mask=mdesc(data=M + 2)) == ffpa.ERR_VALUE  # fp32 mask must be 4-byte aligned
+    assert check(mask=mdesc(data=O)) == ffpa.ERR_VALUE  # overlaps the output
+
+
+def test_status_strings():
+    lib = ffpa.library()
+    names = [lib.ffpa_status_string(s).decode() for s in range(5)]
+    assert len(set(names)) == 5 and all(names)
+    assert lib.ffpa_status_string(99).decode()
+
+
+@pytest.mark.parametrize("status,exc", [(ffpa.ERR_TYPE, TypeError), (ffpa.ERR_VALUE, ValueError),
+                                        (ffpa.ERR_UNSUPPORTED, NotImplementedError), (ffpa.ERR_HIP, RuntimeError)])
+def test_status_maps_to_the_pages_error_classes(status, exc):
+    with pytest.raises(exc):
+        ffpa._raise(status)
+
+
+def test_rows_per_block():
+    rows = {D: ffpa.rows_per_block(D) for D in range(64, 1025, 64)}
+    assert all(r in (64, 128, 256) for r in rows.values()), rows
+    assert ffpa.rows_per_block(96) == 0
+
+
+def test_python_layer_rejects_before_the_library():
+    import torch
+
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.float32)
+    with pytest.raises(NotImplementedError):
+        ffpa.attn(q, q, q, dropout_p=0.1)
+    with pytest.raises(TypeError):
+        ffpa.attn(q, q, q)
+    qb = q.to(torch.bfloat16)
+    kb = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # not on a GPU
+        ffpa.attn(qb, kb, kb, enable_gqa=True)
