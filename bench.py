@@ -1,0 +1,207 @@
+"""Forward throughput of the MI355X attention path on synthetic inputs.
+
+One step is one ffpa_fwd launch over the whole workload (every query row of every head), with the
+inputs already resident in HBM.  The default workload is large-head-dim self-attention
+B=1, H=8, N=4096, D=512 in bf16; the JSON line also carries the D=1024 workloads as secondary
+measurements.  FLOPs per step = 4*B*Hq*Nq*Nkv*D (halved when causal).  Peak = MI355X dense bf16/fp16
+MFMA, 2516.6 TFLOP/s.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA
+METRIC = "forward TFLOPS + % of MI355X bf16 MFMA peak at D=512 and D=1024"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def time_workload(w, steps: int, warmup: int):
+    """Times `steps` launches after `warmup` untimed ones; returns (ms per launch, inputs, outputs)."""
+    import torch
+
+    import exact_attention_head_amd as ffpa
+    import workloads as W
+
+    q, k, v, mask = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    md = mask.to(dev) if mask is not None else None
+    gqa = w.Hq != w.Hkv
+    o = torch.empty_like(qd)
+
+    def step():
+        return ffpa.attn(qd, kd, vd, attn_mask=md, is_causal=w.causal, enable_gqa=gqa, return_lse=True, out=o)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()  # ffpa.attn enqueues on torch's current stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        _, lse = step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return ms, (q, k, v, mask), (o.cpu(), lse.cpu())
+
+
+def cpu_baseline(w, inputs, outputs, seconds: float):
+    """Times the fp64 oracle on a bounded sample of rows of the same workload (all host threads it
+    uses), scales to TFLOPS by the metric's FLOP count, and compares those rows with the GPU output."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    q, k, v, mask = inputs
+    o_gpu, lse_gpu = outputs
+    rng = np.random.default_rng(w.seed + 99)
+    rows_all = rng.permutation(w.B * w.Hq * w.Nq)  # seeded random rows, drawn until the time budget is spent
+
+    def row_flops(rows):
+        if not w.causal:
+            return 4.0 * w.Nkv * w.D * len(rows)
+        vis = [min(w.Nkv, (r % w.Nq) + w.Nkv - w.Nq + 1) for r in rows]
+        return 4.0 * w.D * float(sum(vis))
+
+    n = 8
+    t_total, f_total, done = 0.0, 0.0, []
+    O_ref, L_ref = [], []
+    while True:
+        batch = rows_all[len(done):len(done) + n]
+        if len(batch) == 0:
+            break
+        t0 = time.perf_counter()
+        o_r, l_r = oracle.attention_rows(q, k, v, batch, mask=mask, is_causal=w.causal)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        f_total += row_flops(batch)
+        done.extend(batch)
+        O_ref.append(o_r)
+        L_ref.append(l_r)
+        if t_total >= seconds:
+            break
+        n = max(1, min(len(rows_all), int(len(batch) * min(4.0, max(1.5, seconds / max(t_total, 1e-3) / 2)))))
+    rows = np.asarray(done, dtype=np.int64)
+    o_ref, l_ref = np.concatenate(O_ref), np.concatenate(L_ref)
+    og = o_gpu.float().numpy().reshape(-1, w.D)[rows].astype(np.float64)
+    lg = lse_gpu.numpy().reshape(-1)[rows].astype(np.float64)
+    fin = np.isfinite(l_ref)
+    parity = dict(rows=int(rows.size), o_max_abs=float(np.abs(og - o_ref).max()),
+                  o_rel_l2=float(np.linalg.norm(og - o_ref) / np.linalg.norm(o_ref)),
+                  lse_max_abs=float(np.abs(lg[fin] - l_ref[fin]).max()) if fin.any() else 0.0)
+    sample = (f"{rows.size} seeded random query rows of {w.B * w.Hq * w.Nq} (all heads), each against all of "
+              f"its {w.Nkv if not w.causal else 'visible'} keys; fp64 oracle, ~{seconds:.0f} s budget")
+    return dict(value=f_total / t_total / 1e12, unit="TFLOPS", cores=oracle.max_threads(), kind="oracle",
+                sample=sample, seconds=round(t_total, 2)), parity
+
+
+def copy_calibration() -> None:
+    """A plain device copy of known size (for scaling the FETCH_SIZE / WRITE_SIZE counters)."""
+    import torch
+
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_direction": n, "launches": 3}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_d_self",
+                    help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16]")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    def pick(name):
+        if name.startswith("sweep:"):
+            parts = name.split(":")
+            return W.sweep(int(parts[1]), torch.float16 if len(parts) > 2 and parts[2] == "fp16" else torch.bfloat16)
+        return getattr(W, name)()
+
+    w = pick(args.workload)
+    log(f"workload {w.name}: warmup {args.warmup}, steps {args.steps}")
+    ms, inputs, outputs = time_workload(w, args.steps, args.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    log(f"{w.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak)")
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        traffic = tj.get(w.name)
+    roofline = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(tflops / PEAK_TFLOPS, 4), traffic=traffic,
+                    kernel="ffpa_fwd_kernel", flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))
+
+    secondary = []
+    if not args.no_secondary and args.workload == "large_d_self":
+        for name in ("cross_mask", "sweep:1024", "gqa_causal", "sweep:512"):
+            w2 = pick(name)
+            ms2, _, _ = time_workload(w2, max(5, args.steps // 5), 2)
+            tf2 = w2.flops / (ms2 * 1e-3) / 1e12
+            log(f"{w2.name}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
+            secondary.append(dict(workload=w2.name, D=w2.D, ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
+                                  frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on sampled rows (~{args.cpu_seconds:.0f} s)")
+        cpu, parity = cpu_baseline(w, inputs, outputs, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']:.4g} TFLOPS on {cpu['cores']} threads; parity {parity}")
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp16", "data": "synthetic",
+        "config": w.describe(), "frac_of_peak": round(tflops / PEAK_TFLOPS, 4), "roofline": roofline,
+        "cpu_baseline": cpu, "parity_sample": parity, "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
