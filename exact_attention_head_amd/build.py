@@ -32,12 +32,20 @@ def head_dims() -> list[int]:
 
 
 def _compile(src: str, obj: str, defines: list[str], remarks: bool) -> tuple[str, str]:
-    cmd = [HIPCC, *COMMON, *defines, "-c", src, "-o", obj]
+    """Compiles one object, keeping its gfx950 assembly next to it (obj with .s) for the hazard check."""
+    work = obj + ".tmp.d"
+    shutil.rmtree(work, ignore_errors=True)
+    os.makedirs(work)
+    cmd = [HIPCC, *COMMON, *defines, "-save-temps", "-c", os.path.abspath(src), "-o", os.path.abspath(obj)]
     if remarks:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
-    r = subprocess.run(cmd, capture_output=True, text=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {os.path.basename(obj)}:\n{r.stderr[-4000:]}")
+    asm = [f for f in os.listdir(work) if f.endswith(f"-hip-amdgcn-amd-amdhsa-{ARCH}.s")]
+    if asm:
+        os.replace(os.path.join(work, asm[0]), obj[:-2] + ".s")
+    shutil.rmtree(work, ignore_errors=True)
     return obj, r.stderr
 
 
@@ -73,6 +81,19 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
             if report and "_d" in obj:
                 resources[os.path.basename(obj)[:-2]] = resource_summary(err)
     objs = [o for _, o, _ in tasks]
+    # the kernels' inline assembly relies on rules the compiler does not check: verify them
+    sys.path.insert(0, PKG)
+    try:
+        from check_mfma_hazards import check as check_hazards
+    finally:
+        sys.path.remove(PKG)
+
+    hazards = []
+    for o in objs:
+        if "_d" in os.path.basename(o):
+            hazards += check_hazards(o[:-2] + ".s")
+    if hazards:
+        raise RuntimeError("MFMA / LDS hazards in the generated code:\n" + "\n".join(hazards[:20]))
     tmp = LIB + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
