@@ -107,20 +107,20 @@ struct Elem;
   struct Elem<TAG> {                                                                                          \
     /* d = a*b, d in VGPRs; a from VGPRs, b from VGPRs (BA=false) or AGPRs (BA=true) */                     \
     __device__ static inline void mma_first(f32x16& d, const i32x4& a, const i32x4& b) {                     \
-      asm(INSN " %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));                                                 \
+      asm volatile(INSN " %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));                                                 \
     }                                                                                                         \
     __device__ static inline void mma_first_ba(f32x16& d, const i32x4& a, const i32x4& b) {                  \
-      asm(INSN " %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));                                                 \
+      asm volatile(INSN " %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));                                                 \
     }                                                                                                         \
     __device__ static inline void mma_acc(f32x16& d, const i32x4& a, const i32x4& b) {                       \
-      asm(INSN " %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));                                                 \
+      asm volatile(INSN " %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));                                                 \
     }                                                                                                         \
     __device__ static inline void mma_acc_ba(f32x16& d, const i32x4& a, const i32x4& b) {                    \
-      asm(INSN " %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));                                                 \
+      asm volatile(INSN " %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));                                                 \
     }                                                                                                         \
     /* d += a*b with d in AGPRs and VALU-written operands */                                                  \
     __device__ static inline void mma_acc_agpr(f32x16& d, const i32x4& a, const i32x4& b) {                  \
-      asm("s_nop 1\n\t" INSN " %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));                                 \
+      asm volatile("s_nop 1\n\t" INSN " %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));                                 \
     }                                                                                                         \
   };
 FFPA_DEFINE_MMA(Bf16, "v_mfma_f32_32x32x16_bf16")
@@ -1124,36 +1124,40 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
   const int vkeyA = (g16 >> 1) * 4 + (i16 >> 2);
   const int vofsA = vkeyA * 64 + swz(vkeyA, tr_chunk) * 16 + tr_within;
   const int vofsB = (vkeyA + 8) * 64 + swz(vkeyA + 8, tr_chunk) * 16 + tr_within;
-  auto read_frags = [&](int g, bool is_k, i32x4 (&f)[NF]) {
+  // Fragment reads of stage g in two halves (K: the 16-column steps ks = 0 / 1; V: the 16-key
+  // steps 0-1 / 2-3), so that they can be spread between the products of the previous stage.
+  auto read_frags_part = [&](int g, bool is_k, i32x4 (&f)[NF], int half) {
     const char* slot = ring + (g % NSLOT) * K::SLOT;
     if (is_k) {
       const char* kt = QREG ? slot : slot + 4096;
+      const int kofs = half == 0 ? kofs0 : kofs1;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f[0 * 2 + kb] = lds_read16(kt + kofs0 + kb * 2048);
-        f[1 * 2 + kb] = lds_read16(kt + kofs1 + kb * 2048);
-      }
+      for (int kb = 0; kb < 2; ++kb) f[half * 2 + kb] = lds_read16(kt + kofs + kb * 2048);
       if constexpr (!QREG) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f[4 + 0 * 2 + rb] = lds_read16(slot + kofs0 + rb * 2048);
-          f[4 + 1 * 2 + rb] = lds_read16(slot + kofs1 + rb * 2048);
-        }
+        for (int rb = 0; rb < RB; ++rb) f[4 + half * 2 + rb] = lds_read16(slot + kofs + rb * 2048);
       }
     } else {
       const uint32_t a0 = lds_addr(slot) + (uint32_t)vofsA, b0 = lds_addr(slot) + (uint32_t)vofsB;
-      i32x2 lo[4], hi4[4];
-      lo[0] = lds_read_tr_async<0>(a0);
-      hi4[0] = lds_read_tr_async<0>(b0);
-      lo[1] = lds_read_tr_async<1024>(a0);
-      hi4[1] = lds_read_tr_async<1024>(b0);
-      lo[2] = lds_read_tr_async<2048>(a0);
-      hi4[2] = lds_read_tr_async<2048>(b0);
-      lo[3] = lds_read_tr_async<3072>(a0);
-      hi4[3] = lds_read_tr_async<3072>(b0);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) f[ks] = i32x4{lo[ks][0], lo[ks][1], hi4[ks][0], hi4[ks][1]};
+      i32x2 lo0, hi0, lo1, hi1;
+      if (half == 0) {
+        lo0 = lds_read_tr_async<0>(a0);
+        hi0 = lds_read_tr_async<0>(b0);
+        lo1 = lds_read_tr_async<1024>(a0);
+        hi1 = lds_read_tr_async<1024>(b0);
+      } else {
+        lo0 = lds_read_tr_async<2048>(a0);
+        hi0 = lds_read_tr_async<2048>(b0);
+        lo1 = lds_read_tr_async<3072>(a0);
+        hi1 = lds_read_tr_async<3072>(b0);
+      }
+      f[half * 2 + 0] = i32x4{lo0[0], lo0[1], hi0[0], hi0[1]};
+      f[half * 2 + 1] = i32x4{lo1[0], lo1[1], hi1[0], hi1[1]};
     }
+  };
+  auto read_frags = [&](int g, bool is_k, i32x4 (&f)[NF]) {
+    read_frags_part(g, is_k, f, 0);
+    read_frags_part(g, is_k, f, 1);
   };
 
   f32x16 o_acc[RB][NC];
@@ -1191,14 +1195,16 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
     const bool has_mask = a.mask_kind != kMaskNone;
     if (has_mask) load_bias_dispatch<RB, NQ>(bias, ctx, kown, a.mask_kind, a.mask_vec && !tail);
 
-    // one pipeline step: refill, fetch the next stage's fragments, then this stage's products
-    auto advance = [&](int g, bool next_is_k, i32x4 (&cur)[NF], i32x4 (&nxt)[NF]) {
-      issue(g + NSLOT - 1);
-      if (g + 1 < nstages) {
-        wait_stage(g + 1);
-        read_frags(g + 1, next_is_k, nxt);
+    // One pipeline step for stage g: its 8 products, with the preparation of stage g+1 (the refill
+    // of the slot of stage g-1, the wait for stage g+1's data and its fragment reads) placed
+    // between them so that the matrix core keeps working while the wave does the bookkeeping.
+    auto prep = [&](int g, int part, bool next_is_k, i32x4 (&nxt)[NF]) {
+      if (part == 0) {
+        issue(g + NSLOT - 1);
+      } else if (g + 1 < nstages) {
+        if (part == 1) wait_stage(g + 1);
+        else read_frags_part(g + 1, next_is_k, nxt, part - 2);
       }
-      (void)cur;
     };
 
     // ================= S^T = K Q^T over this wave's columns =================
@@ -1207,7 +1213,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
     for (int u = 0; u < NC; ++u) {
       const int g = j * SPT + u;
       i32x4 (&cur)[NF] = fr[u & 1];
-      advance(g, u + 1 < NC, cur, fr[(u + 1) & 1]);
+      i32x4 (&nxt)[NF] = fr[(u + 1) & 1];
+      const bool next_is_k = u + 1 < NC;
+      int step = 0;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -1222,6 +1230,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
               if (u == 0 && ks == 0) E::mma_first(s_acc[rb][kb], kf, cur[4 + ks * 2 + rb]);
               else E::mma_acc(s_acc[rb][kb], kf, cur[4 + ks * 2 + rb]);
             }
+            if (step < 4) prep(g, step, next_is_k, nxt);
+            ++step;
           }
     }
     mma_guard_v<RB>(s_acc);
@@ -1352,15 +1362,21 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
       const int u = NC + c;
       const int g = j * SPT + u;
       i32x4 (&cur)[NF] = fr[u & 1];
+      i32x4 (&nxt)[NF] = fr[(u + 1) & 1];
       {
         i32x4(&v4)[4] = *reinterpret_cast<i32x4(*)[4]>(&cur[0]);
         lds_frag_wait(v4);  // V fragments were read with the untracked transposed loads
       }
-      advance(g, u + 1 == SPT, cur, fr[(u + 1) & 1]);
+      const bool next_is_k = u + 1 == SPT;
+      int step = 0;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) E::mma_acc_agpr(o_acc[rb][c], cur[ks], pk[rb][ks]);
+        for (int rb = 0; rb < RB; ++rb) {
+          E::mma_acc_agpr(o_acc[rb][c], cur[ks], pk[rb][ks]);
+          if (step < 4) prep(g, step, next_is_k, nxt);
+          ++step;
+        }
     }
     mma_guard_all<RB * NC>(&o_acc[0][0]);  // O is never read within 12 wait states of a product
   }
