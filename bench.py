@@ -111,6 +111,34 @@ def cpu_baseline(w, inputs, outputs, seconds: float):
                 sample=sample, seconds=round(t_total, 2)), parity
 
 
+KERNEL_SOURCES = ("ffpa_kernel.hpp", "ffpa_launch.hpp", "ffpa_inst.hip", "ffpa_api.hip")
+
+
+def kernel_fingerprint() -> str:
+    """First 16 hex digits of the SHA-256 over the kernel sources (ties measured traffic to a kernel)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(path: str, workload: str):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs (already scaled by the copy
+    calibration), or None when none were taken for this workload or the kernel changed since."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tj = json.load(f)
+    if tj.get("kernel_sources_sha256_16") != kernel_fingerprint():
+        log("traffic counters were taken on other kernel sources: traffic = null")
+        return None
+    ent = tj.get(workload)
+    return None if ent is None else ent["hbm_bytes_per_launch"]
+
+
 def copy_calibration() -> None:
     """A plain device copy of known size (for scaling the FETCH_SIZE / WRITE_SIZE counters)."""
     import torch
@@ -167,14 +195,12 @@ def main() -> int:
     tflops = w.flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak)")
 
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        traffic = tj.get(w.name)
+    traffic = measured_traffic(args.traffic_json, w.name)
+    # four column groups per workgroup (D a multiple of 128 from 384 up) run the column-split kernel
+    kernel = "ffpa_fwd_split_kernel" if w.D >= 384 and w.D % 128 == 0 else "ffpa_fwd_kernel"
     roofline = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(tflops / PEAK_TFLOPS, 4), traffic=traffic,
-                    kernel="ffpa_fwd_kernel", flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))
+                    frac=round(tflops / PEAK_TFLOPS, 4), traffic=traffic, traffic_unit="HBM bytes per launch",
+                    kernel=kernel, flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))
 
     secondary = []
     if not args.no_secondary and args.workload == "large_d_self":
