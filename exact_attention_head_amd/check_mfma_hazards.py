@@ -8,9 +8,10 @@ checked here over the generated assembly of every kernel:
    12 wait states (one per issued instruction, N+1 per s_nop N) - except another v_mfma accumulating
    into exactly the same registers.
 2. A VALU write of a register needs 2 wait states before a v_mfma reads it as an operand.
-3. The destination of a ds_read_b64_tr_b16 is valid only after an s_waitcnt lgkmcnt(N) that covers
-   it: LDS returns in order, so lgkmcnt(N) completes a read once N or more LDS instructions were
-   issued after it.  Nothing may read or overwrite those registers before that.
+3. The destination of an LDS read (ds_read*, also when issued from inline assembly) is valid only
+   after an s_waitcnt lgkmcnt(N) that covers it: LDS returns in order, so lgkmcnt(N) completes a
+   read once N or more LDS instructions were issued after it.  Nothing may read or overwrite those
+   registers before that.
 
 The analysis is a forward data-flow pass over the instruction stream: the in-flight state is copied
 at every branch, merged (union) at every label, and the pass runs twice so that states carried by
@@ -61,7 +62,7 @@ class State:
     def __init__(self):
         self.mfma = {}  # (regs, dst operand, text) -> remaining wait states
         self.valu = {}  # (regs, text) -> remaining wait states
-        self.tr = {}  # (regs, text) -> LDS instructions issued after it (minimum over paths)
+        self.tr = {}  # (regs, text) of LDS reads -> LDS instructions issued after it (minimum over paths)
 
     def copy(self):
         s = State()
@@ -167,7 +168,7 @@ def check_function(path: str, name: str, body) -> list:
                 state.mfma[(regs(ops[0]), ops[0], line)] = MFMA_RESULT_WAIT
             elif op.startswith("v_") and ops:
                 state.valu[(regs(ops[0]), line)] = VALU_TO_MFMA_WAIT
-            if op == "ds_read_b64_tr_b16" and ops:
+            if op.startswith("ds_read") and ops:
                 state.tr[(regs(ops[0]), line)] = 0
     return sorted(problems)
 

@@ -48,7 +48,7 @@ size_t mask_elem_size(int kind) {
 int rows_for(int64_t D) {
   switch (D) {
 #define FFPA_ROWS_CASE(Dv) \
-  case Dv: return ffpa::FwdKernel<ffpa::Bf16, Dv>::BR;
+  case Dv: return ffpa::rows_per_block<Dv>();
     FFPA_FOR_EACH_D(FFPA_ROWS_CASE)
 #undef FFPA_ROWS_CASE
     default: return 0;

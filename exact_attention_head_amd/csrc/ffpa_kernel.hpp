@@ -1408,12 +1408,36 @@ __global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
   }
 }
 
+}  // namespace ffpa
+
+#include "ffpa_row_kernel.hpp"
+
+namespace ffpa {
+
+// Query rows per workgroup of the kernel that serves head dim D.
+template <int D>
+constexpr int rows_per_block() {
+  if constexpr (use_row_kernel<D>()) return RowTiling<D>::BR;
+  else return FwdKernel<Bf16, D>::BR;
+}
+
+// Name of the kernel that serves head dim D (for profiles and reports).
+template <int D>
+constexpr const char* kernel_name() {
+  if constexpr (use_row_kernel<D>()) return "ffpa_fwd_row_kernel";
+  else if constexpr (Tiling<D>::RG == 1) return "ffpa_fwd_split_kernel";
+  else return "ffpa_fwd_kernel";
+}
+
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   using K = FwdKernel<T, D>;
-  const int nqt = (a.Nq + K::BR - 1) / K::BR;
+  constexpr int BR = rows_per_block<D>();
+  const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
-  if constexpr (Tiling<D>::RG == 1) {
+  if constexpr (use_row_kernel<D>()) {
+    hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else if constexpr (Tiling<D>::RG == 1) {
     static_assert(SplitKernel<T, D>::BR == K::BR, "same query tile");
     hipLaunchKernelGGL((ffpa_fwd_split_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else {

@@ -1,0 +1,524 @@
+// Row-owner forward kernel for the large head dims (gfx950).
+//
+// Each wave owns 32 query rows and DW = D / DG output columns of them: DG = 1 up to D = 512 (the
+// wave holds the whole O row block, 32 x D fp32 = D/2 AGPRs, and its Q rows in VGPRs, so S needs
+// no cross-wave reduction at all), DG = 2 above (two waves share 32 rows and split the columns;
+// their partial S tiles are summed through LDS once per 32-key block).  The workgroup is 4 waves:
+// 128 query rows for DG = 1, 64 for DG = 2.  This is the output-D split of the ffpa-attn README
+// ("Split-D and TiledMMA") sized for a 512-register CDNA4 lane instead of the pages' 255-register
+// NVIDIA thread.
+//
+// Split-D staging.  K and V reach the matrix cores through a ring of 4 KiB LDS groups, each made
+// of two [32 keys][32 columns] sub-tiles (64-byte rows, 16-byte chunks swizzled by
+// chunk ^ ((row >> 2) & 3)), filled with buffer_load_dwordx4 ... lds (one instruction per wave per
+// group; keys past Nkv read as zero through the descriptor's range check).  A 64-key tile is
+// consumed in four phases - K of keys 0-31, K of keys 32-63, V of keys 0-31, V of keys 32-63 -
+// each streaming the wave's columns in 32-column steps, two products per step.  The ring is
+// shared by the four waves and advanced in epochs of EM products: one s_barrier per epoch makes
+// the next epoch's groups visible and frees the slots of the epoch before last, which are then
+// refilled LA epochs ahead.
+//
+// Products.  S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16 (lane l <-> query row l % 32,
+// so row statistics are lane-local plus one v_permlane32_swap); the operand fragments come from
+// LDS PF products ahead of their use (ds_read_b128 for K, two ds_read_b64_tr_b16 for V^T).
+//
+// Softmax per 32-key block, overlapped with the matrix core: the logits, the row maximum and
+// the exponentials of block kb are computed in small pieces between the products of the next
+// phase (S of block 1 for block 0, P V of block 0 for block 1).  The running maximum is moved
+// only when a block's maximum exceeds it by more than kRescaleSlack (log2 units); then O and l
+// are rescaled in a rare wave-uniform branch - for block 1 after the products of block 0 have
+// been accumulated, so that O always matches the reference of the probabilities added to it.
+#pragma once
+
+#include <utility>
+
+namespace ffpa {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each call with its index as a constant.
+template <typename F, int... Is>
+__device__ inline void static_for_impl(F& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Epoch length (products per wave) and ring size (4 KiB groups) for a head-dim configuration.
+struct RingPlan {
+  int em, ng;
+};
+
+constexpr RingPlan choose_ring(int GT, int MPG, int MPT, int exch_bytes) {
+  RingPlan best{0, 0};
+  int best_score = -1;
+  const int ems[2] = {16, 8};
+  for (int i = 0; i < 2; ++i) {
+    const int em = ems[i];
+    if (MPT % em != 0 || em % MPG != 0) continue;
+    const int bi = em / MPG;  // groups per epoch
+    for (int ng = 40; ng >= bi; --ng) {
+      if (ng % bi != 0 || GT % ng != 0) continue;
+      if (ng * 4096 + exch_bytes > 160 * 1024) continue;
+      const int ne = ng / bi;
+      if (ne < 4) continue;
+      const int ahead = (ne - 2) * em;  // products of lookahead
+      const int capped = ahead < 48 ? ahead : 48;
+      const int score = capped * 16 - MPT / em;  // enough lookahead first, then fewer barriers
+      if (score > best_score) {
+        best_score = score;
+        best = RingPlan{em, ng};
+      }
+    }
+  }
+  return best;
+}
+
+template <int D>
+struct RowTiling {
+  static constexpr int DG = D <= 512 ? 1 : 2;
+  static constexpr int DW = D / DG;             // output columns per wave
+  static constexpr int NSUB = DW / 32;          // 32-column steps per phase
+  static constexpr int RG = 4 / DG;             // row groups
+  static constexpr int BR = 32 * RG;            // query rows per workgroup
+  static constexpr int GT = 2 * NSUB * DG;      // groups per 64-key tile
+  static constexpr int GPP = GT / 4;            // groups per phase
+  static constexpr int MPT = 8 * NSUB;          // products per wave per tile
+  static constexpr int MPG = 4 / DG;            // products per wave per group
+  static constexpr int EXCH = DG == 2 ? 4 * 2 * 4096 : 0;  // partial-S exchange: [wave][block][4 KiB]
+  static constexpr RingPlan PLAN = choose_ring(GT, MPG, MPT, EXCH);
+  static constexpr int EM = PLAN.em;
+  static constexpr int NG = PLAN.ng;
+  static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB >= 2;
+  static constexpr int BI = OK ? EM / MPG : 1;  // groups per epoch
+  static constexpr int NE = OK ? NG / BI : 1;   // epochs held by the ring
+  static constexpr int LA = NE - 2;             // epochs of load lookahead
+  static constexpr int EPT = OK ? MPT / EM : 1; // epochs per tile
+  static constexpr int LDS_BYTES = NG * 4096 + EXCH;
+};
+
+// The head dims that run the row kernel (the others keep the column-split kernels).
+template <int D>
+constexpr bool use_row_kernel() {
+  return RowTiling<D>::OK && D >= 256;
+}
+
+// s_waitcnt lgkmcnt(N) tying the fragment registers it completes.
+template <int N>
+__device__ inline void lgkm_wait_k(i32x4& f) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "n"(N));
+}
+template <int N>
+__device__ inline void lgkm_wait_v(i32x2& lo, i32x2& hi) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "n"(N));
+}
+template <int OFF>
+__device__ inline i32x4 lds_read_b128_async(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  i32x4 d;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF) : "memory");
+  return d;
+}
+template <int OFF>
+__device__ inline void lds_write_b128_async(uint32_t addr, const f32x4& v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
+}
+template <int OFF>
+__device__ inline f32x4 lds_read_f4_async(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  f32x4 d;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF) : "memory");
+  return d;
+}
+template <int N>
+__device__ inline void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// 12 wait states after the products that wrote one VGPR accumulator.
+__device__ inline void mma_guard_s(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(x)); }
+
+// Operand fragments are read this many products ahead of their use.
+constexpr int kRowPF = 3;
+
+// Slot (product index within the tile, after whose issue the piece runs) at which the softmax of
+// 32-key block kb can start: right after its S block for one column group; for two, PF slots
+// after the first epoch barrier that follows the publication of the partial tiles.
+constexpr int row_sm_first(int kb, int DG, int PH, int EM, int PF) {
+  const int p0 = (kb + 1) * PH;
+  if (DG == 1) return p0;
+  int bs = ((p0 + PF + EM - 1) / EM) * EM - PF;  // first barrier slot (e*EM - PF) at or after p0
+  while (bs < p0) bs += EM;
+  return bs + PF;
+}
+constexpr int kRowSmPieces = 9;
+constexpr int row_sm_stride(int kb, int DG, int PH, int EM, int PF) {
+  const int span = (kb + 2) * PH - 2 - row_sm_first(kb, DG, PH, EM, PF);
+  return span >= 2 * kRowSmPieces ? 2 : 1;
+}
+// every piece of both blocks ends before the products that consume the block's probabilities
+constexpr bool row_sm_fits(int DG, int PH, int EM, int PF) {
+  for (int kb = 0; kb < 2; ++kb) {
+    const int last = row_sm_first(kb, DG, PH, EM, PF) + (kRowSmPieces - 1) * row_sm_stride(kb, DG, PH, EM, PF);
+    if (last > (kb + 2) * PH - 2) return false;
+  }
+  return true;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
+  using RT = RowTiling<D>;
+  using E = Elem<T>;
+  static_assert(RT::OK, "no ring plan for this head dim");
+  constexpr int DG = RT::DG, DW = RT::DW, NSUB = RT::NSUB, BR = RT::BR, GPP = RT::GPP;
+  constexpr int MPT = RT::MPT, EM = RT::EM, BI = RT::BI, NG = RT::NG, LA = RT::LA, EPT = RT::EPT;
+  constexpr int PF = kRowPF;     // operand fragments are read this many products ahead
+  constexpr int NFR = PF + 1;    // fragment registers in rotation
+  constexpr int BC = 64;
+  constexpr int PH = 2 * NSUB;   // products per phase
+  static_assert(MPT % NFR == 0, "the fragment rotation must line up with the tile");
+  static_assert(PF < EM && LA >= 2, "ring plan");
+  static_assert(NG * 4096 <= 2 * 65536, "two 64 KiB LDS address windows");
+  static_assert(row_sm_fits(DG, PH, EM, PF), "softmax schedule does not fit the phases");
+  // the second block's mask biases are requested once the first block's logits are formed
+  constexpr int BIAS1_SLOT = row_sm_first(0, DG, PH, EM, PF) + 4 * row_sm_stride(0, DG, PH, EM, PF);
+  static_assert(BIAS1_SLOT < row_sm_first(1, DG, PH, EM, PF), "mask biases before their use");
+
+  __shared__ __attribute__((aligned(1024))) char smem[RT::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dg = DG == 1 ? 0 : (wave & 1);
+  const int rg = DG == 1 ? wave : (wave >> 1);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // ---- work item (b, hq, q tile); consecutive items share an XCD's L2
+  const int Nq = a.Nq, Nkv = a.Nkv;
+  const int nqt = (Nq + BR - 1) / BR;
+  const int total = a.B * a.Hq * nqt;
+  int id = blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  int qt = id % nqt;
+  const int bh = id / nqt;
+  const int hq = bh % a.Hq;
+  const int b = bh / a.Hq;
+  if (a.causal) qt = nqt - 1 - qt;  // heaviest tiles first
+  const int hk = hq / a.group;
+  const int r0 = qt * BR;
+  const int rw0 = r0 + rg * 32;  // first row of this wave
+  const int row = rw0 + l32;     // this lane's row
+  const int col0 = dg * DW;
+  const int off = Nkv - Nq;
+  const uint16_t* qg = a.q + (int64_t)(b * a.Hq + hq) * Nq * D;
+  const uint16_t* kg = a.k + (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  const uint16_t* vg = a.v + (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  int kv_end = Nkv;
+  if (a.causal) {
+    const int lim = r0 + BR + off;
+    kv_end = lim < Nkv ? lim : Nkv;
+  }
+  const int ntiles = (kv_end + BC - 1) / BC;
+  const int total_epochs = ntiles * EPT;
+
+  // ---- this wave's Q rows (its DW columns), in VGPRs for the whole key loop
+  i32x4 qf[DW / 16];
+  {
+    const int qrow = row < Nq ? row : Nq - 1;
+    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * D + col0 + hi * 8);
+#pragma unroll
+    for (int k = 0; k < DW / 16; ++k) qf[k] = src[k * 2];
+  }
+
+  // ---- ring loads: in every group, wave w fills rows 16*(w&1) .. +15 of sub-tile w>>1
+  const int pst = wave >> 1;
+  const int prow = 16 * (wave & 1) + (lane >> 2);
+  const uint32_t voff = (uint32_t)((prow * D + ((lane & 3) ^ ((prow >> 2) & 3)) * 8) * 2);
+  const int64_t head_elems = (int64_t)Nkv * D;
+  char* const ring_w = smem + pst * 2048 + (wave & 1) * 1024;
+  auto issue_group = [&](int j, int gi) {
+    const int ph = gi / GPP, w = gi % GPP;
+    const int key0 = j * BC + (ph & 1) * 32;
+    const int col = DG == 1 ? 64 * w + 32 * pst : pst * DW + 32 * w;
+    int64_t start = (int64_t)key0 * D + col;
+    const int bytes = start < head_elems ? (int)((head_elems - start) * 2) : 0;
+    start = start < head_elems ? start : 0;
+    const uint16_t* src = (ph < 2 ? kg : vg) + start;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FFPA_LDS void*)(ring_w + (gi % NG) * 4096), 16, voff, 0, 0, 0);
+  };
+  // every group of global epoch eg (of tile eg / EPT), if it exists
+  auto issue_epoch = [&](int eg) {
+    if (eg >= total_epochs) return;
+    const int j = eg / EPT;
+    const int e = eg - j * EPT;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) issue_group(j, e * BI + i);
+  };
+  // this wave's loads of global epoch eg are complete (the LA-1 later epochs may be in flight)
+  auto wait_epoch = [&](int eg) {
+    if (eg + LA - 1 < total_epochs) vm_wait<(LA - 1) * BI>();
+    else vm_wait<0>();
+  };
+
+  // ---- operand fragment addresses (per lane; slot and step offsets are immediates)
+  const uint32_t ring_addr = lds_addr(smem);
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int tr_chunk = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  const int tr_within = 8 * (i16 & 1);
+  const int vkeyA = (g16 >> 1) * 4 + (i16 >> 2);
+  const uint32_t sub = ring_addr + dg * 2048;  // two column groups: this wave's sub-tile of each group
+  // K fragment (32 keys x 16 columns, 16-column step ks): key l32, chunk 2*ks + hi
+  const uint32_t ka[2] = {sub + l32 * 64 + swz(l32, hi) * 16, sub + l32 * 64 + swz(l32, 2 + hi) * 16};
+  // V^T fragment (16-key step ks): two transposed reads, keys vkeyA and vkeyA + 8 (+16 per step)
+  const uint32_t va = sub + vkeyA * 64 + swz(vkeyA, tr_chunk) * 16 + tr_within;
+  const uint32_t vb = sub + (vkeyA + 8) * 64 + swz(vkeyA + 8, tr_chunk) * 16 + tr_within;
+
+  const uint32_t ka0h = ka[0] + 65536, ka1h = ka[1] + 65536, vah = va + 65536, vbh = vb + 65536;
+  i32x4 kfr[NFR];
+  i32x2 vlo[NFR], vhi[NFR];
+  // fragment of product M of a tile (M >= MPT: the next tile's product M - MPT, same slots); the
+  // slot and step offsets are instruction immediates on a few per-lane base addresses
+  auto read_frag = [&](auto mc) {
+    constexpr int M = decltype(mc)::value;
+    constexpr int mm = M % MPT;
+    constexpr int ph = mm / PH, s = (mm % PH) / 2, ks = mm % 2;
+    constexpr int gi = ph * GPP + (DG == 1 ? s / 2 : s);
+    constexpr int ofs = (gi % NG) * 4096 + (DG == 1 ? (s & 1) * 2048 : 0);
+    constexpr bool upper = ofs >= 65536;
+    constexpr int r = M % NFR;
+    if constexpr (ph < 2) {
+      const uint32_t base = ks == 0 ? (upper ? ka0h : ka[0]) : (upper ? ka1h : ka[1]);
+      kfr[r] = lds_read_b128_async<(ofs & 65535)>(base);
+    } else {
+      constexpr int o2 = (ofs & 65535) + ks * 1024;
+      vlo[r] = lds_read_tr_async<o2>(upper ? vah : va);
+      vhi[r] = lds_read_tr_async<o2>(upper ? vbh : vb);
+    }
+  };
+
+  f32x16 o_acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    o_acc[s] = f32x16{};
+    asm volatile("" : "+a"(o_acc[s]));
+  }
+  float m_run = kNegInf;  // running reference maximum of this lane's row (log2 domain)
+  float l_lane = 0.f;     // sum of this lane's probabilities (the other half-wave holds the rest)
+  const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
+  const bool has_mask = a.mask_kind != kMaskNone;
+
+  // partial-S exchange (two column groups): [wave][block][4 x 1 KiB], 16 bytes per lane
+  const uint32_t ex_mine = ring_addr + NG * 4096 + wave * 8192 + lane * 16;
+  const uint32_t ex_partner = ring_addr + NG * 4096 + (wave ^ 1) * 8192 + lane * 16;
+
+  // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
+#pragma unroll
+  for (int e = 0; e < LA; ++e) issue_epoch(e);
+  wait_epoch(0);
+  __builtin_amdgcn_s_barrier();
+  issue_epoch(LA);
+  static_for<PF>([&](auto mc) { read_frag(mc); });
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * BC;
+    const bool tail = key0 + BC > Nkv;
+    const bool diag = a.causal && (key0 + BC - 1 > rw0 + off);
+    const bool edge = tail || diag;
+    LogitCtx ctx{a.mask, mask_bh, a.msq, Nq, Nkv, key0, rw0, off, a.causal, edge, a.scale_log2, l32, hi};
+
+    f32x16 s_acc[2];     // S^T of the two 32-key blocks; overwritten in place by the logits
+    f32x4 part[2][4];    // the partner's partial S (two column groups)
+    f32x4 bias[2][4];    // mask biases
+    float lmax[2], m_new[2], alpha[2], psum[2];
+    bool need[2];
+    i32x4 pk[2][2];      // P^T operands (bf16/fp16 pairs) of block kb, 16-key step ks
+
+    if (has_mask)
+      load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[0][0]), ctx, key0, a.mask_kind,
+                               a.mask_vec && !tail);
+
+    // softmax of block kb in pieces c = 0..8: logits of 4-key group c (0-3), the row maximum and
+    // the reference decision (4), exponentials and P^T packing of group c-5 (5-8)
+    auto sm_piece = [&](int kb, int c) {
+      if (c < 4) {
+        const int g = c;
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = s_acc[kb][4 * g + e];
+        if constexpr (DG == 2) x = x + part[kb][g];
+        x = x * a.scale_log2;
+        if (has_mask) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(bias[kb][g][e], kLog2e, x[e]);
+        }
+        if (edge) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = key0 + 32 * kb + 8 * g + 4 * hi + e;
+            const bool dead = kk >= Nkv || (a.causal && kk > row + off);
+            x[e] = dead ? kNegInf : x[e];
+          }
+        }
+        float mx = g == 0 ? kNegInf : lmax[kb];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mx = __builtin_fmaxf(mx, x[e]);
+          s_acc[kb][4 * g + e] = x[e];
+        }
+        lmax[kb] = mx;
+      } else if (c == 4) {
+        const float mt = max_halves(lmax[kb]);
+        const float mo = m_run;
+        const bool nd = mo != kNegInf && mt > mo + kRescaleSlack;
+        const float mn = mo == kNegInf ? mt : (nd ? mt : mo);
+        need[kb] = nd;
+        alpha[kb] = nd ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
+        m_new[kb] = mn;
+        m_run = mn;
+        psum[kb] = 0.f;
+      } else {
+        const int g = c - 5;
+        const float mref = m_new[kb] == kNegInf ? 0.f : m_new[kb];
+        f32x4 p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = __builtin_amdgcn_exp2f(s_acc[kb][4 * g + e] - mref);
+          psum[kb] += p[e];
+        }
+        const int ks = g >> 1, h2 = g & 1;
+        pk[kb][ks][2 * h2 + 0] = (int)pack2<T>(p[0], p[1]);
+        pk[kb][ks][2 * h2 + 1] = (int)pack2<T>(p[2], p[3]);
+      }
+    };
+    // l and O follow block kb's new reference (O holds exactly the blocks before kb)
+    auto apply_rescale = [&](int kb) {
+      l_lane = l_lane * alpha[kb] + psum[kb];
+      if (__builtin_amdgcn_ballot_w64(need[kb]) != 0) {
+        mma_guard_all<NSUB>(o_acc);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+          o_acc[s] *= alpha[kb];
+          asm volatile("" : "+a"(o_acc[s]));
+        }
+      }
+    };
+
+    static_for<MPT>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int ph = m / PH, s = (m % PH) / 2, ks = m % 2;
+      constexpr int r = m % NFR;
+      // ---- product m, once its fragment is complete: the LDS reads issued after it are those of
+      // the fragments m+1 .. m+PF-1 (any other LDS instruction issued later only waits longer)
+      {
+        int after = 0;
+#pragma unroll
+        for (int k = 1; k < PF; ++k) after += ((m + k) % MPT) / PH < 2 ? 1 : 2;
+        if (ph < 2) {
+          if (after <= 2) lgkm_wait_k<2>(kfr[r]);
+          else if (after == 3) lgkm_wait_k<3>(kfr[r]);
+          else lgkm_wait_k<4>(kfr[r]);
+        } else {
+          if (after <= 2) lgkm_wait_v<2>(vlo[r], vhi[r]);
+          else if (after == 3) lgkm_wait_v<3>(vlo[r], vhi[r]);
+          else lgkm_wait_v<4>(vlo[r], vhi[r]);
+        }
+      }
+      if (ph < 2) {
+        if (s == 0 && ks == 0) E::mma_first(s_acc[ph], kfr[r], qf[2 * s + ks]);
+        else E::mma_acc(s_acc[ph], kfr[r], qf[2 * s + ks]);
+      } else {
+        const i32x4 vf = i32x4{vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
+        E::mma_acc_agpr(o_acc[s], vf, pk[ph - 2][ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- an S block finished one product ago: 12 wait states, then publish the partial
+      if (m == PH || m == 2 * PH) {
+        const int kb = m / PH - 1;
+        mma_guard_s(s_acc[kb]);
+        if constexpr (DG == 2) {
+          const f32x16& x = s_acc[kb];
+          const uint32_t dst = ex_mine + kb * 4096;
+          lds_write_b128_async<0>(dst, f32x4{x[0], x[1], x[2], x[3]});
+          lds_write_b128_async<1024>(dst, f32x4{x[4], x[5], x[6], x[7]});
+          lds_write_b128_async<2048>(dst, f32x4{x[8], x[9], x[10], x[11]});
+          lds_write_b128_async<3072>(dst, f32x4{x[12], x[13], x[14], x[15]});
+        }
+      }
+      if (m == BIAS1_SLOT && has_mask)
+        load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[1][0]), ctx, key0 + 32, a.mask_kind,
+                                 a.mask_vec && !tail);
+
+      // ---- epoch boundary: the next epoch's groups become visible; the slots of the epoch before
+      // last are refilled LA epochs ahead
+      if ((m + PF) % EM == 0) {
+        const int eg = j * EPT + (m + PF) / EM;  // (m + PF) / EM == EPT: the next tile's first epoch
+        int pub = -1;  // block whose partial tiles are read after this barrier (two column groups)
+        if (DG == 2) {
+          if (m + PF == row_sm_first(0, DG, PH, EM, PF)) pub = 0;
+          if (m + PF == row_sm_first(1, DG, PH, EM, PF)) pub = 1;
+        }
+        if (eg < total_epochs) {
+          // a partial published fewer than PF products ago may still be in flight
+          if (pub >= 0 && m - (pub + 1) * PH < PF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_epoch(eg);
+          __builtin_amdgcn_s_barrier();
+          issue_epoch(eg + LA);
+        }
+        if (pub >= 0) {
+          const uint32_t src = ex_partner + pub * 4096;
+          part[pub][0] = lds_read_f4_async<0>(src);
+          part[pub][1] = lds_read_f4_async<1024>(src);
+          part[pub][2] = lds_read_f4_async<2048>(src);
+          part[pub][3] = lds_read_f4_async<3072>(src);
+        }
+      }
+
+      // ---- the fragment PF products ahead (the last ones: the next tile's first products)
+      read_frag(std::integral_constant<int, m + PF>{});
+
+      // ---- softmax pieces
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int first = row_sm_first(kb, DG, PH, EM, PF);
+        const int stride = row_sm_stride(kb, DG, PH, EM, PF);
+        // the partner's partial was read before fragment m+... whose completion was waited for
+        // just before this product: it is complete
+        if (DG == 2 && m == first) asm volatile("" : "+v"(part[kb][0]), "+v"(part[kb][1]), "+v"(part[kb][2]), "+v"(part[kb][3]));
+        if (m >= first && (m - first) % stride == 0 && (m - first) / stride < kRowSmPieces) sm_piece(kb, (m - first) / stride);
+      }
+      if constexpr (m == 2 * PH - 1) apply_rescale(0);
+      if constexpr (m == 3 * PH - 1) apply_rescale(1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  vm_wait<0>();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+  // ================= epilogue =================
+  mma_guard_all<NSUB>(o_acc);
+  const float l = sum_halves(l_lane);
+  if (row < Nq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = a.o + ((int64_t)(b * a.Hq + hq) * Nq + row) * D + col0;
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16 acc = o_acc[s];
+        i32x2 w;
+        w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
+        w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
+        *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
+      }
+    }
+    if (a.lse != nullptr && dg == 0 && hi == 0) {
+      const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
+      a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
+    }
+  }
+}
+
+}  // namespace ffpa
