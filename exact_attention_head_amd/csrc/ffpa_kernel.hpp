@@ -122,6 +122,10 @@ struct Elem;
     __device__ static inline void mma_acc_agpr(f32x16& d, const i32x4& a, const i32x4& b) {                  \
       asm volatile("s_nop 1\n\t" INSN " %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));                                 \
     }                                                                                                         \
+    /* d += a*b with d in AGPRs, operands not written by VALU instructions in the last 2 wait states */     \
+    __device__ static inline void mma_acc_agpr_nonop(f32x16& d, const i32x4& a, const i32x4& b) {            \
+      asm volatile(INSN " %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));                                                 \
+    }                                                                                                         \
   };
 FFPA_DEFINE_MMA(Bf16, "v_mfma_f32_32x32x16_bf16")
 FFPA_DEFINE_MMA(Fp16, "v_mfma_f32_32x32x16_f16")
@@ -1436,7 +1440,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
   if constexpr (use_row_kernel<D>()) {
-    hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    const bool raw = a.mask_kind == kMaskNone && !a.causal && a.Nkv % 64 == 0 && a.scale_log2 > 0.f;
+    if (raw) hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else if constexpr (Tiling<D>::RG == 1) {
     static_assert(SplitKernel<T, D>::BR == K::BR, "same query tile");
     hipLaunchKernelGGL((ffpa_fwd_split_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -103,14 +103,14 @@ constexpr bool use_row_kernel() {
   return RowTiling<D>::OK && D >= 256;
 }
 
-// s_waitcnt lgkmcnt(N) tying the fragment registers it completes.
+// s_waitcnt lgkmcnt(N) before a product whose operand fragments were read by inline assembly.
+// It names no registers: volatile assembly statements keep their order, so the product (also
+// volatile assembly) stays behind it, and declaring the fragments as outputs would make the
+// compiler treat them as freshly VALU-written and pad every product with a nop.  That nothing
+// else touches a fragment before its wait is verified on the generated code at build time.
 template <int N>
-__device__ inline void lgkm_wait_k(i32x4& f) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(f) : "n"(N));
-}
-template <int N>
-__device__ inline void lgkm_wait_v(i32x2& lo, i32x2& hi) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(lo), "+v"(hi) : "n"(N));
+__device__ inline void lgkm_wait() {
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
 }
 template <int OFF>
 __device__ inline i32x4 lds_read_b128_async(uint32_t addr) {
@@ -165,7 +165,11 @@ constexpr bool row_sm_fits(int DG, int PH, int EM, int PF) {
   return true;
 }
 
-template <typename T, int D>
+// RAW: the launch has no mask, no causal limit, whole key tiles and a positive scale, so every key
+// of every tile takes part: the row maximum is taken over the raw dot products (scaling by a
+// positive factor keeps the order) and the scale is folded into the exponent,
+// p = exp2(s * scale_log2 - m).  The launcher picks the variant.
+template <typename T, int D, bool RAW>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   using RT = RowTiling<D>;
   using E = Elem<T>;
@@ -173,7 +177,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   constexpr int DG = RT::DG, DW = RT::DW, NSUB = RT::NSUB, BR = RT::BR, GPP = RT::GPP;
   constexpr int MPT = RT::MPT, EM = RT::EM, BI = RT::BI, NG = RT::NG, LA = RT::LA, EPT = RT::EPT;
   constexpr int PF = kRowPF;     // operand fragments are read this many products ahead
-  constexpr int NFR = PF + 1;    // fragment registers in rotation
+  constexpr int NFR = 4;         // fragment registers in rotation (at least PF + 1, dividing MPT)
   constexpr int BC = 64;
   constexpr int PH = 2 * NSUB;   // products per phase
   static_assert(MPT % NFR == 0, "the fragment rotation must line up with the tile");
@@ -229,32 +233,40 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * D + col0 + hi * 8);
 #pragma unroll
     for (int k = 0; k < DW / 16; ++k) qf[k] = src[k * 2];
+    // complete here, and redefine through the assembler: the compiler then has no load of these
+    // registers to wait for inside the key loop (where it would drain the prefetch ring)
+    vm_wait<0>();
+#pragma unroll
+    for (int k = 0; k < DW / 16; ++k) asm volatile("" : "+v"(qf[k]));
   }
 
-  // ---- ring loads: in every group, wave w fills rows 16*(w&1) .. +15 of sub-tile w>>1
+  // ---- ring loads: in every group, wave w fills rows 16*(w&1) .. +15 of sub-tile w>>1, i.e. the
+  // w-th KiB of the group.  One descriptor per tensor head (its size ends at key Nkv, so rows past
+  // it read as zero); the lane's byte offset = fixed lane part + tile part + a constant per group.
   const int pst = wave >> 1;
   const int prow = 16 * (wave & 1) + (lane >> 2);
-  const uint32_t voff = (uint32_t)((prow * D + ((lane & 3) ^ ((prow >> 2) & 3)) * 8) * 2);
-  const int64_t head_elems = (int64_t)Nkv * D;
-  char* const ring_w = smem + pst * 2048 + (wave & 1) * 1024;
-  auto issue_group = [&](int j, int gi) {
-    const int ph = gi / GPP, w = gi % GPP;
-    const int key0 = j * BC + (ph & 1) * 32;
+  const uint32_t voff_lane = (uint32_t)((prow * D + ((lane & 3) ^ ((prow >> 2) & 3)) * 8) * 2);
+  const int head_bytes = (int)((int64_t)Nkv * D * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, 0x00020000);
+  char* const ring_w = smem + wave * 1024;
+  // group gi of tile j + TD, with vt = voff_lane + (byte offset of tile j)
+  auto issue_group = [&](uint32_t vt, auto td_c, auto gi_c) {
+    constexpr int TD = decltype(td_c)::value, gi = decltype(gi_c)::value;
+    constexpr int ph = gi / GPP, w = gi % GPP;
     const int col = DG == 1 ? 64 * w + 32 * pst : pst * DW + 32 * w;
-    int64_t start = (int64_t)key0 * D + col;
-    const int bytes = start < head_elems ? (int)((head_elems - start) * 2) : 0;
-    start = start < head_elems ? start : 0;
-    const uint16_t* src = (ph < 2 ? kg : vg) + start;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FFPA_LDS void*)(ring_w + (gi % NG) * 4096), 16, voff, 0, 0, 0);
+    const uint32_t cst = (uint32_t)(((TD * BC + (ph & 1) * 32) * D + col) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v, (FFPA_LDS void*)(ring_w + (gi % NG) * 4096), 16,
+                                             vt + cst, 0, 0, 0);
   };
-  // every group of global epoch eg (of tile eg / EPT), if it exists
-  auto issue_epoch = [&](int eg) {
-    if (eg >= total_epochs) return;
-    const int j = eg / EPT;
-    const int e = eg - j * EPT;
-#pragma unroll
-    for (int i = 0; i < BI; ++i) issue_group(j, e * BI + i);
+  // every group of local epoch E (E >= EPT: of a later tile) relative to tile j, if that tile exists
+  auto issue_epoch = [&](int j, uint32_t vt, auto e_c) {
+    constexpr int E = decltype(e_c)::value;
+    constexpr int TD = E / EPT, EL = E % EPT;
+    if (j + TD >= ntiles) return;
+    static_for<BI>([&](auto i_c) {
+      issue_group(vt, std::integral_constant<int, TD>{}, std::integral_constant<int, EL * BI + decltype(i_c)::value>{});
+    });
   };
   // this wave's loads of global epoch eg are complete (the LA-1 later epochs may be in flight)
   auto wait_epoch = [&](int eg) {
@@ -298,14 +310,6 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     }
   };
 
-  f32x16 o_acc[NSUB];
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    o_acc[s] = f32x16{};
-    asm volatile("" : "+a"(o_acc[s]));
-  }
-  float m_run = kNegInf;  // running reference maximum of this lane's row (log2 domain)
-  float l_lane = 0.f;     // sum of this lane's probabilities (the other half-wave holds the rest)
   const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
   const bool has_mask = a.mask_kind != kMaskNone;
 
@@ -314,18 +318,27 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const uint32_t ex_partner = ring_addr + NG * 4096 + (wave ^ 1) * 8192 + lane * 16;
 
   // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
-#pragma unroll
-  for (int e = 0; e < LA; ++e) issue_epoch(e);
+  static_for<LA>([&](auto e_c) { issue_epoch(0, voff_lane, e_c); });
   wait_epoch(0);
   __builtin_amdgcn_s_barrier();
-  issue_epoch(LA);
+  issue_epoch(0, voff_lane, std::integral_constant<int, LA>{});
   static_for<PF>([&](auto mc) { read_frag(mc); });
 
-  for (int j = 0; j < ntiles; ++j) {
+  f32x16 o_acc[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    o_acc[s] = f32x16{};
+    asm volatile("" : "+a"(o_acc[s]));
+  }
+  float m_run = kNegInf;  // running reference maximum of this lane's row (log2 domain)
+  float l_lane = 0.f;     // sum of this lane's probabilities (the other half-wave holds the rest)
+  auto tile_body = [&](const int j) {
     const int key0 = j * BC;
     const bool tail = key0 + BC > Nkv;
     const bool diag = a.causal && (key0 + BC - 1 > rw0 + off);
-    const bool edge = tail || diag;
+    const bool edge = RAW ? false : (tail || diag);
+    uint32_t vt = voff_lane + (uint32_t)(j * BC * D * 2);
+    asm volatile("" : "+v"(vt));  // keeps the per-group constants from being hoisted as 32 live registers
     LogitCtx ctx{a.mask, mask_bh, a.msq, Nq, Nkv, key0, rw0, off, a.causal, edge, a.scale_log2, l32, hi};
 
     f32x16 s_acc[2];     // S^T of the two 32-key blocks; overwritten in place by the logits
@@ -335,14 +348,26 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     bool need[2];
     i32x4 pk[2][2];      // P^T operands (bf16/fp16 pairs) of block kb, 16-key step ks
 
-    if (has_mask)
+    if (!RAW && has_mask)
       load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[0][0]), ctx, key0, a.mask_kind,
                                a.mask_vec && !tail);
 
     // softmax of block kb in pieces c = 0..8: logits of 4-key group c (0-3), the row maximum and
     // the reference decision (4), exponentials and P^T packing of group c-5 (5-8)
     auto sm_piece = [&](int kb, int c) {
-      if (c < 4) {
+      if (RAW && c < 4) {
+        const int g = c;
+        float mx = g == 0 ? kNegInf : lmax[kb];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (DG == 2) s_acc[kb][4 * g + e] += part[kb][g][e];
+          mx = __builtin_fmaxf(mx, s_acc[kb][4 * g + e]);
+        }
+        lmax[kb] = mx;
+        // stays in this slot (see the pins below)
+        if constexpr (DG == 2) asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
+        else asm volatile("" : "+v"(lmax[kb]));
+      } else if (c < 4) {
         const int g = c;
         f32x4 x;
 #pragma unroll
@@ -368,8 +393,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           s_acc[kb][4 * g + e] = x[e];
         }
         lmax[kb] = mx;
+        // Pins: the results of every piece are redefined by an empty volatile statement in their
+        // slot, so that no pass sinks the arithmetic past the branches of later slots to its use
+        // (which would bunch it up before the products and lose the overlap).
+        asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
       } else if (c == 4) {
-        const float mt = max_halves(lmax[kb]);
+        const float mt = RAW ? max_halves(lmax[kb]) * a.scale_log2 : max_halves(lmax[kb]);
         const float mo = m_run;
         const bool nd = mo != kNegInf && mt > mo + kRescaleSlack;
         const float mn = mo == kNegInf ? mt : (nd ? mt : mo);
@@ -378,18 +407,21 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         m_new[kb] = mn;
         m_run = mn;
         psum[kb] = 0.f;
+        asm volatile("" : "+v"(alpha[kb]), "+v"(m_new[kb]));
       } else {
         const int g = c - 5;
         const float mref = m_new[kb] == kNegInf ? 0.f : m_new[kb];
         f32x4 p;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(s_acc[kb][4 * g + e] - mref);
+          const float x = RAW ? __builtin_fmaf(s_acc[kb][4 * g + e], a.scale_log2, -mref) : s_acc[kb][4 * g + e] - mref;
+          p[e] = __builtin_amdgcn_exp2f(x);
           psum[kb] += p[e];
         }
         const int ks = g >> 1, h2 = g & 1;
         pk[kb][ks][2 * h2 + 0] = (int)pack2<T>(p[0], p[1]);
         pk[kb][ks][2 * h2 + 1] = (int)pack2<T>(p[2], p[3]);
+        if (h2 == 1) asm volatile("" : "+v"(pk[kb][ks]), "+v"(psum[kb]));
       }
     };
     // l and O follow block kb's new reference (O holds exactly the blocks before kb)
@@ -415,22 +447,19 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         int after = 0;
 #pragma unroll
         for (int k = 1; k < PF; ++k) after += ((m + k) % MPT) / PH < 2 ? 1 : 2;
-        if (ph < 2) {
-          if (after <= 2) lgkm_wait_k<2>(kfr[r]);
-          else if (after == 3) lgkm_wait_k<3>(kfr[r]);
-          else lgkm_wait_k<4>(kfr[r]);
-        } else {
-          if (after <= 2) lgkm_wait_v<2>(vlo[r], vhi[r]);
-          else if (after == 3) lgkm_wait_v<3>(vlo[r], vhi[r]);
-          else lgkm_wait_v<4>(vlo[r], vhi[r]);
-        }
+        if (after <= 1) lgkm_wait<1>();
+        else if (after == 2) lgkm_wait<2>();
+        else if (after == 3) lgkm_wait<3>();
+        else lgkm_wait<4>();
       }
       if (ph < 2) {
         if (s == 0 && ks == 0) E::mma_first(s_acc[ph], kfr[r], qf[2 * s + ks]);
         else E::mma_acc(s_acc[ph], kfr[r], qf[2 * s + ks]);
       } else {
         const i32x4 vf = i32x4{vlo[r][0], vlo[r][1], vhi[r][0], vhi[r][1]};
-        E::mma_acc_agpr(o_acc[s], vf, pk[ph - 2][ks]);
+        // the probabilities were packed by VALU instructions before the phase began
+        if constexpr (s == 0 && ks == 0) E::mma_acc_agpr(o_acc[s], vf, pk[ph - 2][ks]);
+        else E::mma_acc_agpr_nonop(o_acc[s], vf, pk[ph - 2][ks]);
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -447,7 +476,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           lds_write_b128_async<3072>(dst, f32x4{x[12], x[13], x[14], x[15]});
         }
       }
-      if (m == BIAS1_SLOT && has_mask)
+      if (!RAW && m == BIAS1_SLOT && has_mask)
         load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[1][0]), ctx, key0 + 32, a.mask_kind,
                                  a.mask_vec && !tail);
 
@@ -465,7 +494,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           if (pub >= 0 && m - (pub + 1) * PH < PF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           wait_epoch(eg);
           __builtin_amdgcn_s_barrier();
-          issue_epoch(eg + LA);
+          issue_epoch(j, vt, std::integral_constant<int, (m + PF) / EM + LA>{});
         }
         if (pub >= 0) {
           const uint32_t src = ex_partner + pub * 4096;
@@ -493,7 +522,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       if constexpr (m == 3 * PH - 1) apply_rescale(1);
       __builtin_amdgcn_sched_barrier(0);
     });
-  }
+  };
+  for (int j = 0; j < ntiles; ++j) tile_body(j);
   vm_wait<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
@@ -503,17 +533,18 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   if (row < Nq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     uint16_t* orow = a.o + ((int64_t)(b * a.Hq + hq) * Nq + row) * D + col0;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
+    static_for<NSUB>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16 acc = o_acc[s];
+        const f32x16& acc = o_acc[s];
         i32x2 w;
         w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
         w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
         *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);  // one column block at a time: few registers in flight
+    });
     if (a.lse != nullptr && dg == 0 && hi == 0) {
       const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
       a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
