@@ -8,15 +8,17 @@
 // ("Split-D and TiledMMA") sized for a 512-register CDNA4 lane instead of the pages' 255-register
 // NVIDIA thread.
 //
-// Split-D staging.  K and V reach the matrix cores through a ring of 4 KiB LDS groups, each made
-// of two [32 keys][32 columns] sub-tiles (64-byte rows, 16-byte chunks swizzled by
-// chunk ^ ((row >> 2) & 3)), filled with buffer_load_dwordx4 ... lds (one instruction per wave per
-// group; keys past Nkv read as zero through the descriptor's range check).  A 64-key tile is
-// consumed in four phases - K of keys 0-31, K of keys 32-63, V of keys 0-31, V of keys 32-63 -
-// each streaming the wave's columns in 32-column steps, two products per step.  The ring is
-// shared by the four waves and advanced in epochs of EM products: one s_barrier per epoch makes
-// the next epoch's groups visible and frees the slots of the epoch before last, which are then
-// refilled LA epochs ahead.
+// Split-D staging.  K and V reach the matrix cores through a ring of LDS groups; a group holds one
+// [32 keys][64 columns] sub-tile per column group (128-byte rows of eight 16-byte chunks, chunk c
+// of row r stored at position c ^ pi((r >> 1) & 7) with pi(x) = ((x & 1) << 2) | (x >> 1), which
+// keeps both the operand reads and the transposed reads free of bank conflicts).  The groups are
+// filled with buffer_load_dwordx4 ... lds, one instruction per wave per sub-tile covering eight
+// whole 128-byte rows (whole cache lines; keys past Nkv read as zero through the descriptor's
+// range check).  A 64-key tile is consumed in four phases - K of keys 0-31, K of keys 32-63, V of
+// keys 0-31, V of keys 32-63 - each streaming the wave's columns in 32-column steps, two products
+// per step, two steps per group.  The ring is shared by the four waves and advanced in epochs of
+// EM products: one s_barrier per epoch makes the next epoch's groups visible and frees the slots
+// of the epoch before last, which are then refilled LA epochs ahead.
 //
 // Products.  S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16 (lane l <-> query row l % 32,
 // so row statistics are lane-local plus one v_permlane32_swap); the operand fragments come from
@@ -49,17 +51,18 @@ struct RingPlan {
   int em, ng;
 };
 
-constexpr RingPlan choose_ring(int GT, int MPG, int MPT, int exch_bytes) {
+constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes) {
   RingPlan best{0, 0};
   int best_score = -1;
   const int ems[2] = {16, 8};
   for (int i = 0; i < 2; ++i) {
     const int em = ems[i];
-    if (MPT % em != 0 || em % MPG != 0) continue;
-    const int bi = em / MPG;  // groups per epoch
+    if (MPT % em != 0) continue;
+    const int bi = em / 4;  // groups per epoch (four products per wave per group)
     for (int ng = 40; ng >= bi; --ng) {
       if (ng % bi != 0 || GT % ng != 0) continue;
-      if (ng * 4096 + exch_bytes > 160 * 1024) continue;
+      if (ng * DG * 4096 + exch_bytes > 160 * 1024) continue;
+      if (DG == 2 && ng * 4096 > 65536) continue;  // each column group's sub-tiles in one 64 KiB window
       const int ne = ng / bi;
       if (ne < 4) continue;
       const int ahead = (ne - 2) * em;  // products of lookahead
@@ -81,20 +84,20 @@ struct RowTiling {
   static constexpr int NSUB = DW / 32;          // 32-column steps per phase
   static constexpr int RG = 4 / DG;             // row groups
   static constexpr int BR = 32 * RG;            // query rows per workgroup
-  static constexpr int GT = 2 * NSUB * DG;      // groups per 64-key tile
-  static constexpr int GPP = GT / 4;            // groups per phase
+  static constexpr int GPP = NSUB / 2;          // groups per phase (64 columns each)
+  static constexpr int GT = 4 * GPP;            // groups per 64-key tile
   static constexpr int MPT = 8 * NSUB;          // products per wave per tile
-  static constexpr int MPG = 4 / DG;            // products per wave per group
   static constexpr int EXCH = DG == 2 ? 4 * 2 * 4096 : 0;  // partial-S exchange: [wave][block][4 KiB]
-  static constexpr RingPlan PLAN = choose_ring(GT, MPG, MPT, EXCH);
+  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH);
   static constexpr int EM = PLAN.em;
   static constexpr int NG = PLAN.ng;
-  static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB >= 2;
-  static constexpr int BI = OK ? EM / MPG : 1;  // groups per epoch
+  static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB % 2 == 0 && NSUB >= 2;
+  static constexpr int BI = OK ? EM / 4 : 1;    // groups per epoch
   static constexpr int NE = OK ? NG / BI : 1;   // epochs held by the ring
   static constexpr int LA = NE - 2;             // epochs of load lookahead
   static constexpr int EPT = OK ? MPT / EM : 1; // epochs per tile
-  static constexpr int LDS_BYTES = NG * 4096 + EXCH;
+  static constexpr int RING = NG * DG * 4096;   // ring bytes: [column group][slot][4 KiB]
+  static constexpr int LDS_BYTES = RING + EXCH;
 };
 
 // The head dims that run the row kernel (the others keep the column-split kernels).
@@ -151,19 +154,29 @@ constexpr int row_sm_first(int kb, int DG, int PH, int EM, int PF) {
   while (bs < p0) bs += EM;
   return bs + PF;
 }
-constexpr int kRowSmPieces = 9;
-constexpr int row_sm_stride(int kb, int DG, int PH, int EM, int PF) {
-  const int span = (kb + 2) * PH - 2 - row_sm_first(kb, DG, PH, EM, PF);
-  return span >= 2 * kRowSmPieces ? 2 : 1;
+// Softmax micro-pieces of one 32-key block (each a few VALU instructions, so that no gap between
+// two products holds more than the matrix core's shadow): logits and row maximum (4 raw pieces,
+// one per 4-key group, or 8 when bias, masking and scaling are applied, two keys each), the
+// maximum across the half-waves and the reference decision (3), then the exponential, row sum and
+// packing of one key each (16).
+constexpr int row_sm_logit_pieces(bool raw) { return raw ? 4 : 8; }
+constexpr int row_sm_pieces(bool raw) { return row_sm_logit_pieces(raw) + 3 + 16; }
+// the window a block's pieces are spread over: first .. last slot (inclusive)
+constexpr int row_sm_last(int kb, int PH) { return (kb + 2) * PH - 2; }
+// slot of piece k of block kb: evenly spread over the window (several per slot if it is short)
+constexpr int row_sm_slot(int kb, int k, bool raw, int DG, int PH, int EM, int PF) {
+  const int first = row_sm_first(kb, DG, PH, EM, PF);
+  const int w = row_sm_last(kb, PH) - first + 1;
+  return first + (k * w) / row_sm_pieces(raw);
 }
-// every piece of both blocks ends before the products that consume the block's probabilities
 constexpr bool row_sm_fits(int DG, int PH, int EM, int PF) {
-  for (int kb = 0; kb < 2; ++kb) {
-    const int last = row_sm_first(kb, DG, PH, EM, PF) + (kRowSmPieces - 1) * row_sm_stride(kb, DG, PH, EM, PF);
-    if (last > (kb + 2) * PH - 2) return false;
-  }
+  for (int kb = 0; kb < 2; ++kb)
+    if (row_sm_first(kb, DG, PH, EM, PF) > row_sm_last(kb, PH)) return false;
   return true;
 }
+// Slot at which load i of the epoch refilled after the barrier at slot bs is issued: spread over
+// the slots that follow the barrier, within the tile.
+constexpr int row_load_slot(int bs, int i, int MPT) { return bs + 1 + i < MPT ? bs + 1 + i : MPT - 1; }
 
 // RAW: the launch has no mask, no causal limit, whole key tiles and a positive scale, so every key
 // of every tile takes part: the row maximum is taken over the raw dot products (scaling by a
@@ -176,17 +189,21 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   static_assert(RT::OK, "no ring plan for this head dim");
   constexpr int DG = RT::DG, DW = RT::DW, NSUB = RT::NSUB, BR = RT::BR, GPP = RT::GPP;
   constexpr int MPT = RT::MPT, EM = RT::EM, BI = RT::BI, NG = RT::NG, LA = RT::LA, EPT = RT::EPT;
+  constexpr int CGB = NG * 4096;  // bytes of one column group's sub-tiles in the ring
   constexpr int PF = kRowPF;     // operand fragments are read this many products ahead
   constexpr int NFR = 4;         // fragment registers in rotation (at least PF + 1, dividing MPT)
   constexpr int BC = 64;
   constexpr int PH = 2 * NSUB;   // products per phase
   static_assert(MPT % NFR == 0, "the fragment rotation must line up with the tile");
   static_assert(PF < EM && LA >= 2, "ring plan");
-  static_assert(NG * 4096 <= 2 * 65536, "two 64 KiB LDS address windows");
+  static_assert(RT::RING <= 2 * 65536 && (DG == 1 || CGB <= 65536), "LDS address windows");
   static_assert(row_sm_fits(DG, PH, EM, PF), "softmax schedule does not fit the phases");
+  constexpr int NLP = row_sm_logit_pieces(RAW);
+  constexpr int NSP = row_sm_pieces(RAW);
   // the second block's mask biases are requested once the first block's logits are formed
-  constexpr int BIAS1_SLOT = row_sm_first(0, DG, PH, EM, PF) + 4 * row_sm_stride(0, DG, PH, EM, PF);
+  constexpr int BIAS1_SLOT = row_sm_slot(0, NLP, RAW, DG, PH, EM, PF);
   static_assert(BIAS1_SLOT < row_sm_first(1, DG, PH, EM, PF), "mask biases before their use");
+  static_assert(BI + 1 < EM, "the loads after a barrier end before the next one");
 
   __shared__ __attribute__((aligned(1024))) char smem[RT::LDS_BYTES];
 
@@ -240,54 +257,65 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     for (int k = 0; k < DW / 16; ++k) asm volatile("" : "+v"(qf[k]));
   }
 
-  // ---- ring loads: in every group, wave w fills rows 16*(w&1) .. +15 of sub-tile w>>1, i.e. the
-  // w-th KiB of the group.  One descriptor per tensor head (its size ends at key Nkv, so rows past
-  // it read as zero); the lane's byte offset = fixed lane part + tile part + a constant per group.
-  const int pst = wave >> 1;
-  const int prow = 16 * (wave & 1) + (lane >> 2);
-  const uint32_t voff_lane = (uint32_t)((prow * D + ((lane & 3) ^ ((prow >> 2) & 3)) * 8) * 2);
+  // ---- ring loads: wave w fills rows 8w .. 8w+7 of every sub-tile (its w-th KiB): lane t takes
+  // row 8w + t/8 and stores physical chunk t%8, i.e. logical chunk (t%8) ^ pi((row >> 1) & 7).
+  // One descriptor per tensor head (its size ends at key Nkv, so rows past it read as zero); the
+  // lane's byte offset = fixed lane part + tile part + a constant per group.
+  const int prow = 8 * wave + (lane >> 3);
+  auto pi7 = [](int x) { return ((x & 1) << 2) | (x >> 1); };
+  const uint32_t voff_lane = (uint32_t)((prow * D + ((lane & 7) ^ pi7((prow >> 1) & 7)) * 8) * 2);
   const int head_bytes = (int)((int64_t)Nkv * D * 2);
   const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, 0x00020000);
   char* const ring_w = smem + wave * 1024;
-  // group gi of tile j + TD, with vt = voff_lane + (byte offset of tile j)
-  auto issue_group = [&](uint32_t vt, auto td_c, auto gi_c) {
-    constexpr int TD = decltype(td_c)::value, gi = decltype(gi_c)::value;
+  // sub-tile of column group cg of group gi of tile j + TD, with vt = voff_lane + (byte offset of tile j)
+  auto issue_sub = [&](uint32_t vt, auto td_c, auto gi_c, auto cg_c) {
+    constexpr int TD = decltype(td_c)::value, gi = decltype(gi_c)::value, cg = decltype(cg_c)::value;
     constexpr int ph = gi / GPP, w = gi % GPP;
-    const int col = DG == 1 ? 64 * w + 32 * pst : pst * DW + 32 * w;
-    const uint32_t cst = (uint32_t)(((TD * BC + (ph & 1) * 32) * D + col) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v, (FFPA_LDS void*)(ring_w + (gi % NG) * 4096), 16,
-                                             vt + cst, 0, 0, 0);
+    constexpr uint32_t cst = (uint32_t)(((TD * BC + (ph & 1) * 32) * D + cg * DW + 64 * w) * 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v,
+                                             (FFPA_LDS void*)(ring_w + cg * CGB + (gi % NG) * 4096), 16, vt + cst, 0,
+                                             0, 0);
   };
-  // every group of local epoch E (E >= EPT: of a later tile) relative to tile j, if that tile exists
-  auto issue_epoch = [&](int j, uint32_t vt, auto e_c) {
-    constexpr int E = decltype(e_c)::value;
+  auto issue_group = [&](uint32_t vt, auto td_c, auto gi_c) {
+    static_for<DG>([&](auto cg_c) { issue_sub(vt, td_c, gi_c, cg_c); });
+  };
+  // group i of local epoch E (E >= EPT: of a later tile) relative to tile j, if that tile exists
+  auto issue_epoch_group = [&](int j, uint32_t vt, auto e_c, auto i_c) {
+    constexpr int E = decltype(e_c)::value, I = decltype(i_c)::value;
     constexpr int TD = E / EPT, EL = E % EPT;
     if (j + TD >= ntiles) return;
-    static_for<BI>([&](auto i_c) {
-      issue_group(vt, std::integral_constant<int, TD>{}, std::integral_constant<int, EL * BI + decltype(i_c)::value>{});
-    });
+    issue_group(vt, std::integral_constant<int, TD>{}, std::integral_constant<int, EL * BI + I>{});
+  };
+  auto issue_epoch = [&](int j, uint32_t vt, auto e_c) {
+    static_for<BI>([&](auto i_c) { issue_epoch_group(j, vt, e_c, i_c); });
   };
   // this wave's loads of global epoch eg are complete (the LA-1 later epochs may be in flight)
   auto wait_epoch = [&](int eg) {
-    if (eg + LA - 1 < total_epochs) vm_wait<(LA - 1) * BI>();
+    if (eg + LA - 1 < total_epochs) vm_wait<(LA - 1) * BI * DG>();
     else vm_wait<0>();
   };
 
   // ---- operand fragment addresses (per lane; slot and step offsets are immediates)
   const uint32_t ring_addr = lds_addr(smem);
+  const uint32_t cgb = ring_addr + dg * CGB;  // this wave's column group's sub-tiles
   const int g16 = lane >> 4, i16 = lane & 15;
   const int tr_chunk = 2 * (g16 & 1) + ((i16 & 3) >> 1);
   const int tr_within = 8 * (i16 & 1);
   const int vkeyA = (g16 >> 1) * 4 + (i16 >> 2);
-  const uint32_t sub = ring_addr + dg * 2048;  // two column groups: this wave's sub-tile of each group
-  // K fragment (32 keys x 16 columns, 16-column step ks): key l32, chunk 2*ks + hi
-  const uint32_t ka[2] = {sub + l32 * 64 + swz(l32, hi) * 16, sub + l32 * 64 + swz(l32, 2 + hi) * 16};
-  // V^T fragment (16-key step ks): two transposed reads, keys vkeyA and vkeyA + 8 (+16 per step)
-  const uint32_t va = sub + vkeyA * 64 + swz(vkeyA, tr_chunk) * 16 + tr_within;
-  const uint32_t vb = sub + (vkeyA + 8) * 64 + swz(vkeyA + 8, tr_chunk) * 16 + tr_within;
+  // K fragment (32 keys x 16 columns; 32-column half h of the sub-tile, 16-column step ks): key
+  // l32, logical chunk 4h + 2ks + hi.  V^T fragment (half h, 16-key step ks): two transposed reads
+  // of keys vkeyA and vkeyA + 8 (+16 per step, an immediate: the swizzle's row term repeats every
+  // 16 rows), logical chunk 4h + tr_chunk.
+  uint32_t ka[2][2], va[2], vb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) ka[h][ks] = cgb + l32 * 128 + ((4 * h + 2 * ks + hi) ^ pi7((l32 >> 1) & 7)) * 16;
+    va[h] = cgb + vkeyA * 128 + ((4 * h + tr_chunk) ^ pi7((vkeyA >> 1) & 7)) * 16 + tr_within;
+    vb[h] = cgb + (vkeyA + 8) * 128 + ((4 * h + tr_chunk) ^ pi7(((vkeyA + 8) >> 1) & 7)) * 16 + tr_within;
+  }
 
-  const uint32_t ka0h = ka[0] + 65536, ka1h = ka[1] + 65536, vah = va + 65536, vbh = vb + 65536;
   i32x4 kfr[NFR];
   i32x2 vlo[NFR], vhi[NFR];
   // fragment of product M of a tile (M >= MPT: the next tile's product M - MPT, same slots); the
@@ -296,17 +324,17 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     constexpr int M = decltype(mc)::value;
     constexpr int mm = M % MPT;
     constexpr int ph = mm / PH, s = (mm % PH) / 2, ks = mm % 2;
-    constexpr int gi = ph * GPP + (DG == 1 ? s / 2 : s);
-    constexpr int ofs = (gi % NG) * 4096 + (DG == 1 ? (s & 1) * 2048 : 0);
-    constexpr bool upper = ofs >= 65536;
+    constexpr int gi = ph * GPP + s / 2, h = s & 1;
+    constexpr int ofs = (gi % NG) * 4096;
+    constexpr uint32_t win = ofs >= 65536 ? 65536u : 0u;
     constexpr int r = M % NFR;
     if constexpr (ph < 2) {
-      const uint32_t base = ks == 0 ? (upper ? ka0h : ka[0]) : (upper ? ka1h : ka[1]);
-      kfr[r] = lds_read_b128_async<(ofs & 65535)>(base);
+      kfr[r] = lds_read_b128_async<(ofs & 65535)>(ka[h][ks] + win);
     } else {
-      constexpr int o2 = (ofs & 65535) + ks * 1024;
-      vlo[r] = lds_read_tr_async<o2>(upper ? vah : va);
-      vhi[r] = lds_read_tr_async<o2>(upper ? vbh : vb);
+      constexpr int o2 = (ofs & 65535) + ks * 2048;
+      static_assert(o2 < 65536, "ds offset field");
+      vlo[r] = lds_read_tr_async<o2>(va[h] + win);
+      vhi[r] = lds_read_tr_async<o2>(vb[h] + win);
     }
   };
 
@@ -314,8 +342,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const bool has_mask = a.mask_kind != kMaskNone;
 
   // partial-S exchange (two column groups): [wave][block][4 x 1 KiB], 16 bytes per lane
-  const uint32_t ex_mine = ring_addr + NG * 4096 + wave * 8192 + lane * 16;
-  const uint32_t ex_partner = ring_addr + NG * 4096 + (wave ^ 1) * 8192 + lane * 16;
+  const uint32_t ex_mine = ring_addr + RT::RING + wave * 8192 + lane * 16;
+  const uint32_t ex_partner = ring_addr + RT::RING + (wave ^ 1) * 8192 + lane * 16;
 
   // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
   static_for<LA>([&](auto e_c) { issue_epoch(0, voff_lane, e_c); });
@@ -352,76 +380,75 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[0][0]), ctx, key0, a.mask_kind,
                                a.mask_vec && !tail);
 
-    // softmax of block kb in pieces c = 0..8: logits of 4-key group c (0-3), the row maximum and
-    // the reference decision (4), exponentials and P^T packing of group c-5 (5-8)
-    auto sm_piece = [&](int kb, int c) {
-      if (RAW && c < 4) {
-        const int g = c;
-        float mx = g == 0 ? kNegInf : lmax[kb];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (DG == 2) s_acc[kb][4 * g + e] += part[kb][g][e];
-          mx = __builtin_fmaxf(mx, s_acc[kb][4 * g + e]);
-        }
-        lmax[kb] = mx;
-        // stays in this slot (see the pins below)
-        if constexpr (DG == 2) asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
-        else asm volatile("" : "+v"(lmax[kb]));
-      } else if (c < 4) {
-        const int g = c;
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = s_acc[kb][4 * g + e];
-        if constexpr (DG == 2) x = x + part[kb][g];
-        x = x * a.scale_log2;
-        if (has_mask) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = __builtin_fmaf(bias[kb][g][e], kLog2e, x[e]);
-        }
-        if (edge) {
+    float mt[2], m_old[2], mref[2], pv[2][2];
+    // softmax micro-piece k of block kb (see row_sm_pieces)
+    auto sm_micro = [&](int kb, int k) {
+      if (k < NLP) {
+        if constexpr (RAW) {
+          const int g = k;
+          float mx = g == 0 ? kNegInf : lmax[kb];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kk = key0 + 32 * kb + 8 * g + 4 * hi + e;
-            const bool dead = kk >= Nkv || (a.causal && kk > row + off);
-            x[e] = dead ? kNegInf : x[e];
+            if constexpr (DG == 2) s_acc[kb][4 * g + e] += part[kb][g][e];
+            mx = __builtin_fmaxf(mx, s_acc[kb][4 * g + e]);
           }
-        }
-        float mx = g == 0 ? kNegInf : lmax[kb];
+          lmax[kb] = mx;
+          // Pins: the results of every piece are redefined by an empty volatile statement in its
+          // slot, so that no pass sinks the arithmetic past the branches of later slots to its
+          // use (which would bunch it up in front of the products and lose the overlap).
+          if constexpr (DG == 2) asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
+          else asm volatile("" : "+v"(lmax[kb]));
+        } else {
+          const int g = k >> 1, e0 = 2 * (k & 1);
+          float mx = k == 0 ? kNegInf : lmax[kb];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mx = __builtin_fmaxf(mx, x[e]);
-          s_acc[kb][4 * g + e] = x[e];
+          for (int e = e0; e < e0 + 2; ++e) {
+            float x = s_acc[kb][4 * g + e];
+            if constexpr (DG == 2) x += part[kb][g][e];
+            x *= a.scale_log2;
+            if (has_mask) x = __builtin_fmaf(bias[kb][g][e], kLog2e, x);
+            if (edge) {
+              const int kk = key0 + 32 * kb + 8 * g + 4 * hi + e;
+              const bool dead = kk >= Nkv || (a.causal && kk > row + off);
+              x = dead ? kNegInf : x;
+            }
+            mx = __builtin_fmaxf(mx, x);
+            s_acc[kb][4 * g + e] = x;
+          }
+          lmax[kb] = mx;
+          asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
         }
-        lmax[kb] = mx;
-        // Pins: the results of every piece are redefined by an empty volatile statement in their
-        // slot, so that no pass sinks the arithmetic past the branches of later slots to its use
-        // (which would bunch it up before the products and lose the overlap).
-        asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
-      } else if (c == 4) {
-        const float mt = RAW ? max_halves(lmax[kb]) * a.scale_log2 : max_halves(lmax[kb]);
-        const float mo = m_run;
-        const bool nd = mo != kNegInf && mt > mo + kRescaleSlack;
-        const float mn = mo == kNegInf ? mt : (nd ? mt : mo);
+      } else if (k == NLP) {
+        mt[kb] = RAW ? max_halves(lmax[kb]) * a.scale_log2 : max_halves(lmax[kb]);
+        m_old[kb] = m_run;
+        asm volatile("" : "+v"(mt[kb]), "+v"(m_old[kb]));
+      } else if (k == NLP + 1) {
+        const float mo = m_old[kb];
+        const bool nd = mo != kNegInf && mt[kb] > mo + kRescaleSlack;
+        const float mn = mo == kNegInf ? mt[kb] : (nd ? mt[kb] : mo);
         need[kb] = nd;
-        alpha[kb] = nd ? __builtin_amdgcn_exp2f(mo - mn) : 1.f;
         m_new[kb] = mn;
         m_run = mn;
+        mref[kb] = mn == kNegInf ? 0.f : mn;
+        asm volatile("" : "+v"(m_new[kb]), "+v"(mref[kb]));
+      } else if (k == NLP + 2) {
+        alpha[kb] = need[kb] ? __builtin_amdgcn_exp2f(m_old[kb] - m_new[kb]) : 1.f;
         psum[kb] = 0.f;
-        asm volatile("" : "+v"(alpha[kb]), "+v"(m_new[kb]));
+        asm volatile("" : "+v"(alpha[kb]), "+v"(psum[kb]));
       } else {
-        const int g = c - 5;
-        const float mref = m_new[kb] == kNegInf ? 0.f : m_new[kb];
-        f32x4 p;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = RAW ? __builtin_fmaf(s_acc[kb][4 * g + e], a.scale_log2, -mref) : s_acc[kb][4 * g + e] - mref;
-          p[e] = __builtin_amdgcn_exp2f(x);
-          psum[kb] += p[e];
+        const int i = k - NLP - 3;  // key 0..15 of this lane's 16 in the block
+        const int g = i >> 2, e = i & 3;
+        const float sv = s_acc[kb][4 * g + e];
+        const float x = RAW ? __builtin_fmaf(sv, a.scale_log2, -mref[kb]) : sv - mref[kb];
+        const float p = __builtin_amdgcn_exp2f(x);
+        psum[kb] += p;
+        if ((e & 1) == 0) {
+          pv[kb][0] = p;
+          asm volatile("" : "+v"(pv[kb][0]), "+v"(psum[kb]));
+        } else {
+          pk[kb][g >> 1][2 * (g & 1) + (e >> 1)] = (int)pack2<T>(pv[kb][0], p);
+          asm volatile("" : "+v"(pk[kb][g >> 1]), "+v"(psum[kb]));
         }
-        const int ks = g >> 1, h2 = g & 1;
-        pk[kb][ks][2 * h2 + 0] = (int)pack2<T>(p[0], p[1]);
-        pk[kb][ks][2 * h2 + 1] = (int)pack2<T>(p[2], p[3]);
-        if (h2 == 1) asm volatile("" : "+v"(pk[kb][ks]), "+v"(psum[kb]));
       }
     };
     // l and O follow block kb's new reference (O holds exactly the blocks before kb)
@@ -494,7 +521,6 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           if (pub >= 0 && m - (pub + 1) * PH < PF) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           wait_epoch(eg);
           __builtin_amdgcn_s_barrier();
-          issue_epoch(j, vt, std::integral_constant<int, (m + PF) / EM + LA>{});
         }
         if (pub >= 0) {
           const uint32_t src = ex_partner + pub * 4096;
@@ -505,18 +531,31 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         }
       }
 
+      // ---- refills of the slots freed by the last barrier, spread over the following slots
+      static_for<EPT + 1>([&](auto eb_c) {
+        constexpr int eb = decltype(eb_c)::value;  // barrier of local epoch eb sits at slot eb*EM - PF
+        constexpr int bs = eb * EM - PF;
+        if constexpr (bs >= 0 && bs < MPT) {
+          static_for<BI>([&](auto i_c) {
+            if constexpr (row_load_slot(bs, decltype(i_c)::value, MPT) == m)
+              issue_epoch_group(j, vt, std::integral_constant<int, eb + LA>{}, i_c);
+          });
+        }
+      });
+
       // ---- the fragment PF products ahead (the last ones: the next tile's first products)
       read_frag(std::integral_constant<int, m + PF>{});
 
-      // ---- softmax pieces
+      // ---- softmax micro-pieces
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int first = row_sm_first(kb, DG, PH, EM, PF);
-        const int stride = row_sm_stride(kb, DG, PH, EM, PF);
-        // the partner's partial was read before fragment m+... whose completion was waited for
-        // just before this product: it is complete
-        if (DG == 2 && m == first) asm volatile("" : "+v"(part[kb][0]), "+v"(part[kb][1]), "+v"(part[kb][2]), "+v"(part[kb][3]));
-        if (m >= first && (m - first) % stride == 0 && (m - first) / stride < kRowSmPieces) sm_piece(kb, (m - first) / stride);
+        // the partner's partial was read before a fragment whose completion was waited for just
+        // before this product: it is complete
+        if (DG == 2 && m == row_sm_first(kb, DG, PH, EM, PF))
+          asm volatile("" : "+v"(part[kb][0]), "+v"(part[kb][1]), "+v"(part[kb][2]), "+v"(part[kb][3]));
+#pragma unroll
+        for (int k = 0; k < NSP; ++k)
+          if (row_sm_slot(kb, k, RAW, DG, PH, EM, PF) == m) sm_micro(kb, k);
       }
       if constexpr (m == 2 * PH - 1) apply_rescale(0);
       if constexpr (m == 3 * PH - 1) apply_rescale(1);
