@@ -1440,9 +1440,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
   if constexpr (use_row_kernel<D>()) {
-    const bool raw = a.mask_kind == kMaskNone && !a.causal && a.Nkv % 64 == 0 && a.scale_log2 > 0.f;
-    if (raw) hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    const bool plain = a.mask_kind == kMaskNone && a.scale_log2 > 0.f;
+    if (plain && !a.causal && a.Nkv % 64 == 0)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (plain && a.causal)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowCausal>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else if constexpr (Tiling<D>::RG == 1) {
     static_assert(SplitKernel<T, D>::BR == K::BR, "same query tile");
     hipLaunchKernelGGL((ffpa_fwd_split_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -178,11 +178,17 @@ constexpr bool row_sm_fits(int DG, int PH, int EM, int PF) {
 // the slots that follow the barrier, within the tile.
 constexpr int row_load_slot(int bs, int i, int MPT) { return bs + 1 + i < MPT ? bs + 1 + i : MPT - 1; }
 
-// RAW: the launch has no mask, no causal limit, whole key tiles and a positive scale, so every key
-// of every tile takes part: the row maximum is taken over the raw dot products (scaling by a
+// Tile variants.  A raw tile has every key taking part for every row of the workgroup and no mask,
+// under a positive scale: the row maximum is taken over the raw dot products (scaling by a
 // positive factor keeps the order) and the scale is folded into the exponent,
-// p = exp2(s * scale_log2 - m).  The launcher picks the variant.
-template <typename T, int D, bool RAW>
+// p = exp2(s * scale_log2 - m).  Other tiles form the logits explicitly (scale, mask bias, -inf
+// for keys past Nkv or past the causal limit).  MODE selects the kernel's tiles: kRowGeneral (every
+// tile explicit), kRowRaw (every tile raw: no mask, no causal limit, whole tiles), kRowCausal (no
+// mask, causal: the tiles below the workgroup's diagonal raw, the diagonal ones explicit, in two
+// successive loops).  The launcher picks the variant.
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowCausal = 2 };
+
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   using RT = RowTiling<D>;
   using E = Elem<T>;
@@ -198,10 +204,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   static_assert(PF < EM && LA >= 2, "ring plan");
   static_assert(RT::RING <= 2 * 65536 && (DG == 1 || CGB <= 65536), "LDS address windows");
   static_assert(row_sm_fits(DG, PH, EM, PF), "softmax schedule does not fit the phases");
-  constexpr int NLP = row_sm_logit_pieces(RAW);
-  constexpr int NSP = row_sm_pieces(RAW);
   // the second block's mask biases are requested once the first block's logits are formed
-  constexpr int BIAS1_SLOT = row_sm_slot(0, NLP, RAW, DG, PH, EM, PF);
+  constexpr int BIAS1_SLOT = row_sm_slot(0, row_sm_logit_pieces(false), false, DG, PH, EM, PF);
   static_assert(BIAS1_SLOT < row_sm_first(1, DG, PH, EM, PF), "mask biases before their use");
   static_assert(BI + 1 < EM, "the loads after a barrier end before the next one");
 
@@ -360,11 +364,19 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   }
   float m_run = kNegInf;  // running reference maximum of this lane's row (log2 domain)
   float l_lane = 0.f;     // sum of this lane's probabilities (the other half-wave holds the rest)
-  auto tile_body = [&](const int j) {
+  auto tile_body = [&](const int j, auto raw_c) {
+    constexpr bool RAW = decltype(raw_c)::value;
+    constexpr int NLP = row_sm_logit_pieces(RAW);
+    constexpr int NSP = row_sm_pieces(RAW);
     const int key0 = j * BC;
     const bool tail = key0 + BC > Nkv;
     const bool diag = a.causal && (key0 + BC - 1 > rw0 + off);
     const bool edge = RAW ? false : (tail || diag);
+    // last key of the tile this lane's row may see (keys past Nkv and past the causal limit are
+    // excluded), relative to the tile's first key
+    int edge_lim = Nkv - 1;
+    if (a.causal) edge_lim = edge_lim < row + off ? edge_lim : row + off;
+    edge_lim -= key0;
     uint32_t vt = voff_lane + (uint32_t)(j * BC * D * 2);
     asm volatile("" : "+v"(vt));  // keeps the per-group constants from being hoisted as 32 live registers
     LogitCtx ctx{a.mask, mask_bh, a.msq, Nq, Nkv, key0, rw0, off, a.causal, edge, a.scale_log2, l32, hi};
@@ -400,6 +412,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           else asm volatile("" : "+v"(lmax[kb]));
         } else {
           const int g = k >> 1, e0 = 2 * (k & 1);
+          // key 8g + e of this lane's block-relative keys (8g + 4hi + e) is excluded past lim
+          const int lim = edge_lim - 32 * kb - 4 * hi;
           float mx = k == 0 ? kNegInf : lmax[kb];
 #pragma unroll
           for (int e = e0; e < e0 + 2; ++e) {
@@ -407,11 +421,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
             if constexpr (DG == 2) x += part[kb][g][e];
             x *= a.scale_log2;
             if (has_mask) x = __builtin_fmaf(bias[kb][g][e], kLog2e, x);
-            if (edge) {
-              const int kk = key0 + 32 * kb + 8 * g + 4 * hi + e;
-              const bool dead = kk >= Nkv || (a.causal && kk > row + off);
-              x = dead ? kNegInf : x;
-            }
+            if (edge) x = 8 * g + e > lim ? kNegInf : x;
             mx = __builtin_fmaxf(mx, x);
             s_acc[kb][4 * g + e] = x;
           }
@@ -562,7 +572,17 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  for (int j = 0; j < ntiles; ++j) tile_body(j);
+  if constexpr (MODE == kRowRaw) {
+    for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
+  } else if constexpr (MODE == kRowGeneral) {
+    for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
+  } else {
+    // tiles whose last key is visible to the workgroup's first row are visible to all its rows
+    int nraw = (r0 + off + 1) / BC;
+    nraw = nraw < ntiles ? nraw : ntiles;
+    for (int j = 0; j < nraw; ++j) tile_body(j, std::true_type{});
+    for (int j = nraw; j < ntiles; ++j) tile_body(j, std::false_type{});
+  }
   vm_wait<0>();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
