@@ -1436,12 +1436,23 @@ constexpr const char* kernel_name() {
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   using K = FwdKernel<T, D>;
+  // The kernels index K/V heads as hq / group: refuse a grouping that does not tile Hq exactly
+  // (the C ABI validates its arguments; this guards every other caller of the launcher).
+  if (a.group < 1 || a.Hkv < 1 || a.Hq != a.group * a.Hkv || a.B < 1 || a.Nq < 1 || a.Nkv < 1)
+    return hipErrorInvalidValue;
   constexpr int BR = rows_per_block<D>();
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
   if constexpr (use_row_kernel<D>()) {
     const bool plain = a.mask_kind == kMaskNone && a.scale_log2 > 0.f;
-    if (plain && !a.causal && a.Nkv % 64 == 0)
+    // fp32 additive mask with 16-byte-aligned rows whose 32-key blocks start on 128-byte lines
+    // and whose byte range (including the rows of a partial last query tile) stays below 2 GiB
+    const bool staged_mask = a.mask_kind == kMaskAddF32 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
+                             a.msq % 32 == 0 &&
+                             ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq * 4 + (int64_t)a.Nkv * 4 < (1LL << 31);
+    if (staged_mask)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (plain && !a.causal && a.Nkv % 64 == 0)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (plain && a.causal)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowCausal>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -87,8 +87,9 @@ struct RowTiling {
   static constexpr int GPP = NSUB / 2;          // groups per phase (64 columns each)
   static constexpr int GT = 4 * GPP;            // groups per 64-key tile
   static constexpr int MPT = 8 * NSUB;          // products per wave per tile
-  static constexpr int EXCH = DG == 2 ? 4 * 2 * 4096 : 0;  // partial-S exchange: [wave][block][4 KiB]
-  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH);
+  static constexpr int EXCH = DG == 2 ? 4 * 4096 : 0;  // partial-S exchange: [wave][4 KiB]
+  static constexpr int MASKB = BR * 128 * 2;            // staged fp32 mask: [block][row][32 keys]
+  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH + MASKB);
   static constexpr int EM = PLAN.em;
   static constexpr int NG = PLAN.ng;
   static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB % 2 == 0 && NSUB >= 2;
@@ -97,7 +98,7 @@ struct RowTiling {
   static constexpr int LA = NE - 2;             // epochs of load lookahead
   static constexpr int EPT = OK ? MPT / EM : 1; // epochs per tile
   static constexpr int RING = NG * DG * 4096;   // ring bytes: [column group][slot][4 KiB]
-  static constexpr int LDS_BYTES = RING + EXCH;
+  static constexpr int LDS_BYTES = RING + EXCH;  // + MASKB when the mask is staged
 };
 
 // The head dims that run the row kernel (the others keep the column-split kernels).
@@ -185,8 +186,41 @@ constexpr int row_load_slot(int bs, int i, int MPT) { return bs + 1 + i < MPT ? 
 // for keys past Nkv or past the causal limit).  MODE selects the kernel's tiles: kRowGeneral (every
 // tile explicit), kRowRaw (every tile raw: no mask, no causal limit, whole tiles), kRowCausal (no
 // mask, causal: the tiles below the workgroup's diagonal raw, the diagonal ones explicit, in two
-// successive loops).  The launcher picks the variant.
-enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowCausal = 2 };
+// successive loops), kRowMaskF32 (every tile explicit, with an fp32 additive mask whose rows are
+// staged through LDS: whole 128-byte lines per direct-to-LDS load, one tile ahead, instead of
+// scattered 16-byte loads per lane).  The launcher picks the variant.
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowCausal = 2, kRowMaskF32 = 3 };
+
+// Group loads (per wave) issued in slot x of a tile: load i of the refill after the barrier at
+// slot e*EM - PF goes to row_load_slot(...).
+constexpr int row_loads_at(int x, int MPT, int EM, int PF, int BI) {
+  int n = 0;
+  for (int e = 1; e * EM - PF < MPT; ++e)
+    for (int i = 0; i < BI; ++i)
+      if (row_load_slot(e * EM - PF, i, MPT) == x) ++n;
+  return n;
+}
+// Loads issued after the staged mask rows of block kb (sent in slot nb of one tile, after that
+// slot's refills) and before the wait of the last barrier at or before the next tile's read slot:
+// they must be at least the number the barrier waits leave in flight, so that the in-order
+// completion of loads has finished the mask rows by then.
+constexpr bool row_mask_covered(int first, int MPT, int EM, int PF, int BI, int LA) {
+  int nb = first;
+  while ((nb + PF) % EM != 0) ++nb;
+  int rd = first - PF, bl = rd;
+  while ((bl + PF) % EM != 0) --bl;
+  int n = 0;
+  for (int x = nb + 1; x < MPT; ++x) n += row_loads_at(x, MPT, EM, PF, BI);
+  for (int x = 0; x < bl; ++x) n += row_loads_at(x, MPT, EM, PF, BI);
+  return bl >= 0 && n >= (LA - 1) * BI;
+}
+
+// Every staged-mask or exchange reuse below relies on an epoch barrier inside [first, last].
+constexpr bool row_barrier_within(int first, int last, int EM, int PF) {
+  for (int b = first; b <= last; ++b)
+    if ((b + PF) % EM == 0) return true;
+  return false;
+}
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
@@ -209,7 +243,24 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   static_assert(BIAS1_SLOT < row_sm_first(1, DG, PH, EM, PF), "mask biases before their use");
   static_assert(BI + 1 < EM, "the loads after a barrier end before the next one");
 
-  __shared__ __attribute__((aligned(1024))) char smem[RT::LDS_BYTES];
+  constexpr bool MASK_LDS = MODE == kRowMaskF32;
+  constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  // the partner's partial of block 0 is read (after a barrier, complete PF products later) before
+  // block 1's partial overwrites the single exchange buffer: a barrier must separate the two
+  static_assert(DG == 1 || row_barrier_within(row_sm_first(0, DG, PH, EM, PF), 2 * PH - 1, EM, PF),
+                "exchange reuse needs a barrier in between");
+  // staged mask of block kb: read at slot row_sm_first(kb) - PF, complete at row_sm_first(kb); the
+  // next tile's rows are loaded after the first barrier that follows (all waves done reading)
+  static_assert(!MASK_LDS || (row_sm_first(0, DG, PH, EM, PF) >= PF &&
+                              row_barrier_within(row_sm_first(0, DG, PH, EM, PF), MPT - 1, EM, PF) &&
+                              row_barrier_within(row_sm_first(1, DG, PH, EM, PF), MPT - 1, EM, PF)),
+                "mask staging schedule");
+  static_assert(!MASK_LDS || (row_mask_covered(row_sm_first(0, DG, PH, EM, PF), MPT, EM, PF, BI, LA) &&
+                              row_mask_covered(row_sm_first(1, DG, PH, EM, PF), MPT, EM, PF, BI, LA)),
+                "staged mask rows must be complete at the barrier before their reads");
+
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -345,11 +396,44 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
   const bool has_mask = a.mask_kind != kMaskNone;
 
-  // partial-S exchange (two column groups): [wave][block][4 x 1 KiB], 16 bytes per lane
-  const uint32_t ex_mine = ring_addr + RT::RING + wave * 8192 + lane * 16;
-  const uint32_t ex_partner = ring_addr + RT::RING + (wave ^ 1) * 8192 + lane * 16;
+  // partial-S exchange (two column groups): [wave][4 x 1 KiB], 16 bytes per lane, one block at a time
+  const uint32_t ex_mine = ring_addr + RT::RING + wave * 4096 + lane * 16;
+  const uint32_t ex_partner = ring_addr + RT::RING + (wave ^ 1) * 4096 + lane * 16;
 
-  // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
+  // ---- staged fp32 mask: block kb of the workgroup's rows at MASK_OFF + kb * BR * 128, row r's 32
+  // keys as eight 16-byte chunks swizzled like the K/V sub-tiles.  Wave w loads rows 8(w + 4i) ..
+  // +7 (i < BR/32); keys are whole tiles (Nkv % 64 == 0), rows past Nq read as zero through the
+  // descriptor (their results are never stored).
+  constexpr int MASK_OFF = RT::RING + RT::EXCH;
+  constexpr int MLOADS = BR / 32;  // loads per wave per block
+  const int mask_bytes = MASK_LDS ? (int)(((int64_t)(Nq - 1) * a.msq + Nkv) * 4) : 0;
+  const __amdgpu_buffer_rsrc_t rsrc_m =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)a.mask + (MASK_LDS ? mask_bh : 0)), (short)0,
+                                        mask_bytes, 0x00020000);
+  const int mrow0 = 8 * wave + (lane >> 3);  // row of load i: mrow0 + 32 i (same swizzle phase)
+  const uint32_t mvoff = (uint32_t)(((int64_t)(r0 + mrow0) * a.msq + ((lane & 7) ^ pi7((mrow0 >> 1) & 7)) * 4) * 4);
+  const uint32_t mrow_step = (uint32_t)(32 * a.msq * 4);
+  // rows of tile jt's block kb into the staging buffer
+  auto issue_mask = [&](int jt, int kb) {
+    const uint32_t kofs = (uint32_t)((jt * BC + 32 * kb) * 4);
+#pragma unroll
+    for (int i = 0; i < MLOADS; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_m,
+                                               (FFPA_LDS void*)(smem + MASK_OFF + kb * BR * 128 + (wave + 4 * i) * 1024),
+                                               16, mvoff + i * mrow_step + kofs, 0, 0, 0);
+  };
+  // this lane's 16 biases of block kb (keys 8g + 4hi + e): 4 reads, complete once a fragment read
+  // issued after them has been waited for
+  const int mr = rg * 32 + l32;  // the lane's row within the workgroup
+  const uint32_t mrd = ring_addr + MASK_OFF + mr * 128;
+  const int mswz = pi7((mr >> 1) & 7);
+
+  // ---- prologue: the first tile's mask rows and epochs 0 .. LA-1 in flight, epoch 0 (and the
+  // mask, issued before it) visible, the first PF fragments requested
+  if constexpr (MASK_LDS) {
+    issue_mask(0, 0);
+    issue_mask(0, 1);
+  }
   static_for<LA>([&](auto e_c) { issue_epoch(0, voff_lane, e_c); });
   wait_epoch(0);
   __builtin_amdgcn_s_barrier();
@@ -388,7 +472,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     bool need[2];
     i32x4 pk[2][2];      // P^T operands (bf16/fp16 pairs) of block kb, 16-key step ks
 
-    if (!RAW && has_mask)
+    if (!RAW && !MASK_LDS && has_mask)
       load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[0][0]), ctx, key0, a.mask_kind,
                                a.mask_vec && !tail);
 
@@ -506,14 +590,14 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         mma_guard_s(s_acc[kb]);
         if constexpr (DG == 2) {
           const f32x16& x = s_acc[kb];
-          const uint32_t dst = ex_mine + kb * 4096;
+          const uint32_t dst = ex_mine;
           lds_write_b128_async<0>(dst, f32x4{x[0], x[1], x[2], x[3]});
           lds_write_b128_async<1024>(dst, f32x4{x[4], x[5], x[6], x[7]});
           lds_write_b128_async<2048>(dst, f32x4{x[8], x[9], x[10], x[11]});
           lds_write_b128_async<3072>(dst, f32x4{x[12], x[13], x[14], x[15]});
         }
       }
-      if (!RAW && m == BIAS1_SLOT && has_mask)
+      if (!RAW && !MASK_LDS && m == BIAS1_SLOT && has_mask)
         load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[1][0]), ctx, key0 + 32, a.mask_kind,
                                  a.mask_vec && !tail);
 
@@ -533,7 +617,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           __builtin_amdgcn_s_barrier();
         }
         if (pub >= 0) {
-          const uint32_t src = ex_partner + pub * 4096;
+          const uint32_t src = ex_partner;
           part[pub][0] = lds_read_f4_async<0>(src);
           part[pub][1] = lds_read_f4_async<1024>(src);
           part[pub][2] = lds_read_f4_async<2048>(src);
@@ -553,12 +637,36 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         }
       });
 
+      // ---- staged mask: this tile's reads ahead of the block's logits (before the fragment read of
+      // this slot, so that waiting for that fragment completes them), and the next tile's rows
+      // after the first barrier that follows the reads' completion
+      if constexpr (MASK_LDS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int first = row_sm_first(kb, DG, PH, EM, PF);
+          if (m == first - PF) {
+            const uint32_t base = mrd + kb * BR * 128;
+            bias[kb][0] = lds_read_f4_async<0>(base + ((0 + hi) ^ mswz) * 16);
+            bias[kb][1] = lds_read_f4_async<0>(base + ((2 + hi) ^ mswz) * 16);
+            bias[kb][2] = lds_read_f4_async<0>(base + ((4 + hi) ^ mswz) * 16);
+            bias[kb][3] = lds_read_f4_async<0>(base + ((6 + hi) ^ mswz) * 16);
+          }
+          int nb = first;
+          while ((nb + PF) % EM != 0) ++nb;
+          if (m == nb && j + 1 < ntiles) issue_mask(j + 1, kb);
+        }
+      }
+
       // ---- the fragment PF products ahead (the last ones: the next tile's first products)
       read_frag(std::integral_constant<int, m + PF>{});
 
       // ---- softmax micro-pieces
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        // the staged biases were read before a fragment whose completion was waited for just
+        // before this product: they are complete
+        if (MASK_LDS && m == row_sm_first(kb, DG, PH, EM, PF))
+          asm volatile("" : "+v"(bias[kb][0]), "+v"(bias[kb][1]), "+v"(bias[kb][2]), "+v"(bias[kb][3]));
         // the partner's partial was read before a fragment whose completion was waited for just
         // before this product: it is complete
         if (DG == 2 && m == row_sm_first(kb, DG, PH, EM, PF))
@@ -574,9 +682,10 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   };
   if constexpr (MODE == kRowRaw) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
-  } else if constexpr (MODE == kRowGeneral) {
+  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
   } else {
+    static_assert(MODE == kRowCausal, "tile mode");
     // tiles whose last key is visible to the workgroup's first row are visible to all its rows
     int nraw = (r0 + off + 1) / BC;
     nraw = nraw < ntiles ? nraw : ntiles;

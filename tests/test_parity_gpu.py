@@ -97,6 +97,17 @@ def test_mask_broadcast(shape):
     _log(f"mask shape {shape}", compare(o, l, q, k, v, mask=mask))
 
 
+@pytest.mark.parametrize("shape", [(130, 256), (1, 1, 130, 256), (2, 1, 1, 256), (1, 3, 1, 256), (2, 3, 130, 256)])
+@pytest.mark.parametrize("D", [256, 512, 1024])
+def test_fp32_mask_staged_shapes(shape, D):
+    """fp32 masks over whole 64-key tiles (staged through LDS by the kernels), with broadcast batch,
+    head and row strides and a partial last query tile."""
+    q, k, v = _case(2, 3, 3, 130, 256, D, seed=D + len(shape))
+    mask = _bias(shape, seed=D * 3 + sum(shape))
+    o, l = run_gpu(q, k, v, mask=mask)
+    _log(f"staged mask shape {shape} D={D}", compare(o, l, q, k, v, mask=mask))
+
+
 def test_fully_masked_rows():
     """Rows with every key excluded: O = 0 and LSE = -inf (the convention of the oracle)."""
     q, k, v = _case(1, 2, 2, 70, 90, 512, seed=8)
