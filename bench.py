@@ -111,7 +111,7 @@ def cpu_baseline(w, inputs, outputs, seconds: float):
                 sample=sample, seconds=round(t_total, 2)), parity
 
 
-KERNEL_SOURCES = ("ffpa_kernel.hpp", "ffpa_launch.hpp", "ffpa_inst.hip", "ffpa_api.hip")
+KERNEL_SOURCES = ("ffpa_kernel.hpp", "ffpa_row_kernel.hpp", "ffpa_launch.hpp", "ffpa_inst.hip", "ffpa_api.hip")
 
 
 def kernel_fingerprint() -> str:
@@ -196,8 +196,9 @@ def main() -> int:
     log(f"{w.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak)")
 
     traffic = measured_traffic(args.traffic_json, w.name)
-    # four column groups per workgroup (D a multiple of 128 from 384 up) run the column-split kernel
-    kernel = "ffpa_fwd_split_kernel" if w.D >= 384 and w.D % 128 == 0 else "ffpa_fwd_kernel"
+    import exact_attention_head_amd as ffpa
+
+    kernel = ffpa.kernel_name(w.D)
     roofline = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(tflops / PEAK_TFLOPS, 4), traffic=traffic, traffic_unit="HBM bytes per launch",
                     kernel=kernel, flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))

@@ -18,7 +18,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn", "ffpa_fwd", "ffpa_check_args", "library", "rows_per_block", "FFPA_BF16", "FFPA_FP16",
+__all__ = ["attn", "ffpa_fwd", "ffpa_check_args", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,7 +28,8 @@ FFPA_BF16, FFPA_FP16 = 0, 1
 MASK_NONE, MASK_BOOL_U8, MASK_ADD_F32, MASK_ADD_BF16, MASK_ADD_FP16 = 0, 1, 2, 3, 4
 OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 
-EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block")
+EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
+            "ffpa_kernel_name")
 
 
 class MaskDesc(ctypes.Structure):
@@ -61,6 +62,8 @@ def library() -> ctypes.CDLL:
     lib.ffpa_last_error_detail.restype = ctypes.c_char_p
     lib.ffpa_rows_per_block.argtypes = [i64]
     lib.ffpa_rows_per_block.restype = i32
+    lib.ffpa_kernel_name.argtypes = [i64]
+    lib.ffpa_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -91,6 +94,12 @@ def ffpa_check_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, N
 
 def rows_per_block(D: int) -> int:
     return int(library().ffpa_rows_per_block(D))
+
+
+def kernel_name(D: int):
+    """Name of the GPU kernel serving head dim D (None if D is unsupported)."""
+    name = library().ffpa_kernel_name(D)
+    return None if name is None else name.decode()
 
 
 def _mask_desc(attn_mask, B, Hq, Nq, Nkv):

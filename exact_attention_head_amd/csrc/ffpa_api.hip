@@ -189,4 +189,14 @@ const char* ffpa_last_error_detail(void) { return g_detail; }
 
 int ffpa_rows_per_block(int64_t D) { return rows_for(D); }
 
+const char* ffpa_kernel_name(int64_t D) {
+  switch (D) {
+#define FFPA_NAME_CASE(Dv) \
+  case Dv: return ffpa::kernel_name<Dv>();
+    FFPA_FOR_EACH_D(FFPA_NAME_CASE)
+#undef FFPA_NAME_CASE
+    default: return nullptr;
+  }
+}
+
 }  // extern "C"

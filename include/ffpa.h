@@ -109,6 +109,12 @@ const char* ffpa_last_error_detail(void);
  * use), or 0 for an unsupported D.  Host-only; for schedulers and tests. */
 int ffpa_rows_per_block(int64_t D);
 
+/* Name of the GPU kernel that serves head dim D (as profilers list it, without
+ * template arguments), or NULL for an unsupported D.  Which variant of that
+ * kernel runs also depends on the mask and causal arguments.  Host-only; a
+ * static string. */
+const char* ffpa_kernel_name(int64_t D);
+
 #ifdef __cplusplus
 }
 #endif

@@ -119,6 +119,14 @@ def test_rows_per_block():
     assert ffpa.rows_per_block(96) == 0
 
 
+def test_kernel_name():
+    names = {D: ffpa.kernel_name(D) for D in range(64, 1025, 64)}
+    assert set(names.values()) <= {"ffpa_fwd_row_kernel", "ffpa_fwd_split_kernel", "ffpa_fwd_kernel"}, names
+    # the head dims of the benchmark run the row kernel
+    assert names[512] == "ffpa_fwd_row_kernel" and names[1024] == "ffpa_fwd_row_kernel"
+    assert ffpa.kernel_name(96) is None and ffpa.kernel_name(2048) is None
+
+
 def test_python_layer_rejects_before_the_library():
     import torch
 
