@@ -1,6 +1,10 @@
-// Exact large-head-dim attention forward for gfx950 (MI355X, CDNA4).
+// Exact large-head-dim attention forward for gfx950 (MI355X, CDNA4): shared definitions (argument
+// block, matrix-core wrappers, logit and mask helpers), the launcher, and the shared-staging
+// kernel that serves the head dims the row-owner kernel (ffpa_row_kernel.hpp, every other head
+// dim from 256 to 1024) does not: 64, 128, 192 and the multiples of 64 above 512 whose half is
+// an odd number of 32-column steps (576, 704, 832, 960).
 //
-// One workgroup = 4 wave64s = one (batch, query head, tile of BR query rows).
+// Shared-staging kernel.  One workgroup = 4 wave64s = one (batch, query head, tile of BR query rows).
 // It loops over the keys in tiles of BC = 64 and keeps an online softmax, as
 // in the FlashAttention-2 scheme the older FFPA page builds on
 // (sourcepulse page, "How It Works").  The large-D design follows the two
@@ -945,473 +949,6 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Column-split kernel (one row group): the four waves share the query tile (BR = 64 rows) and
-// wave dg owns output columns dg*DW .. dg*DW + DW - 1 (DW = D/4).  Each wave only ever reads its
-// own column slice of Q, K and V, so its LDS staging ring is private: the ring needs no
-// workgroup barrier, only the wave's own vmcnt waits, and can run deep (six slots for D <= 512,
-// where the query slice sits in AGPRs; three for larger D, where the query slice streams with K).
-// The waves meet twice per key tile, to sum the four partial score tiles (each wave then owns 16
-// keys) and to share the packed probabilities; the running row maximum of the previous tile
-// serves as the softmax reference, and only when a tile's maximum exceeds it by more than the
-// slack (or on a row's first visible tile) do they meet a third time to move it.
-// ---------------------------------------------------------------------------------------------
-template <typename T, int D>
-struct SplitKernel {
-  using TL = Tiling<D>;
-  static_assert(TL::RG == 1 && TL::DG == 4 && TL::RB == 2, "column-split tiling");
-  static constexpr int DG = 4, RB = 2, BR = 64, DW = D / DG, NC = DW / 32, BC = 64;
-  static constexpr bool QREG = TL::QREG;
-  static constexpr int THREADS = 256;
-  static constexpr int SLOT = QREG ? 4096 : 8192;  // per wave: one 32-column K or V sub-tile (+ the Q sub-tile)
-  static constexpr int NSLOT = QREG ? 6 : 3;
-  static constexpr int RING_W = NSLOT * SLOT;       // ring bytes per wave
-  static constexpr int SPT = 2 * NC;                // stages per key tile: NC of K, NC of V
-  static constexpr int NQ = 8 / DG;                 // owned groups of 4 keys per lane
-  static constexpr int OTHER = 8 - NQ;
-  static constexpr int OWN_KS = 4 / DG;             // owned 16-key steps
-  static constexpr int PART_W = RB * OTHER * 64 * 16;
-  static constexpr int EX_PART = 4 * RING_W;
-  static constexpr int EX_MX = EX_PART + 4 * PART_W;
-  static constexpr int EX_RS = EX_MX + 4 * RB * 32 * 4;
-  static constexpr int EX_PK = EX_RS + 4 * RB * 32 * 4;
-  static constexpr int LDS_BYTES = EX_PK + 4 * RB * OWN_KS * 64 * 16;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static constexpr int K_LOADS = QREG ? 4 : 8;  // 16-byte loads per lane for a K stage (Q + K when streamed)
-  static constexpr int V_LOADS = 4;
-};
-
-// One wave stages [64 rows][32 columns] of its own slice into a private LDS tile ([64][4 chunks],
-// swizzled) with buffer_load_dwordx4 ... lds; rows past the block read as zero.
-struct WaveTileLoader {
-  uint32_t voff[4];
-  __device__ inline void init(int D, int lane) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int s = t * 64 + lane;
-      const int row = s >> 2;
-      voff[t] = (uint32_t)((row * D + swz(row, s & 3) * 8) * 2);
-    }
-  }
-  __device__ inline void issue(char* dst, const uint16_t* head, int rows, int row0, int col, int D) const {
-    const int64_t start = (int64_t)row0 * D + col;
-    const uint32_t bytes = (uint32_t)(((int64_t)rows * D - start) * 2);
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(head + start), (short)0, (int)bytes, 0x00020000);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (FFPA_LDS void*)(dst + t * 1024), 16, voff[t], 0, 0, 0);
-  }
-};
-
-// s_waitcnt vmcnt(n) for a wave-uniform run-time n that is a multiple of 4 up to 32.
-__device__ inline void wait_vmem_n(int n) {
-  switch (n) {
-    case 0: wait_vmem<0>(); break;
-    case 4: wait_vmem<4>(); break;
-    case 8: wait_vmem<8>(); break;
-    case 12: wait_vmem<12>(); break;
-    case 16: wait_vmem<16>(); break;
-    case 20: wait_vmem<20>(); break;
-    case 24: wait_vmem<24>(); break;
-    case 28: wait_vmem<28>(); break;
-    default: wait_vmem<32>(); break;
-  }
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void ffpa_fwd_split_kernel(FwdArgs a) {
-  using K = SplitKernel<T, D>;
-  using E = Elem<T>;
-  constexpr int DG = K::DG, RB = K::RB, BR = K::BR, DW = K::DW, NC = K::NC, BC = K::BC, NSLOT = K::NSLOT;
-  constexpr int SPT = K::SPT, NQ = K::NQ, OWN_KS = K::OWN_KS;
-  constexpr bool QREG = K::QREG;
-
-  __shared__ __attribute__((aligned(1024))) char smem[K::LDS_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int dg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = column group
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  char* const ring = smem + dg * K::RING_W;
-
-  // ---- work item (b, hq, q tile); consecutive items share an XCD's L2
-  const int Nq = a.Nq, Nkv = a.Nkv;
-  const int nqt = (Nq + BR - 1) / BR;
-  const int total = a.B * a.Hq * nqt;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  int qt = id % nqt;
-  const int bh = id / nqt;
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
-  if (a.causal) qt = nqt - 1 - qt;
-  const int hk = hq / a.group;
-  const int r0 = qt * BR;
-  const int col0 = dg * DW;
-  const int off = Nkv - Nq;
-  const uint16_t* qg = a.q + (int64_t)(b * a.Hq + hq) * Nq * D;
-  const uint16_t* kg = a.k + (int64_t)(b * a.Hkv + hk) * Nkv * D;
-  const uint16_t* vg = a.v + (int64_t)(b * a.Hkv + hk) * Nkv * D;
-  int kv_end = Nkv;
-  if (a.causal) {
-    const int lim = r0 + BR + off;
-    kv_end = lim < Nkv ? lim : Nkv;
-  }
-  const int ntiles = (kv_end + BC - 1) / BC;
-  const int nstages = ntiles * SPT;
-
-  WaveTileLoader ld;
-  ld.init(D, lane);
-
-  // ---- the query slice, kept in AGPRs for the whole key loop when it fits (D <= 512)
-  i32x4 qf[QREG ? RB : 1][QREG ? DW / 16 : 1];
-  if constexpr (QREG) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      char* dst = ring + (c % NSLOT) * K::SLOT;
-      ld.issue(dst, qg, Nq, r0, col0 + c * 32, D);
-      wait_vmem<0>();
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = rb * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) qf[rb][c * 2 + ks] = lds_read16(dst + row * 64 + swz(row, ks * 2 + hi) * 16);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-  }
-
-  // ---- stage g = j*SPT + u: u < NC is K chunk u (with Q chunk u when streamed), else V chunk u-NC.
-  // Software pipeline: while the MFMAs of stage g run, the LDS fragments of stage g+1 are already
-  // in flight, and the ring slot of stage g-1 (whose fragments were consumed before this point)
-  // is refilled with stage g + NSLOT - 1.
-  auto stage_loads = [&](int g) -> int {
-    if (g >= nstages) return 0;
-    return (g % SPT) < NC ? K::K_LOADS : K::V_LOADS;
-  };
-  auto issue = [&](int g) {
-    if (g >= nstages) return;
-    char* dst = ring + (g % NSLOT) * K::SLOT;
-    const int j = g / SPT, u = g % SPT;
-    if (u < NC) {
-      if constexpr (!QREG) {
-        ld.issue(dst, qg, Nq, r0, col0 + u * 32, D);
-        dst += 4096;
-      }
-      ld.issue(dst, kg, Nkv, j * BC, col0 + u * 32, D);
-    } else {
-      ld.issue(dst, vg, Nkv, j * BC, col0 + (u - NC) * 32, D);
-    }
-  };
-  // data of stage g is in LDS once at most the loads of stages g+1 .. g+NSLOT-2 are outstanding
-  auto wait_stage = [&](int g) {
-    int pending = 0;
-#pragma unroll
-    for (int d = 1; d <= NSLOT - 2; ++d) pending += stage_loads(g + d);
-    wait_vmem_n(pending);
-    asm volatile("" ::: "memory");
-  };
-  // fragments of one stage: K stage -> kf[ks*2 + kb] (+ Q for streamed Q at [4 + ks*2 + rb]);
-  // V stage -> the V^T operand of 16-key step ks at [ks]
-  constexpr int NF = QREG ? 4 : 8;
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int tr_chunk = 2 * (g16 & 1) + ((i16 & 3) >> 1);
-  const int tr_within = 8 * (i16 & 1);
-  // Per-lane LDS offsets inside a slot, fixed for the whole kernel (the swizzle makes them
-  // independent of the 32-key block and of the 16-key step, which become immediate offsets).
-  //  K fragment (32 keys x 16 columns, ks = 0/1): key l32 (+32 per key block), chunk ks*2 + hi
-  //  V fragment (transposed, 16-key step ks): keys (g16>>1)*4 + (i16>>2) (+8 for the second read)
-  const int kofs0 = l32 * 64 + swz(l32, hi) * 16;
-  const int kofs1 = l32 * 64 + swz(l32, 2 + hi) * 16;
-  const int vkeyA = (g16 >> 1) * 4 + (i16 >> 2);
-  const int vofsA = vkeyA * 64 + swz(vkeyA, tr_chunk) * 16 + tr_within;
-  const int vofsB = (vkeyA + 8) * 64 + swz(vkeyA + 8, tr_chunk) * 16 + tr_within;
-  // Fragment reads of stage g in two halves (K: the 16-column steps ks = 0 / 1; V: the 16-key
-  // steps 0-1 / 2-3), so that they can be spread between the products of the previous stage.
-  auto read_frags_part = [&](int g, bool is_k, i32x4 (&f)[NF], int half) {
-    const char* slot = ring + (g % NSLOT) * K::SLOT;
-    if (is_k) {
-      const char* kt = QREG ? slot : slot + 4096;
-      const int kofs = half == 0 ? kofs0 : kofs1;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) f[half * 2 + kb] = lds_read16(kt + kofs + kb * 2048);
-      if constexpr (!QREG) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) f[4 + half * 2 + rb] = lds_read16(slot + kofs + rb * 2048);
-      }
-    } else {
-      const uint32_t a0 = lds_addr(slot) + (uint32_t)vofsA, b0 = lds_addr(slot) + (uint32_t)vofsB;
-      i32x2 lo0, hi0, lo1, hi1;
-      if (half == 0) {
-        lo0 = lds_read_tr_async<0>(a0);
-        hi0 = lds_read_tr_async<0>(b0);
-        lo1 = lds_read_tr_async<1024>(a0);
-        hi1 = lds_read_tr_async<1024>(b0);
-      } else {
-        lo0 = lds_read_tr_async<2048>(a0);
-        hi0 = lds_read_tr_async<2048>(b0);
-        lo1 = lds_read_tr_async<3072>(a0);
-        hi1 = lds_read_tr_async<3072>(b0);
-      }
-      f[half * 2 + 0] = i32x4{lo0[0], lo0[1], hi0[0], hi0[1]};
-      f[half * 2 + 1] = i32x4{lo1[0], lo1[1], hi1[0], hi1[1]};
-    }
-  };
-  auto read_frags = [&](int g, bool is_k, i32x4 (&f)[NF]) {
-    read_frags_part(g, is_k, f, 0);
-    read_frags_part(g, is_k, f, 1);
-  };
-
-  f32x16 o_acc[RB][NC];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) o_acc[rb][c] = f32x16{};
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
-  }
-  const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
-  f32x4* const part_mine = (f32x4*)(smem + K::EX_PART + dg * K::PART_W);
-  float* const ex_mx = (float*)(smem + K::EX_MX);
-  float* const ex_rs = (float*)(smem + K::EX_RS);
-  i32x4* const ex_pk = (i32x4*)(smem + K::EX_PK);
-
-  // prologue: stages 0 .. NSLOT-2 in flight, fragments of stage 0 in registers
-#pragma unroll
-  for (int g = 0; g < NSLOT - 1; ++g) issue(g);
-  i32x4 fr[2][NF];
-  wait_stage(0);
-  read_frags(0, true, fr[0]);
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int key0 = j * BC;
-    const int kown = key0 + (BC / DG) * dg;  // first key this wave owns in the tile
-    const bool tail = key0 + BC > Nkv;
-    const bool diag = a.causal && (key0 + BC - 1 > r0 + off);
-    LogitCtx ctx{a.mask, mask_bh, a.msq, Nq, Nkv, key0, r0, off, a.causal, tail || diag, a.scale_log2, l32, hi};
-    // mask biases of the owned keys, requested early so that their latency hides behind the S phase
-    f32x4 bias[RB][NQ];
-    const bool has_mask = a.mask_kind != kMaskNone;
-    if (has_mask) load_bias_dispatch<RB, NQ>(bias, ctx, kown, a.mask_kind, a.mask_vec && !tail);
-
-    // One pipeline step for stage g: its 8 products, with the preparation of stage g+1 (the refill
-    // of the slot of stage g-1, the wait for stage g+1's data and its fragment reads) placed
-    // between them so that the matrix core keeps working while the wave does the bookkeeping.
-    auto prep = [&](int g, int part, bool next_is_k, i32x4 (&nxt)[NF]) {
-      if (part == 0) {
-        issue(g + NSLOT - 1);
-      } else if (g + 1 < nstages) {
-        if (part == 1) wait_stage(g + 1);
-        else read_frags_part(g + 1, next_is_k, nxt, part - 2);
-      }
-    };
-
-    // ================= S^T = K Q^T over this wave's columns =================
-    f32x16 s_acc[RB][2];
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const int g = j * SPT + u;
-      i32x4 (&cur)[NF] = fr[u & 1];
-      i32x4 (&nxt)[NF] = fr[(u + 1) & 1];
-      const bool next_is_k = u + 1 < NC;
-      int step = 0;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const i32x4& kf = cur[ks * 2 + kb];
-            if constexpr (QREG) {
-              if (u == 0 && ks == 0) E::mma_first_ba(s_acc[rb][kb], kf, qf[rb][u * 2 + ks]);
-              else E::mma_acc_ba(s_acc[rb][kb], kf, qf[rb][u * 2 + ks]);
-            } else {
-              if (u == 0 && ks == 0) E::mma_first(s_acc[rb][kb], kf, cur[4 + ks * 2 + rb]);
-              else E::mma_acc(s_acc[rb][kb], kf, cur[4 + ks * 2 + rb]);
-            }
-            if (step < 4) prep(g, step, next_is_k, nxt);
-            ++step;
-          }
-    }
-    mma_guard_v<RB>(s_acc);
-
-    // ================= sum the four partial tiles of the owned keys =================
-    // publish the groups the other waves own: group gg of wave dg sits at position gg - (gg > own ? NQ : 0)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int gg = 0; gg < 8; ++gg) {
-        if (gg / NQ == dg) continue;
-        const int pos = gg < dg * NQ ? gg : gg - NQ;
-        const int v = (gg & 3) * 4;
-        part_mine[(rb * K::OTHER + pos) * 64 + lane] =
-            f32x4{s_acc[rb][gg >> 2][v], s_acc[rb][gg >> 2][v + 1], s_acc[rb][gg >> 2][v + 2], s_acc[rb][gg >> 2][v + 3]};
-      }
-    block_sync();  // A: partial tiles published
-    f32x4 t4[RB][NQ];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int g = 0; g < NQ; ++g) {
-        f32x4 mine = {};
-#pragma unroll
-        for (int d2 = 0; d2 < DG; ++d2) {
-          const int gg = d2 * NQ + g;
-          const int v = (gg & 3) * 4;
-          if (d2 == dg)
-            mine = f32x4{s_acc[rb][gg >> 2][v], s_acc[rb][gg >> 2][v + 1], s_acc[rb][gg >> 2][v + 2],
-                         s_acc[rb][gg >> 2][v + 3]};
-        }
-        const int gg = dg * NQ + g;
-        f32x4 sum;
-#pragma unroll
-        for (int d2 = 0; d2 < DG; ++d2) {
-          const int pos = gg < d2 * NQ ? gg : gg - NQ;
-          const f32x4* part = (const f32x4*)(smem + K::EX_PART + d2 * K::PART_W);
-          const f32x4 x = d2 == dg ? mine : part[(rb * K::OTHER + pos) * 64 + lane];
-          sum = d2 == 0 ? x : sum + x;
-        }
-        t4[rb][g] = sum;
-      }
-
-    // ================= softmax of the owned keys against the running maximum =================
-    float mx[RB];
-    apply_logits<RB, NQ>(t4, bias, has_mask, mx, ctx, kown);
-    i32x4 pk[RB][4];
-    auto probs = [&](const float (&mref)[RB]) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float m0 = mref[rb] == kNegInf ? 0.f : mref[rb];
-        float sum = 0.f;
-        f32x4 p[NQ];
-#pragma unroll
-        for (int g = 0; g < NQ; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[g][e] = __builtin_amdgcn_exp2f(t4[rb][g][e] - m0);
-            sum += p[g][e];
-          }
-#pragma unroll
-        for (int k2 = 0; k2 < OWN_KS; ++k2) {
-          i32x4 w;
-          w[0] = (int)pack2<T>(p[2 * k2][0], p[2 * k2][1]);
-          w[1] = (int)pack2<T>(p[2 * k2][2], p[2 * k2][3]);
-          w[2] = (int)pack2<T>(p[2 * k2 + 1][0], p[2 * k2 + 1][1]);
-          w[3] = (int)pack2<T>(p[2 * k2 + 1][2], p[2 * k2 + 1][3]);
-          ex_pk[((dg * RB + rb) * OWN_KS + k2) * 64 + lane] = w;
-        }
-        sum = sum_halves(sum);
-        if (hi == 0) ex_rs[(dg * RB + rb) * 32 + l32] = sum;
-      }
-    };
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float m = max_halves(mx[rb]);
-      if (hi == 0) ex_mx[(dg * RB + rb) * 32 + l32] = m;
-    }
-    probs(m_run);
-    block_sync();  // B: row maxima, row sums and probabilities published
-    bool need_any = false;
-    float m_new[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float mt = ex_mx[(0 * RB + rb) * 32 + l32];
-#pragma unroll
-      for (int d2 = 1; d2 < DG; ++d2) mt = __builtin_fmaxf(mt, ex_mx[(d2 * RB + rb) * 32 + l32]);
-      const float mo = m_run[rb];
-      const bool need = mo == kNegInf ? (mt != kNegInf) : (mt > mo + kRescaleSlack);
-      m_new[rb] = need ? mt : mo;
-      need_any |= need;
-    }
-    if (__builtin_amdgcn_ballot_w64(need_any) != 0) {
-      // Rare: move the reference to the tile maximum, rescale O and l, and republish (identical
-      // decision in every wave, since all read the same maxima).
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float mo = m_run[rb];
-        const float alpha = (mo == kNegInf || m_new[rb] == mo) ? 1.f : __builtin_amdgcn_exp2f(mo - m_new[rb]);
-        l_run[rb] *= alpha;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          mma_guard_a(o_acc[rb][c]);
-          o_acc[rb][c] *= alpha;
-          // back into AGPRs inside the branch, so that both paths leave O in the same register class
-          asm volatile("" : "+a"(o_acc[rb][c]));
-        }
-        m_run[rb] = m_new[rb];
-      }
-      probs(m_run);
-      block_sync();  // C: republished
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float tot = 0.f;
-#pragma unroll
-      for (int d2 = 0; d2 < DG; ++d2) {
-        tot += ex_rs[(d2 * RB + rb) * 32 + l32];
-#pragma unroll
-        for (int k2 = 0; k2 < OWN_KS; ++k2) pk[rb][d2 * OWN_KS + k2] = ex_pk[((d2 * RB + rb) * OWN_KS + k2) * 64 + lane];
-      }
-      l_run[rb] += tot;
-    }
-
-    // ================= O^T += V^T P^T over this wave's columns =================
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int u = NC + c;
-      const int g = j * SPT + u;
-      i32x4 (&cur)[NF] = fr[u & 1];
-      i32x4 (&nxt)[NF] = fr[(u + 1) & 1];
-      {
-        i32x4(&v4)[4] = *reinterpret_cast<i32x4(*)[4]>(&cur[0]);
-        lds_frag_wait(v4);  // V fragments were read with the untracked transposed loads
-      }
-      const bool next_is_k = u + 1 == SPT;
-      int step = 0;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          E::mma_acc_agpr(o_acc[rb][c], cur[ks], pk[rb][ks]);
-          if (step < 4) prep(g, step, next_is_k, nxt);
-          ++step;
-        }
-    }
-    mma_guard_all<RB * NC>(&o_acc[0][0]);  // O is never read within 12 wait states of a product
-  }
-
-  // ================= epilogue =================
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = r0 + rb * 32 + l32;
-    if (row < Nq) {
-      const float l = l_run[rb];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* orow = a.o + ((int64_t)(b * a.Hq + hq) * Nq + row) * D + col0;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x16 acc = o_acc[rb][c];
-          i32x2 w;
-          w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
-          w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
-          *(i32x2*)(orow + c * 32 + q4 * 8 + hi * 4) = w;
-        }
-      }
-      if (a.lse != nullptr && dg == 0 && hi == 0) {
-        const float lse = l > 0.f ? (m_run[rb] + __builtin_log2f(l)) * kLn2 : kNegInf;
-        a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
-      }
-    }
-  }
-}
-
 }  // namespace ffpa
 
 #include "ffpa_row_kernel.hpp"
@@ -1429,7 +966,6 @@ constexpr int rows_per_block() {
 template <int D>
 constexpr const char* kernel_name() {
   if constexpr (use_row_kernel<D>()) return "ffpa_fwd_row_kernel";
-  else if constexpr (Tiling<D>::RG == 1) return "ffpa_fwd_split_kernel";
   else return "ffpa_fwd_kernel";
 }
 
@@ -1458,9 +994,6 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowCausal>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  } else if constexpr (Tiling<D>::RG == 1) {
-    static_assert(SplitKernel<T, D>::BR == K::BR, "same query tile");
-    hipLaunchKernelGGL((ffpa_fwd_split_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((ffpa_fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(K::THREADS), 0, stream, a);
   }
