@@ -142,6 +142,14 @@ __device__ inline void vm_wait() {
 // 12 wait states after the products that wrote one VGPR accumulator.
 __device__ inline void mma_guard_s(f32x16& x) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(x)); }
 
+// LDS instructions of the fragment reads issued after fragment m's (those of m+1 .. m+PF-1: one
+// ds_read_b128 for a K fragment, two transposed reads for a V^T fragment).
+constexpr int row_reads_after(int m, int PF, int MPT, int PH) {
+  int n = 0;
+  for (int k = 1; k < PF; ++k) n += ((m + k) % MPT) / PH < 2 ? 1 : 2;
+  return n;
+}
+
 // Operand fragments are read this many products ahead of their use.
 constexpr int kRowPF = 3;
 
@@ -177,7 +185,14 @@ constexpr bool row_sm_fits(int DG, int PH, int EM, int PF) {
 }
 // Slot at which load i of the epoch refilled after the barrier at slot bs is issued: spread over
 // the slots that follow the barrier, within the tile.
-constexpr int row_load_slot(int bs, int i, int MPT) { return bs + 1 + i < MPT ? bs + 1 + i : MPT - 1; }
+// Slot of load q (one sub-tile per wave) of the refill after the barrier at slot bs: the refill's
+// loads are spread evenly over the epoch that follows (a burst of loads would fill the
+// texture-address queue and stall the issuing wave while the matrix core drains), all within
+// the tile and before the next barrier's wait.
+constexpr int row_load_step(int EM, int nloads) { return EM / nloads > 1 ? EM / nloads : 1; }
+constexpr int row_load_slot(int bs, int q, int step, int MPT) {
+  return bs + 1 + q * step < MPT ? bs + 1 + q * step : MPT - 1;
+}
 
 // Tile variants.  A raw tile has every key taking part for every row of the workgroup and no mask,
 // under a positive scale: the row maximum is taken over the raw dot products (scaling by a
@@ -191,28 +206,28 @@ constexpr int row_load_slot(int bs, int i, int MPT) { return bs + 1 + i < MPT ? 
 // scattered 16-byte loads per lane).  The launcher picks the variant.
 enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowCausal = 2, kRowMaskF32 = 3 };
 
-// Group loads (per wave) issued in slot x of a tile: load i of the refill after the barrier at
-// slot e*EM - PF goes to row_load_slot(...).
-constexpr int row_loads_at(int x, int MPT, int EM, int PF, int BI) {
+// Loads (per wave) issued in slot x of a tile: load q of the refill after the barrier at slot
+// e*EM - PF goes to row_load_slot(...).
+constexpr int row_loads_at(int x, int MPT, int EM, int PF, int NL) {
   int n = 0;
   for (int e = 1; e * EM - PF < MPT; ++e)
-    for (int i = 0; i < BI; ++i)
-      if (row_load_slot(e * EM - PF, i, MPT) == x) ++n;
+    for (int q = 0; q < NL; ++q)
+      if (row_load_slot(e * EM - PF, q, row_load_step(EM, NL), MPT) == x) ++n;
   return n;
 }
 // Loads issued after the staged mask rows of block kb (sent in slot nb of one tile, after that
 // slot's refills) and before the wait of the last barrier at or before the next tile's read slot:
 // they must be at least the number the barrier waits leave in flight, so that the in-order
 // completion of loads has finished the mask rows by then.
-constexpr bool row_mask_covered(int first, int MPT, int EM, int PF, int BI, int LA) {
+constexpr bool row_mask_covered(int first, int MPT, int EM, int PF, int NL, int LA) {
   int nb = first;
   while ((nb + PF) % EM != 0) ++nb;
   int rd = first - PF, bl = rd;
   while ((bl + PF) % EM != 0) --bl;
   int n = 0;
-  for (int x = nb + 1; x < MPT; ++x) n += row_loads_at(x, MPT, EM, PF, BI);
-  for (int x = 0; x < bl; ++x) n += row_loads_at(x, MPT, EM, PF, BI);
-  return bl >= 0 && n >= (LA - 1) * BI;
+  for (int x = nb + 1; x < MPT; ++x) n += row_loads_at(x, MPT, EM, PF, NL);
+  for (int x = 0; x < bl; ++x) n += row_loads_at(x, MPT, EM, PF, NL);
+  return bl >= 0 && n >= (LA - 1) * NL;
 }
 
 // Every staged-mask or exchange reuse below relies on an epoch barrier inside [first, last].
@@ -231,7 +246,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   constexpr int MPT = RT::MPT, EM = RT::EM, BI = RT::BI, NG = RT::NG, LA = RT::LA, EPT = RT::EPT;
   constexpr int CGB = NG * 4096;  // bytes of one column group's sub-tiles in the ring
   constexpr int PF = kRowPF;     // operand fragments are read this many products ahead
-  constexpr int NFR = 4;         // fragment registers in rotation (at least PF + 1, dividing MPT)
+  constexpr int NFR = PF < 4 ? 4 : 8;  // fragment registers in rotation (at least PF + 1, dividing MPT)
   constexpr int BC = 64;
   constexpr int PH = 2 * NSUB;   // products per phase
   static_assert(MPT % NFR == 0, "the fragment rotation must line up with the tile");
@@ -241,7 +256,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   // the second block's mask biases are requested once the first block's logits are formed
   constexpr int BIAS1_SLOT = row_sm_slot(0, row_sm_logit_pieces(false), false, DG, PH, EM, PF);
   static_assert(BIAS1_SLOT < row_sm_first(1, DG, PH, EM, PF), "mask biases before their use");
-  static_assert(BI + 1 < EM, "the loads after a barrier end before the next one");
+  constexpr int NL = BI * DG;                        // loads per wave per epoch
+  constexpr int LSTEP = row_load_step(EM, NL);
+  static_assert(1 + (NL - 1) * LSTEP < EM, "the loads after a barrier end before the next one");
 
   constexpr bool MASK_LDS = MODE == kRowMaskF32;
   constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
@@ -256,8 +273,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
                               row_barrier_within(row_sm_first(0, DG, PH, EM, PF), MPT - 1, EM, PF) &&
                               row_barrier_within(row_sm_first(1, DG, PH, EM, PF), MPT - 1, EM, PF)),
                 "mask staging schedule");
-  static_assert(!MASK_LDS || (row_mask_covered(row_sm_first(0, DG, PH, EM, PF), MPT, EM, PF, BI, LA) &&
-                              row_mask_covered(row_sm_first(1, DG, PH, EM, PF), MPT, EM, PF, BI, LA)),
+  static_assert(!MASK_LDS || (row_mask_covered(row_sm_first(0, DG, PH, EM, PF), MPT, EM, PF, BI * DG, LA) &&
+                              row_mask_covered(row_sm_first(1, DG, PH, EM, PF), MPT, EM, PF, BI * DG, LA)),
                 "staged mask rows must be complete at the barrier before their reads");
 
   __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
@@ -341,6 +358,14 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     constexpr int TD = E / EPT, EL = E % EPT;
     if (j + TD >= ntiles) return;
     issue_group(vt, std::integral_constant<int, TD>{}, std::integral_constant<int, EL * BI + I>{});
+  };
+  // load q (group q / DG, column group q % DG) of local epoch E relative to tile j
+  auto issue_epoch_load = [&](int j, uint32_t vt, auto e_c, auto q_c) {
+    constexpr int E = decltype(e_c)::value, Q = decltype(q_c)::value;
+    constexpr int TD = E / EPT, EL = E % EPT;
+    if (j + TD >= ntiles) return;
+    issue_sub(vt, std::integral_constant<int, TD>{}, std::integral_constant<int, EL * BI + Q / DG>{},
+              std::integral_constant<int, Q % DG>{});
   };
   auto issue_epoch = [&](int j, uint32_t vt, auto e_c) {
     static_for<BI>([&](auto i_c) { issue_epoch_group(j, vt, e_c, i_c); });
@@ -565,13 +590,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       // ---- product m, once its fragment is complete: the LDS reads issued after it are those of
       // the fragments m+1 .. m+PF-1 (any other LDS instruction issued later only waits longer)
       {
-        int after = 0;
-#pragma unroll
-        for (int k = 1; k < PF; ++k) after += ((m + k) % MPT) / PH < 2 ? 1 : 2;
-        if (after <= 1) lgkm_wait<1>();
-        else if (after == 2) lgkm_wait<2>();
-        else if (after == 3) lgkm_wait<3>();
-        else lgkm_wait<4>();
+        constexpr int after = row_reads_after(m, PF, MPT, PH);
+        static_assert(after <= 15, "lgkmcnt range");
+        lgkm_wait<after>();
       }
       if (ph < 2) {
         if (s == 0 && ks == 0) E::mma_first(s_acc[ph], kfr[r], qf[2 * s + ks]);
@@ -630,9 +651,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         constexpr int eb = decltype(eb_c)::value;  // barrier of local epoch eb sits at slot eb*EM - PF
         constexpr int bs = eb * EM - PF;
         if constexpr (bs >= 0 && bs < MPT) {
-          static_for<BI>([&](auto i_c) {
-            if constexpr (row_load_slot(bs, decltype(i_c)::value, MPT) == m)
-              issue_epoch_group(j, vt, std::integral_constant<int, eb + LA>{}, i_c);
+          static_for<NL>([&](auto q_c) {
+            if constexpr (row_load_slot(bs, decltype(q_c)::value, LSTEP, MPT) == m)
+              issue_epoch_load(j, vt, std::integral_constant<int, eb + LA>{}, q_c);
           });
         }
       });
