@@ -54,8 +54,8 @@ struct RingPlan {
 constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes) {
   RingPlan best{0, 0};
   int best_score = -1;
-  const int ems[2] = {16, 8};
-  for (int i = 0; i < 2; ++i) {
+  const int ems[3] = {32, 16, 8};
+  for (int i = 0; i < 3; ++i) {
     const int em = ems[i];
     if (MPT % em != 0) continue;
     const int bi = em / 4;  // groups per epoch (four products per wave per group)
@@ -587,10 +587,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       constexpr int m = decltype(mc)::value;
       constexpr int ph = m / PH, s = (m % PH) / 2, ks = m % 2;
       constexpr int r = m % NFR;
-      // ---- product m, once its fragment is complete: the LDS reads issued after it are those of
-      // the fragments m+1 .. m+PF-1 (any other LDS instruction issued later only waits longer)
-      {
-        constexpr int after = row_reads_after(m, PF, MPT, PH);
+      // ---- product m, once its fragment is complete: the LDS reads issued after fragment x are those
+      // of the fragments x+1 .. x+PF-1 (any other LDS instruction issued later only waits longer)
+      // (one wait per pair of products: before product m, m even, for fragments m and m + 1; the
+      // reads issued after fragment m + 1 by then are those of fragments m + 2 .. m + PF - 1)
+      if constexpr (m % 2 == 0) {
+        constexpr int after = row_reads_after(m + 1, PF - 1, MPT, PH);
         static_assert(after <= 15, "lgkmcnt range");
         lgkm_wait<after>();
       }
