@@ -48,6 +48,18 @@ def test_transposed_read_needs_covering_wait(tmp_path):
     assert not _check(tmp_path, [tr, "s_waitcnt lgkmcnt(0)", "v_mov_b32 v40, v20"])
 
 
+def test_any_lds_read_needs_covering_wait(tmp_path):
+    # operand fragments read by inline assembly: a later read may not reuse the registers of one
+    # that is still in flight, nor may a product consume them early
+    rd = "ds_read_b128 v[164:167], v178 offset:0x8000"
+    assert _check(tmp_path, [rd, "ds_read_b128 v[164:167], v177 offset:0x9000"])
+    assert _check(tmp_path, [rd, "ds_read_b128 v[160:163], v182", "s_waitcnt lgkmcnt(2)",
+                             "v_mfma_f32_32x32x16_bf16 v[0:15], v[164:167], v[36:39], v[0:15]"])
+    assert not _check(tmp_path, [rd, "ds_read_b128 v[160:163], v182", "s_waitcnt lgkmcnt(1)",
+                                 "v_mfma_f32_32x32x16_bf16 v[0:15], v[164:167], v[36:39], v[0:15]",
+                                 "ds_read_b128 v[164:167], v177 offset:0x9000"])
+
+
 def test_state_survives_branches_and_loop_back_edges(tmp_path):
     # the hazard sits on the taken path only
     assert _check(tmp_path, [MFMA, "s_cbranch_scc1 .LBB0_2", "s_nop 7", "s_nop 7", ".LBB0_2:",
