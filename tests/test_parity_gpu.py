@@ -134,6 +134,18 @@ def test_explicit_scale_and_large_logits():
     _log("ramp bias", compare(o, l, q, k, v, mask=ramp))
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.05])
+@pytest.mark.parametrize("D", [256, 512, 1024])
+def test_nonpositive_and_small_scales(scale, D):
+    """Whole 64-key tiles without a mask: a positive scale runs the raw-logit variant (row maximum over
+    raw dot products), zero and negative scales must take the explicit one."""
+    q, k, v = _case(1, 2, 2, 130, 256, D, seed=D + int(scale * 100))
+    o, l = run_gpu(q, k, v, scale=scale)
+    _log(f"scale {scale} D={D}", compare(o, l, q, k, v, scale=scale))
+    o, l = run_gpu(q, k, v, scale=scale, is_causal=True)
+    _log(f"scale {scale} D={D} causal", compare(o, l, q, k, v, scale=scale, is_causal=True))
+
+
 def test_golden_fixtures_on_gpu():
     """The hand-worked fixtures, zero-padded to D = 64 (padding adds nothing to any dot product)."""
     import glob
