@@ -165,6 +165,8 @@ def main() -> int:
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (from rocprofv3 --pmc), if present")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="secondary lines for the whole head-dim sweep (every D, bf16 and fp16) instead of the default set")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -204,13 +206,18 @@ def main() -> int:
                     kernel=kernel, flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))
 
     secondary = []
+    if args.sweep:
+        names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
+    else:
+        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512"]
     if not args.no_secondary and args.workload == "large_d_self":
-        for name in ("cross_mask", "sweep:1024", "gqa_causal", "sweep:512"):
+        for name in names:
             w2 = pick(name)
             ms2, _, _ = time_workload(w2, max(5, args.steps // 5), 2)
             tf2 = w2.flops / (ms2 * 1e-3) / 1e12
             log(f"{w2.name}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
-            secondary.append(dict(workload=w2.name, D=w2.D, ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
+            secondary.append(dict(workload=w2.name, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
+                                  kernel=ffpa.kernel_name(w2.D), ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
                                   frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
 
     cpu, parity = None, None
