@@ -19,6 +19,12 @@ query row r of batch b and query head h, with kv head ``h // (Hq // Hkv)``,
 
 ``scale=None`` means 1/sqrt(D).  A boolean mask excludes keys whose entry is
 false.  A row with every key excluded gets O = 0 and LSE = -inf.
+
+``attention_varlen`` is the packed variable-length form (same page,
+``ffpa_attn_varlen_func``): sequence b of a batch packed as [T, H, D] holds
+query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens cu_k[b] .. cu_k[b+1]-1 and
+is attended on its own, with the causal rule of its own lengths; the LSE is
+laid out [Hq, Tq].
 """
 from __future__ import annotations
 
@@ -183,3 +189,56 @@ def attention(q, k, v, mask=None, scale: Optional[float] = None, is_causal: bool
     O, L = attention_rows(q, k, v, np.arange(B * Hq * Nq), mask=mask, scale=scale, is_causal=is_causal,
                           threads=threads, fault=fault)
     return O.reshape(B, Hq, Nq, D), L.reshape(B, Hq, Nq)
+
+
+# Planted-mistake switches of the packed form (tests of the pins only).
+VL_FAULT_NONE = 0
+VL_FAULT_SHARED_OFFSETS = 1   # keys cut with the query offsets
+VL_FAULT_TOPLEFT_CAUSAL = 2   # each sequence's causal rule aligned at the top-left
+VL_FAULT_LSE_TOKEN_MAJOR = 3  # LSE laid out [Tq, Hq] instead of [Hq, Tq]
+
+
+def attention_varlen(q, k, v, cu_q: Sequence[int], cu_k: Optional[Sequence[int]] = None,
+                     scale: Optional[float] = None, is_causal: bool = False, tokens: Optional[Sequence[int]] = None,
+                     threads: int = 0, fault: int = VL_FAULT_NONE):
+    """Packed variable-length attention in fp64: each sequence is one dense problem.
+
+    q [Tq, Hq, D]; k, v [Tk, Hkv, D] (torch bf16/fp16); cu_q, cu_k: B+1 offsets (cu_k None: cu_q).
+    tokens: query token indices to compute (None: all).  Returns O [n, Hq, D] and LSE [Hq, n] as
+    float64 arrays, n = Tq or len(tokens).  A sequence with no key gives its rows O = 0, LSE = -inf
+    (the rule for rows that see no key).
+    """
+    cq = [int(x) for x in (cu_q.tolist() if hasattr(cu_q, "tolist") else cu_q)]
+    ck = cq if cu_k is None else [int(x) for x in (cu_k.tolist() if hasattr(cu_k, "tolist") else cu_k)]
+    Tq, Hq, D = (int(x) for x in q.shape)
+    Tk, Hkv, Dk = (int(x) for x in k.shape)
+    if tuple(v.shape) != tuple(k.shape) or Dk != D or len(cq) != len(ck) or len(cq) < 2:
+        raise ValueError("inconsistent packed shapes or offsets")
+    if cq[0] != 0 or ck[0] != 0 or cq[-1] != Tq or ck[-1] != Tk:
+        raise ValueError("offsets must start at 0 and end at the token counts")
+    if any(b < a for a, b in zip(cq, cq[1:])) or any(b < a for a, b in zip(ck, ck[1:])):
+        raise ValueError("offsets must not decrease")
+    if fault == VL_FAULT_SHARED_OFFSETS:
+        ck = [min(x, Tk) for x in cq]
+    want = np.arange(Tq) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    O = np.zeros((want.size, Hq, D), dtype=np.float64)
+    L = np.full((Hq, want.size), -np.inf, dtype=np.float64)
+    seq_of = np.searchsorted(np.asarray(cq[1:]), want, side="right")
+    dense_fault = FAULT_TOPLEFT_CAUSAL if fault == VL_FAULT_TOPLEFT_CAUSAL else FAULT_NONE
+    for b in range(len(cq) - 1):
+        sel = np.nonzero(seq_of == b)[0]
+        nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        if sel.size == 0 or nq == 0 or nk == 0:
+            continue  # no key: the rows keep O = 0, LSE = -inf
+        r = want[sel] - cq[b]
+        qs = q[cq[b]:cq[b + 1]].permute(1, 0, 2).unsqueeze(0)   # [1, Hq, nq, D]
+        ks = k[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0)   # [1, Hkv, nk, D]
+        vs = v[ck[b]:ck[b + 1]].permute(1, 0, 2).unsqueeze(0)
+        rows = (np.arange(Hq)[:, None] * nq + r[None, :]).reshape(-1)
+        o, lse = attention_rows(qs, ks, vs, rows, scale=scale, is_causal=is_causal, threads=threads,
+                                fault=dense_fault)
+        O[sel] = o.reshape(Hq, sel.size, D).transpose(1, 0, 2)
+        L[:, sel] = lse.reshape(Hq, sel.size)
+    if fault == VL_FAULT_LSE_TOKEN_MAJOR:
+        L = np.ascontiguousarray(L.T).reshape(Hq, want.size)
+    return O, L

@@ -125,6 +125,77 @@ def additive_mask(g: torch.Generator, B: int, Nq: int, Nkv: int, drop: float = 0
     return bias
 
 
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """A packed batch (ffpa-attn "API Reference", ffpa_attn_varlen_func): sequence b has lens_q[b]
+    query tokens and lens_k[b] key tokens; tensors [T, H, D]."""
+    name: str
+    lens_q: Tuple[int, ...]
+    lens_k: Tuple[int, ...]
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: torch.dtype = torch.bfloat16
+    seed: int = 0
+    causal: bool = False
+
+    @property
+    def flops(self) -> float:
+        """Sum over sequences of 4*Hq*Nq_b*Nkv_b*D, halved for causal (the metric's convention)."""
+        f = sum(4.0 * self.Hq * nq * nk * self.D for nq, nk in zip(self.lens_q, self.lens_k))
+        return f / 2 if self.causal else f
+
+    def describe(self) -> dict:
+        return dict(workload=self.name, B=len(self.lens_q), Hq=self.Hq, Hkv=self.Hkv, Tq=sum(self.lens_q),
+                    Tk=sum(self.lens_k), max_seqlen_q=max(self.lens_q), max_seqlen_k=max(self.lens_k), D=self.D,
+                    dtype=str(self.dtype).replace("torch.", ""), causal=self.causal, seed=self.seed,
+                    lens_q=list(self.lens_q))
+
+
+def varlen_causal() -> VarlenWorkload:
+    """Packed causal self-attention (a prefill batch): 8 sequences, lengths drawn uniformly from
+    256..8192 with seed 6, Hq = Hkv = 16, D = 512, bf16."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(6)
+    lens = tuple(int(x) for x in torch.randint(256, 8193, (8,), generator=g).tolist())
+    return VarlenWorkload("varlen_causal_B8_H16_D512", lens, lens, 16, 16, 512, seed=6, causal=True)
+
+
+def make_varlen_inputs(w: VarlenWorkload):
+    """Host tensors q [Tq, Hq, D], k/v [Tk, Hkv, D] (drawn by the recipe above, in the order q, k, v)
+    and the int32 offsets cu_q, cu_k [B+1]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed + 1)
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32).to(w.dtype)
+
+    Tq, Tk = sum(w.lens_q), sum(w.lens_k)
+    q = draw(Tq, w.Hq, w.D)
+    k = draw(Tk, w.Hkv, w.D)
+    v = draw(Tk, w.Hkv, w.D)
+    cu_q = torch.tensor([0] + list(torch.tensor(w.lens_q).cumsum(0).tolist()), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(torch.tensor(w.lens_k).cumsum(0).tolist()), dtype=torch.int32)
+    return q, k, v, cu_q, cu_k
+
+
+def sample_tokens(lens: Tuple[int, ...], seed: int, bucket: int = 64) -> List[int]:
+    """Packed query tokens to compare at full size: per sequence, one seeded token per `bucket`-token
+    bucket plus its first, second and last tokens."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 7907)
+    out, base = [], 0
+    for n in lens:
+        picked = {r for r in (0, 1, n - 1) if 0 <= r < n}
+        nb = (n + bucket - 1) // bucket
+        for i, o in enumerate(torch.randint(0, bucket, (nb,), generator=g).tolist()):
+            if i * bucket + o < n:
+                picked.add(i * bucket + o)
+        out.extend(base + r for r in sorted(picked))
+        base += n
+    return out
+
+
 def random_qkv(B: int, Hq: int, Hkv: int, Nq: int, Nkv: int, D: int, dtype=torch.bfloat16, seed: int = 0,
                factor: float = 1.0):
     """Small ad-hoc cases for tests, same recipe."""
