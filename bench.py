@@ -60,6 +60,44 @@ def time_workload(w, steps: int, warmup: int):
     return ms, (q, k, v, mask), (o.cpu(), lse.cpu())
 
 
+def time_varlen(w, steps: int, warmup: int):
+    """As time_workload, for a packed variable-length batch (one ffpa_fwd_varlen launch per step)."""
+    import torch
+
+    import exact_attention_head_amd as ffpa
+    import workloads as W
+
+    q, k, v, cu_q, cu_k = W.make_varlen_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, cqd, ckd = (t.to(dev) for t in (q, k, v, cu_q, cu_k))
+    Tq, Tk = q.shape[0], k.shape[0]
+    o = torch.empty_like(qd)
+    lse = torch.empty((w.Hq, Tq), dtype=torch.float32, device=dev)
+    dtype = ffpa.FFPA_BF16 if w.dtype == torch.bfloat16 else ffpa.FFPA_FP16
+    # the offsets are checked once on the host, as attn_varlen does before every launch
+    for c, T, mx in ((cu_q, Tq, max(w.lens_q)), (cu_k, Tk, max(w.lens_k))):
+        assert ffpa.ffpa_check_cu_seqlens(c.tolist(), T, mx) == ffpa.OK
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = ffpa.ffpa_fwd_varlen(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), cqd.data_ptr(), ckd.data_ptr(),
+                                  o.data_ptr(), lse.data_ptr(), len(w.lens_q), w.Hq, w.Hkv, Tq, Tk, max(w.lens_q),
+                                  max(w.lens_k), w.D, float("nan"), w.causal, dtype, stream.cuda_stream)
+        if st != ffpa.OK:
+            raise RuntimeError(f"ffpa_fwd_varlen returned {st}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(w, inputs, outputs, seconds: float):
     """Times the fp64 oracle on a bounded sample of rows of the same workload (all host threads it
     uses), scales to TFLOPS by the metric's FLOP count, and compares those rows with the GPU output."""
@@ -158,7 +196,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_d_self",
-                    help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16]")
+                    help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16] | varlen_causal")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -193,7 +231,11 @@ def main() -> int:
 
     w = pick(args.workload)
     log(f"workload {w.name}: warmup {args.warmup}, steps {args.steps}")
-    ms, inputs, outputs = time_workload(w, args.steps, args.warmup)
+    packed = isinstance(w, W.VarlenWorkload)
+    if packed:
+        ms, inputs, outputs = time_varlen(w, args.steps, args.warmup), None, None
+    else:
+        ms, inputs, outputs = time_workload(w, args.steps, args.warmup)
     tflops = w.flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak)")
 
@@ -209,11 +251,14 @@ def main() -> int:
     if args.sweep:
         names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
     else:
-        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512"]
+        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal"]
     if not args.no_secondary and args.workload == "large_d_self":
         for name in names:
             w2 = pick(name)
-            ms2, _, _ = time_workload(w2, max(5, args.steps // 5), 2)
+            if isinstance(w2, W.VarlenWorkload):
+                ms2 = time_varlen(w2, max(5, args.steps // 5), 2)
+            else:
+                ms2, _, _ = time_workload(w2, max(5, args.steps // 5), 2)
             tf2 = w2.flops / (ms2 * 1e-3) / 1e12
             log(f"{w2.name}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
             secondary.append(dict(workload=w2.name, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
@@ -221,7 +266,9 @@ def main() -> int:
                                   frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
 
     cpu, parity = None, None
-    if not args.no_cpu_baseline:
+    if packed and not args.no_cpu_baseline:
+        log("cpu baseline: measured on the dense workloads only")
+    elif not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on sampled rows (~{args.cpu_seconds:.0f} s)")
         cpu, parity = cpu_baseline(w, inputs, outputs, args.cpu_seconds)
         log(f"cpu baseline {cpu['value']:.4g} TFLOPS on {cpu['cores']} threads; parity {parity}")

@@ -4,7 +4,9 @@
 with the semantics of ffpa_attn_func on the ffpa-attn "API Reference" page: SDPA-style layout
 [B, H, N, D], GQA/MQA through enable_gqa, cross-attention (Nq != Nkv), tail-aligned causal masking
 (row r sees keys k <= r + Nkv - Nq, requiring Nkv >= Nq), boolean masks (True takes part) and
-additive floating masks, and scale = 1/sqrt(D) by default.
+additive floating masks, and scale = 1/sqrt(D) by default.  ``attn_varlen`` is the packed
+variable-length form of ffpa_attn_varlen_func on the same page: THD tensors [T, H, D], cumulative
+sequence offsets, the longest lengths, and an [Hq, Tq] LSE.
 
 Everything here is argument marshalling around the C ABI of ``libffpa.so`` (include/ffpa.h):
 tensors are passed by device pointer, outputs are allocated with torch, and the work is enqueued
@@ -18,7 +20,8 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn", "ffpa_fwd", "ffpa_check_args", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
+__all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
+           "ffpa_check_cu_seqlens", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +32,7 @@ MASK_NONE, MASK_BOOL_U8, MASK_ADD_F32, MASK_ADD_BF16, MASK_ADD_FP16 = 0, 1, 2, 3
 OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
-            "ffpa_kernel_name")
+            "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens")
 
 
 class MaskDesc(ctypes.Structure):
@@ -64,6 +67,13 @@ def library() -> ctypes.CDLL:
     lib.ffpa_rows_per_block.restype = i32
     lib.ffpa_kernel_name.argtypes = [i64]
     lib.ffpa_kernel_name.restype = ctypes.c_char_p
+    vargs = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32]
+    lib.ffpa_fwd_varlen.argtypes = vargs + [p]
+    lib.ffpa_fwd_varlen.restype = i32
+    lib.ffpa_check_varlen_args.argtypes = vargs
+    lib.ffpa_check_varlen_args.restype = i32
+    lib.ffpa_check_cu_seqlens.argtypes = [ctypes.POINTER(ctypes.c_int32), i64, i64, i64]
+    lib.ffpa_check_cu_seqlens.restype = i32
     _lib = lib
     return lib
 
@@ -90,6 +100,25 @@ def ffpa_check_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, N
     m = ctypes.byref(mask) if mask is not None else None
     return library().ffpa_check_args(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
                                      int(is_causal), dtype)
+
+
+def ffpa_fwd_varlen(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D, scale, is_causal, dtype,
+                    stream) -> int:
+    """The raw packed entry point: pointers are integers (device addresses), returns the status code."""
+    return library().ffpa_fwd_varlen(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D,
+                                     ctypes.c_float(scale), int(is_causal), dtype, stream)
+
+
+def ffpa_check_varlen_args(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D, scale, is_causal,
+                           dtype) -> int:
+    return library().ffpa_check_varlen_args(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D,
+                                            ctypes.c_float(scale), int(is_causal), dtype)
+
+
+def ffpa_check_cu_seqlens(offsets, T: int, max_seqlen: int) -> int:
+    """Checks a host sequence of B+1 cumulative offsets (ints); returns the status code."""
+    arr = (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
+    return library().ffpa_check_cu_seqlens(arr, len(offsets) - 1, T, max_seqlen)
 
 
 def rows_per_block(D: int) -> int:
@@ -171,6 +200,82 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
                       lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal),
                       dtype, stream)
     del keep
+    if st != OK:
+        _raise(st)
+    return (o, lse) if return_lse else o
+
+
+# keyword arguments of ffpa_attn_varlen_func that this forward rejects when given a non-default value
+_VARLEN_UNSUPPORTED = ("window_size", "softcap", "sink", "attention_mask", "attn_mask", "block_mask", "score_mod",
+                       "aux_tensors", "seqused_k", "block_table", "num_splits", "alibi_slopes")
+
+
+def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                dropout_p: float = 0.0, softmax_scale: Optional[float] = None, causal: bool = False,
+                enable_gqa: bool = False, return_lse: bool = False, **kwargs):
+    """Packed variable-length forward.  q [Tq, Hq, D]; k/v [Tk, Hkv, D]; cu_seqlens_* int32 [B+1]
+    (cu_seqlens_k None: the query offsets, for self-attention).  Each sequence is attended on its
+    own, with the tail-aligned causal rule of its own lengths.
+
+    Returns O [Tq, Hq, D], or (O, LSE [Hq, Tq] float32) with return_lse.  The offsets are checked on
+    a host copy (one device-to-host transfer) before the launch.
+    """
+    import torch
+
+    for name, val in kwargs.items():
+        if name in _VARLEN_UNSUPPORTED:
+            if val is not None and val is not False and not (name == "window_size" and tuple(val) == (-1, -1)):
+                raise NotImplementedError(f"{name} is not supported")
+        else:
+            raise TypeError(f"unexpected keyword argument {name!r}")
+    if dropout_p != 0.0:
+        raise NotImplementedError("attention dropout is not implemented (dropout_p must be 0)")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3:
+            raise ValueError(f"{name} must be a 3-D tensor [T, H, D]")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"q dtype {q.dtype} is neither bfloat16 nor float16")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if cu_seqlens_k is None:
+        cu_seqlens_k = cu_seqlens_q
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if not isinstance(c, torch.Tensor) or c.dtype != torch.int32:
+            raise TypeError(f"{name} must be an int32 tensor")
+        if c.dim() != 1 or c.numel() < 2:
+            raise ValueError(f"{name} must be 1-D with B+1 >= 2 entries")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    Tq, Hq, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must share [Tk, Hkv, D]")
+    if Dk != D:
+        raise ValueError("q and k disagree on the head dim")
+    if Hq != Hkv and not enable_gqa:
+        raise ValueError("Hq != Hkv needs enable_gqa=True")
+    B = cu_seqlens_q.numel() - 1
+    for c, T, mx in ((cu_seqlens_q, Tq, max_seqlen_q), (cu_seqlens_k, Tk, max_seqlen_k)):
+        st = ffpa_check_cu_seqlens(c.cpu().tolist(), T, int(mx))
+        if st != OK:
+            _raise(st)
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k and v must live on the same GPU")
+    cq = cu_seqlens_q.to(q.device).contiguous()
+    ck = cq if cu_seqlens_k is cu_seqlens_q else cu_seqlens_k.to(q.device).contiguous()
+    qc, kc, vc = q.contiguous(), k.contiguous(), v.contiguous()
+    dtype = FFPA_BF16 if q.dtype == torch.bfloat16 else FFPA_FP16
+    o = torch.empty((Tq, Hq, D), dtype=q.dtype, device=q.device)
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
+    sc = math.nan if softmax_scale is None else float(softmax_scale)
+
+    def ptr(t):
+        return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = ffpa_fwd_varlen(ptr(qc), ptr(kc), ptr(vc), cq.data_ptr(), ck.data_ptr(), ptr(o), ptr(lse), B, Hq, Hkv,
+                             Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), D, sc, bool(causal), dtype, stream)
     if st != OK:
         _raise(st)
     return (o, lse) if return_lse else o

@@ -115,6 +115,52 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
   return FFPA_OK;
 }
 
+// Argument rules of the packed entry (ffpa-attn "API Reference", ffpa_attn_varlen_func): the
+// same dtype, head and scale rules as the dense entry, plus the offsets' pointers and the 32-bit
+// offsets the kernels form (one sequence's key rows, and token x head indexes).
+int check_varlen(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                 const void* o, const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Tq, int64_t Tk,
+                 int64_t maxq, int64_t maxk, int64_t D, float scale, int is_causal, int dtype) {
+  g_detail[0] = '\0';
+  if (dtype != FFPA_BF16 && dtype != FFPA_FP16) return fail(FFPA_ERR_TYPE, "dtype %d is neither bf16 nor fp16", dtype);
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1)
+    return fail(FFPA_ERR_VALUE, "B, Hq, Hkv and D must be >= 1 (B=%lld Hq=%lld Hkv=%lld D=%lld)", (long long)B,
+                (long long)Hq, (long long)Hkv, (long long)D);
+  if (Tq < 0 || Tk < 0 || maxq < 0 || maxk < 0)
+    return fail(FFPA_ERR_VALUE, "token counts and longest lengths must be >= 0");
+  if (Hq % Hkv != 0)
+    return fail(FFPA_ERR_VALUE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)Hq, (long long)Hkv);
+  if (is_causal != 0 && is_causal != 1) return fail(FFPA_ERR_VALUE, "is_causal must be 0 or 1");
+  if (std::isinf(scale)) return fail(FFPA_ERR_VALUE, "scale must be finite (NaN selects 1/sqrt(D))");
+  if (cu_q == nullptr || cu_k == nullptr) return fail(FFPA_ERR_VALUE, "cu_seqlens_q and cu_seqlens_k must be non-null");
+  if (((uintptr_t)cu_q | (uintptr_t)cu_k) & 3) return fail(FFPA_ERR_VALUE, "cu_seqlens must be 4-byte aligned");
+  if ((Tq > 0 && (q == nullptr || o == nullptr)) || (Tk > 0 && (k == nullptr || v == nullptr)))
+    return fail(FFPA_ERR_VALUE, "q, k, v and o must be non-null when their tensors are not empty");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
+    return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
+  if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
+  if (D < 64 || D > 1024 || D % 64 != 0)
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
+  const int br = rows_for(D);
+  if (B > (1LL << 30) || B * Hq * ((maxq + br - 1) / br) > 0x7fffffffLL)
+    return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
+  if (Tq >= (1LL << 31) || Tk >= (1LL << 31) || Tq * Hq >= (1LL << 31) || Tk * Hkv >= (1LL << 31))
+    return fail(FFPA_ERR_UNSUPPORTED, "token x head counts beyond the 32-bit indexing of the kernels");
+  if ((maxq + 256) * Hq * D * 2 >= (1LL << 31) || (maxk + 256) * Hkv * D * 2 >= (1LL << 31))
+    return fail(FFPA_ERR_UNSUPPORTED, "one sequence's Q or K/V rows must span below 2 GiB (buffer addressing)");
+  const size_t qbytes = (size_t)(Tq * Hq * D) * 2, kvbytes = (size_t)(Tk * Hkv * D) * 2;
+  const size_t lbytes = lse ? (size_t)(Tq * Hq) * 4 : 0, cbytes = (size_t)(B + 1) * 4;
+  if (ranges_overlap(o, qbytes, q, qbytes) || ranges_overlap(o, qbytes, k, kvbytes) ||
+      ranges_overlap(o, qbytes, v, kvbytes) || ranges_overlap(o, qbytes, lse, lbytes) ||
+      ranges_overlap(o, qbytes, cu_q, cbytes) || ranges_overlap(o, qbytes, cu_k, cbytes))
+    return fail(FFPA_ERR_VALUE, "o must not overlap q, k, v, lse or the offsets");
+  if (lse != nullptr && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
+                         ranges_overlap(lse, lbytes, v, kvbytes) || ranges_overlap(lse, lbytes, cu_q, cbytes) ||
+                         ranges_overlap(lse, lbytes, cu_k, cbytes)))
+    return fail(FFPA_ERR_VALUE, "lse must not overlap q, k, v or the offsets");
+  return FFPA_OK;
+}
+
 template <typename T>
 hipError_t dispatch(int64_t D, const ffpa::FwdArgs& a, hipStream_t s) {
   switch (D) {
@@ -171,6 +217,64 @@ int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mas
   const hipStream_t s = (hipStream_t)stream;
   const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FFPA_OK;
+}
+
+int ffpa_check_varlen_args(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const void* o, const float* lse, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                           int64_t D, float scale, int is_causal, int dtype) {
+  return check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, B, Hq, Hkv, Tq, Tk, max_seqlen_q, max_seqlen_k, D,
+                      scale, is_causal, dtype);
+}
+
+int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, float scale,
+                    int is_causal, int dtype, void* stream) {
+  const int st = check_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, o, lse, B, Hq, Hkv, Tq, Tk, max_seqlen_q,
+                              max_seqlen_k, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  if (Tq == 0 || max_seqlen_q == 0) return FFPA_OK;  // no query row anywhere
+  ffpa::FwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.mask_kind = ffpa::kMaskNone;
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Nq = (int)max_seqlen_q;
+  a.Nkv = (int)max_seqlen_k;
+  a.group = (int)(Hq / Hkv);
+  const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.causal = is_causal;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.Tq = (int)Tq;
+  a.Tk = (int)Tk;
+  const hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FFPA_OK;
+}
+
+int ffpa_check_cu_seqlens(const int32_t* cu_host, int64_t B, int64_t T, int64_t max_seqlen) {
+  g_detail[0] = '\0';
+  if (cu_host == nullptr || B < 1) return fail(FFPA_ERR_VALUE, "need B >= 1 and B+1 offsets");
+  if (cu_host[0] != 0) return fail(FFPA_ERR_VALUE, "cu_seqlens[0] is %d, not 0", (int)cu_host[0]);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t len = (int64_t)cu_host[b + 1] - cu_host[b];
+    if (len < 0) return fail(FFPA_ERR_VALUE, "cu_seqlens decreases at index %lld", (long long)(b + 1));
+    if (len > max_seqlen)
+      return fail(FFPA_ERR_VALUE, "sequence %lld has %lld tokens, more than max_seqlen %lld", (long long)b,
+                  (long long)len, (long long)max_seqlen);
+  }
+  if (cu_host[B] != T)
+    return fail(FFPA_ERR_VALUE, "cu_seqlens[B] is %d, not the token count %lld", (int)cu_host[B], (long long)T);
   return FFPA_OK;
 }
 

@@ -87,7 +87,29 @@ struct FwdArgs {
   int B, Hq, Hkv, Nq, Nkv, group;
   float scale_log2;       // scale * log2(e)
   int causal;
+  // Packed variable-length batch (null cu_q: the dense [B, H, N, D] layout).  Q/O are [Tq, Hq, D]
+  // and K/V [Tk, Hkv, D]; sequence b holds query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens
+  // cu_k[b] .. cu_k[b+1]-1; Nq and Nkv above are then the longest lengths (they size the grid);
+  // LSE is [Hq, Tq].
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int Tq, Tk;
 };
+
+// Tokens of sequence b of a packed batch.  The offsets are clamped to the packed tensors and the
+// lengths to the longest lengths, so that malformed offsets can change results but never move an
+// access outside the tensors (the C ABI documents the well-formed case).
+struct SeqRange {
+  int q0, nq, k0, nkv;
+};
+__device__ inline SeqRange seq_range(const FwdArgs& a, int b) {
+  auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+  const int q0 = clampi(a.cu_q[b], 0, a.Tq), q1 = clampi(a.cu_q[b + 1], q0, a.Tq);
+  const int k0 = clampi(a.cu_k[b], 0, a.Tk), k1 = clampi(a.cu_k[b + 1], k0, a.Tk);
+  const int nq = q1 - q0 < a.Nq ? q1 - q0 : a.Nq;
+  const int nkv = k1 - k0 < a.Nkv ? k1 - k0 : a.Nkv;
+  return SeqRange{q0, nq, k0, nkv};
+}
 
 struct Bf16 {};
 struct Fp16 {};
@@ -553,6 +575,7 @@ struct ChunkLoader {
   static_assert(DG * NROWS * 4 % 256 == 0, "whole loads");
   uint32_t voff[N];
 
+  // D: the tensor's row stride in elements (the head dim, or heads x head dim when packed)
   __device__ inline void init(int D, int wave, int lane) {
 #pragma unroll
     for (int t = 0; t < N; ++t) {
@@ -567,7 +590,8 @@ struct ChunkLoader {
   // head: first element of the [rows, D] block; rows: its row count; chunk origin (row0, col).
   __device__ inline void issue(char* dst, const uint16_t* head, int rows, int row0, int col, int D, int wave) const {
     const int64_t start = (int64_t)row0 * D + col;
-    const uint32_t bytes = (uint32_t)(((int64_t)rows * D - start) * 2);
+    const int64_t left = (int64_t)rows * D - start;  // elements from the chunk origin to the block's end
+    const uint32_t bytes = left > 0 ? (uint32_t)(left * 2) : 0u;
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(head + start), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
@@ -596,9 +620,11 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item: (b, hq, q tile); consecutive items go to one XCD so that a head's tiles share L2
-  const int Nq = a.Nq, Nkv = a.Nkv;
-  const int nqt = (Nq + BR - 1) / BR;
+  // ---- work item: (b, hq, q tile); consecutive items go to one XCD so that a head's tiles share L2.
+  // A packed batch (cu_q set) sizes the grid by its longest sequence; items past their sequence's
+  // query length leave at once (the whole workgroup, before any barrier).
+  const bool packed = a.cu_q != nullptr;
+  const int nqt = (a.Nq + BR - 1) / BR;
   const int total = a.B * a.Hq * nqt;
   int id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
@@ -609,32 +635,48 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   if (a.causal) qt = nqt - 1 - qt;  // longest tiles of a head first
   const int hk = hq / a.group;
   const int r0 = qt * BR;              // first query row of the workgroup
+  int Nq = a.Nq, Nkv = a.Nkv;
+  int64_t q_base = (int64_t)(b * a.Hq + hq) * Nq * D, kv_base = (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  int64_t lse_base = (int64_t)(b * a.Hq + hq) * Nq;
+  int q_rs = D, kv_rs = D;             // row strides (elements)
+  if (packed) {
+    const SeqRange sr = seq_range(a, b);
+    Nq = sr.nq;
+    Nkv = sr.nkv;
+    q_base = (int64_t)sr.q0 * a.Hq * D + hq * D;
+    kv_base = (int64_t)sr.k0 * a.Hkv * D + hk * D;
+    lse_base = (int64_t)hq * a.Tq + sr.q0;
+    q_rs = a.Hq * D;
+    kv_rs = a.Hkv * D;
+    if (r0 >= Nq) return;
+  }
   const int rw0 = r0 + rg * R;         // first query row of this wave
   const int col0 = dg * DW;            // first output column of this wave
   const int off = Nkv - Nq;            // tail alignment of the causal rule
 
-  const uint16_t* qg = a.q + (int64_t)(b * a.Hq + hq) * Nq * D;
-  const uint16_t* kg = a.k + (int64_t)(b * a.Hkv + hk) * Nkv * D;
-  const uint16_t* vg = a.v + (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  const uint16_t* qg = a.q + q_base;
+  const uint16_t* kg = a.k + kv_base;
+  const uint16_t* vg = a.v + kv_base;
 
   int kv_end = Nkv;
   if (a.causal) {
     const int lim = r0 + BR + off;
     kv_end = lim < Nkv ? lim : Nkv;
+    kv_end = kv_end > 0 ? kv_end : 0;  // a packed sequence may hold fewer keys than queries
   }
   const int ntiles = (kv_end + BC - 1) / BC;
 
   ChunkLoader<DG, DW, BR> q_loader;
   ChunkLoader<DG, DW, BC> kv_loader;
-  q_loader.init(D, wave, lane);
-  kv_loader.init(D, wave, lane);
+  q_loader.init(q_rs, wave, lane);
+  kv_loader.init(kv_rs, wave, lane);
 
   // ---- Q fragments kept for the whole key loop (D <= 512): qf[rb][k-step of 16 columns]
   i32x4 qf[QREG ? RB : 1][QREG ? DW / 16 : 1];
   if constexpr (QREG) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      q_loader.issue(qk_ring, qg, Nq, r0, c * 32, D, wave);
+      q_loader.issue(qk_ring, qg, Nq, r0, c * 32, q_rs, wave);
       wait_vmem<0>();
       block_sync();
 #pragma unroll
@@ -653,12 +695,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   // ---- stage issue: K stage (j, c) -> QK slot (j*NC + c) % 3; V stage (j, c) -> V slot (j*NC + c) % 3
   auto issue_k = [&](int j, int c) {
     char* slot = qk_ring + ((j * NC + c) % 3) * K::QK_SLOT;
-    if constexpr (!QREG) q_loader.issue(slot, qg, Nq, r0, c * 32, D, wave);
-    kv_loader.issue(slot + K::Q_PART, kg, Nkv, j * BC, c * 32, D, wave);
+    if constexpr (!QREG) q_loader.issue(slot, qg, Nq, r0, c * 32, q_rs, wave);
+    kv_loader.issue(slot + K::Q_PART, kg, Nkv, j * BC, c * 32, kv_rs, wave);
   };
   auto issue_v = [&](int j, int c) {
     char* slot = v_ring + ((j * NC + c) % 3) * K::V_SLOT;
-    kv_loader.issue(slot, vg, Nkv, j * BC, c * 32, D, wave);
+    kv_loader.issue(slot, vg, Nkv, j * BC, c * 32, kv_rs, wave);
   };
 
   // ---- running state
@@ -677,8 +719,10 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   // mask base for this (b, hq)
   const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
 
-  issue_k(0, 0);
-  issue_k(0, 1);
+  if (ntiles > 0) {  // (a packed sequence may have no key to load)
+    issue_k(0, 0);
+    issue_k(0, 1);
+  }
 
   for (int j = 0; j < ntiles; ++j) {
     // ================= S^T = K Q^T over this wave's columns (Split-D chunks) =================
@@ -929,7 +973,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
     if (row < Nq) {
       const float l = l_run[rb];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* orow = a.o + ((int64_t)(b * a.Hq + hq) * Nq + row) * D + col0;
+      uint16_t* orow = a.o + q_base + (int64_t)row * q_rs + col0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -943,7 +987,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
       }
       if (a.lse != nullptr && dg == 0 && hi == 0) {
         const float lse = l > 0.f ? (m_run[rb] + __builtin_log2f(l)) * kLn2 : kNegInf;
-        a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
+        a.lse[lse_base + row] = lse;
       }
     }
   }
@@ -974,8 +1018,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   using K = FwdKernel<T, D>;
   // The kernels index K/V heads as hq / group: refuse a grouping that does not tile Hq exactly
   // (the C ABI validates its arguments; this guards every other caller of the launcher).
-  if (a.group < 1 || a.Hkv < 1 || a.Hq != a.group * a.Hkv || a.B < 1 || a.Nq < 1 || a.Nkv < 1)
+  const bool packed = a.cu_q != nullptr;
+  if (a.group < 1 || a.Hkv < 1 || a.Hq != a.group * a.Hkv || a.B < 1 || a.Nq < 1 || a.Nkv < (packed ? 0 : 1))
     return hipErrorInvalidValue;
+  // a packed batch has both offset arrays and no mask
+  if (packed && (a.cu_k == nullptr || a.mask_kind != kMaskNone || a.Tq < 0 || a.Tk < 0)) return hipErrorInvalidValue;
   constexpr int BR = rows_per_block<D>();
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
@@ -986,14 +1033,23 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     const bool staged_mask = a.mask_kind == kMaskAddF32 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
                              a.msq % 32 == 0 &&
                              ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq * 4 + (int64_t)a.Nkv * 4 < (1LL << 31);
-    if (staged_mask)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    // packed batches: the lengths live on the device, so whole and partial tiles are told apart
+    // in the kernel
+    if (packed && plain)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (packed)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+    else if (staged_mask)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
     else if (plain && !a.causal && a.Nkv % 64 == 0)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    else if (plain && a.causal)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowCausal>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (plain)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
   } else {
     hipLaunchKernelGGL((ffpa_fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(K::THREADS), 0, stream, a);
   }

@@ -199,12 +199,13 @@ constexpr int row_load_slot(int bs, int q, int step, int MPT) {
 // positive factor keeps the order) and the scale is folded into the exponent,
 // p = exp2(s * scale_log2 - m).  Other tiles form the logits explicitly (scale, mask bias, -inf
 // for keys past Nkv or past the causal limit).  MODE selects the kernel's tiles: kRowGeneral (every
-// tile explicit), kRowRaw (every tile raw: no mask, no causal limit, whole tiles), kRowCausal (no
-// mask, causal: the tiles below the workgroup's diagonal raw, the diagonal ones explicit, in two
-// successive loops), kRowMaskF32 (every tile explicit, with an fp32 additive mask whose rows are
+// tile explicit), kRowRaw (every tile raw: no mask, no causal limit, whole tiles), kRowSplit (no
+// mask: the tiles that every row of the workgroup sees whole are raw, the rest (the causal
+// diagonal, a partial last tile) explicit, in two successive loops), kRowMaskF32 (every tile
+// explicit, with an fp32 additive mask whose rows are
 // staged through LDS: whole 128-byte lines per direct-to-LDS load, one tile ahead, instead of
 // scattered 16-byte loads per lane).  The launcher picks the variant.
-enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowCausal = 2, kRowMaskF32 = 3 };
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3 };
 
 // Loads (per wave) issued in slot x of a tile: load q of the refill after the barrier at slot
 // e*EM - PF goes to row_load_slot(...).
@@ -237,7 +238,9 @@ constexpr bool row_barrier_within(int first, int last, int EM, int PF) {
   return false;
 }
 
-template <typename T, int D, int MODE>
+// VL: a packed variable-length batch (FwdArgs::cu_q): row strides of heads x D elements and
+// per-sequence lengths, offsets and LSE layout; the dense layout keeps them compile-time.
+template <typename T, int D, int MODE, bool VL>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   using RT = RowTiling<D>;
   using E = Elem<T>;
@@ -287,9 +290,10 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // ---- work item (b, hq, q tile); consecutive items share an XCD's L2
-  const int Nq = a.Nq, Nkv = a.Nkv;
-  const int nqt = (Nq + BR - 1) / BR;
+  // ---- work item (b, hq, q tile); consecutive items share an XCD's L2.  A packed batch sizes the
+  // grid by its longest sequence; items past their sequence's query length leave at once (the
+  // whole workgroup, before any barrier).
+  const int nqt = (a.Nq + BR - 1) / BR;
   const int total = a.B * a.Hq * nqt;
   int id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
@@ -300,17 +304,32 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   if (a.causal) qt = nqt - 1 - qt;  // heaviest tiles first
   const int hk = hq / a.group;
   const int r0 = qt * BR;
+  int Nq = a.Nq, Nkv = a.Nkv;
+  int64_t q_base = (int64_t)(b * a.Hq + hq) * Nq * D, kv_base = (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  int64_t lse_base = (int64_t)(b * a.Hq + hq) * Nq;
+  if constexpr (VL) {
+    const SeqRange sr = seq_range(a, b);
+    Nq = sr.nq;
+    Nkv = sr.nkv;
+    q_base = (int64_t)sr.q0 * a.Hq * D + hq * D;
+    kv_base = (int64_t)sr.k0 * a.Hkv * D + hk * D;
+    lse_base = (int64_t)hq * a.Tq + sr.q0;
+    if (r0 >= Nq) return;
+  }
+  const int q_rs = VL ? a.Hq * D : D;    // row strides (elements)
+  const int kv_rs = VL ? a.Hkv * D : D;
   const int rw0 = r0 + rg * 32;  // first row of this wave
   const int row = rw0 + l32;     // this lane's row
   const int col0 = dg * DW;
   const int off = Nkv - Nq;
-  const uint16_t* qg = a.q + (int64_t)(b * a.Hq + hq) * Nq * D;
-  const uint16_t* kg = a.k + (int64_t)(b * a.Hkv + hk) * Nkv * D;
-  const uint16_t* vg = a.v + (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  const uint16_t* qg = a.q + q_base;
+  const uint16_t* kg = a.k + kv_base;
+  const uint16_t* vg = a.v + kv_base;
   int kv_end = Nkv;
   if (a.causal) {
     const int lim = r0 + BR + off;
     kv_end = lim < Nkv ? lim : Nkv;
+    kv_end = kv_end > 0 ? kv_end : 0;  // a packed sequence may hold fewer keys than queries
   }
   const int ntiles = (kv_end + BC - 1) / BC;
   const int total_epochs = ntiles * EPT;
@@ -319,7 +338,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   i32x4 qf[DW / 16];
   {
     const int qrow = row < Nq ? row : Nq - 1;
-    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * D + col0 + hi * 8);
+    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 8);
 #pragma unroll
     for (int k = 0; k < DW / 16; ++k) qf[k] = src[k * 2];
     // complete here, and redefine through the assembler: the compiler then has no load of these
@@ -335,8 +354,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   // lane's byte offset = fixed lane part + tile part + a constant per group.
   const int prow = 8 * wave + (lane >> 3);
   auto pi7 = [](int x) { return ((x & 1) << 2) | (x >> 1); };
-  const uint32_t voff_lane = (uint32_t)((prow * D + ((lane & 7) ^ pi7((prow >> 1) & 7)) * 8) * 2);
-  const int head_bytes = (int)((int64_t)Nkv * D * 2);
+  const uint32_t voff_lane = (uint32_t)((prow * kv_rs + ((lane & 7) ^ pi7((prow >> 1) & 7)) * 8) * 2);
+  const int head_bytes = (int)((int64_t)Nkv * kv_rs * 2);
+  const uint32_t rows32_bytes = (uint32_t)(32 * kv_rs * 2);  // packed: byte step of 32 key rows
   const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, 0x00020000);
   char* const ring_w = smem + wave * 1024;
@@ -344,10 +364,18 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   auto issue_sub = [&](uint32_t vt, auto td_c, auto gi_c, auto cg_c) {
     constexpr int TD = decltype(td_c)::value, gi = decltype(gi_c)::value, cg = decltype(cg_c)::value;
     constexpr int ph = gi / GPP, w = gi % GPP;
-    constexpr uint32_t cst = (uint32_t)(((TD * BC + (ph & 1) * 32) * D + cg * DW + 64 * w) * 2);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v,
-                                             (FFPA_LDS void*)(ring_w + cg * CGB + (gi % NG) * 4096), 16, vt + cst, 0,
-                                             0, 0);
+    if constexpr (!VL) {
+      constexpr uint32_t cst = (uint32_t)(((TD * BC + (ph & 1) * 32) * D + cg * DW + 64 * w) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v,
+                                               (FFPA_LDS void*)(ring_w + cg * CGB + (gi % NG) * 4096), 16, vt + cst,
+                                               0, 0, 0);
+    } else {
+      // the row part of the offset is a runtime multiple of the row stride: a scalar offset
+      const uint32_t so = (uint32_t)(2 * TD + (ph & 1)) * rows32_bytes + (uint32_t)((cg * DW + 64 * w) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ph < 2 ? rsrc_k : rsrc_v,
+                                               (FFPA_LDS void*)(ring_w + cg * CGB + (gi % NG) * 4096), 16, vt, so,
+                                               0, 0);
+    }
   };
   auto issue_group = [&](uint32_t vt, auto td_c, auto gi_c) {
     static_for<DG>([&](auto cg_c) { issue_sub(vt, td_c, gi_c, cg_c); });
@@ -486,7 +514,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     int edge_lim = Nkv - 1;
     if (a.causal) edge_lim = edge_lim < row + off ? edge_lim : row + off;
     edge_lim -= key0;
-    uint32_t vt = voff_lane + (uint32_t)(j * BC * D * 2);
+    uint32_t vt = voff_lane + (uint32_t)j * 2 * rows32_bytes;
     asm volatile("" : "+v"(vt));  // keeps the per-group constants from being hoisted as 32 live registers
     LogitCtx ctx{a.mask, mask_bh, a.msq, Nq, Nkv, key0, rw0, off, a.causal, edge, a.scale_log2, l32, hi};
 
@@ -708,10 +736,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
   } else {
-    static_assert(MODE == kRowCausal, "tile mode");
-    // tiles whose last key is visible to the workgroup's first row are visible to all its rows
-    int nraw = (r0 + off + 1) / BC;
+    static_assert(MODE == kRowSplit, "tile mode");
+    // tiles whose keys all lie below Nkv and (causal) whose last key is visible to the workgroup's
+    // first row are whole for all its rows
+    int nraw = (a.causal ? r0 + off + 1 : Nkv) / BC;
     nraw = nraw < ntiles ? nraw : ntiles;
+    nraw = nraw > 0 ? nraw : 0;
     for (int j = 0; j < nraw; ++j) tile_body(j, std::true_type{});
     for (int j = nraw; j < ntiles; ++j) tile_body(j, std::false_type{});
   }
@@ -723,7 +753,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const float l = sum_halves(l_lane);
   if (row < Nq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = a.o + ((int64_t)(b * a.Hq + hq) * Nq + row) * D + col0;
+    uint16_t* orow = a.o + q_base + (int64_t)row * q_rs + col0;
     static_for<NSUB>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
 #pragma unroll
@@ -738,7 +768,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     });
     if (a.lse != nullptr && dg == 0 && hi == 0) {
       const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
-      a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
+      a.lse[lse_base + row] = lse;
     }
   }
 }

@@ -115,6 +115,57 @@ int ffpa_rows_per_block(int64_t D);
  * static string. */
 const char* ffpa_kernel_name(int64_t D);
 
+/*
+ * ffpa_fwd_varlen -- enqueue the attention forward over a packed batch of
+ * sequences of different lengths (ffpa-attn "API Reference" page,
+ * ffpa_attn_varlen_func: packed THD layout, cumulative sequence offsets,
+ * longest lengths, and an [H_q, T_q] fp32 LSE).  Sequence b takes query
+ * tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key tokens
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1, and each sequence is one dense
+ * problem of the form above (GQA heads, tail-aligned causal rule with its own
+ * Nq_b and Nkv_b; no mask).
+ *
+ *   q, o  device, [Tq, Hq, D], contiguous, dtype elements (o written)
+ *   k, v  device, [Tk, Hkv, D], contiguous, dtype elements
+ *   cu_seqlens_q, cu_seqlens_k  device, B+1 int32 each: 0 = c[0] <= c[1] <= ...
+ *         <= c[B] = Tq (resp. Tk).  May be the same array.
+ *   lse   device, [Hq, Tq] float32, natural log; written; NULL skips it
+ *   B >= 1, Hq >= 1, Hkv >= 1 with Hq % Hkv == 0, Tq >= 0, Tk >= 0
+ *   max_seqlen_q, max_seqlen_k  at least every sequence's query (key) length;
+ *         they size the grid and the kernels' 32-bit offsets
+ *   D, scale, dtype, stream  as for ffpa_fwd
+ *   is_causal  0 or 1.  A sequence with fewer keys than queries is allowed:
+ *         its first Nq_b - Nkv_b rows see no key, and every row that sees no
+ *         key (also any row of a sequence with no keys) gets O = 0 and
+ *         LSE = -inf.
+ *
+ * The offsets live in device memory, so the host cannot read them: offsets
+ * that break the rules above give unspecified values in o and lse (the
+ * kernels clamp every sequence to [0, Tq) and [0, Tk) and to the longest
+ * lengths, so no access leaves the tensors), and rows past max_seqlen_q of a
+ * longer sequence are not written.  ffpa_check_cu_seqlens checks a host copy.
+ * q, k, v and o must be 16-byte aligned (pointers of empty tensors may be
+ * NULL); o must not overlap q, k, v, lse or the offsets.  Tq == 0 or
+ * max_seqlen_q == 0 enqueues nothing.  Other rules as for ffpa_fwd.
+ */
+int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                    const int32_t* cu_seqlens_k, void* o, float* lse, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, float scale,
+                    int is_causal, int dtype, void* stream);
+
+/* The host-side argument check ffpa_fwd_varlen performs (the offsets are not
+ * read), without enqueuing anything. */
+int ffpa_check_varlen_args(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const void* o, const float* lse, int64_t B, int64_t Hq,
+                           int64_t Hkv, int64_t Tq, int64_t Tk, int64_t max_seqlen_q, int64_t max_seqlen_k,
+                           int64_t D, float scale, int is_causal, int dtype);
+
+/* Checks a HOST copy of B+1 cumulative offsets against the rules of
+ * ffpa_fwd_varlen: c[0] == 0, non-decreasing, c[B] == T, and every length
+ * c[b+1] - c[b] <= max_seqlen.  FFPA_ERR_VALUE (with a detail) if not.
+ * Host-only; reads cu_host[0..B]. */
+int ffpa_check_cu_seqlens(const int32_t* cu_host, int64_t B, int64_t T, int64_t max_seqlen);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,3 +68,46 @@ def compare(o_gpu, lse_gpu, q, k, v, rows=None, mask=None, is_causal=False, scal
     assert rel_l2 <= O_REL_L2, m
     assert lse_err <= LSE_MAX_ABS, m
     return m
+
+
+def run_gpu_varlen(q, k, v, cu_q, cu_k, max_q=None, max_k=None, causal=False, scale=None):
+    """Packed host tensors in, host tensors out: O [Tq, Hq, D] and LSE [Hq, Tq]; one kernel launch."""
+    dev = torch.device("cuda:0")
+    lq = (cu_q[1:] - cu_q[:-1]).tolist()
+    lk = (cu_k[1:] - cu_k[:-1]).tolist()
+    max_q = max(lq) if max_q is None else max_q
+    max_k = max(lk) if max_k is None else max_k
+    o, lse = ffpa.attn_varlen(q.to(dev), k.to(dev), v.to(dev), cu_q.to(dev), cu_k.to(dev), max_q, max_k,
+                              softmax_scale=scale, causal=causal, enable_gqa=q.shape[1] != k.shape[1],
+                              return_lse=True)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def compare_varlen(o_gpu, lse_gpu, q, k, v, cu_q, cu_k, tokens=None, causal=False, scale=None):
+    """Element-by-element comparison of packed GPU rows with the oracle, to the tolerances above; rows
+    that see no key must be O = 0 and LSE = -inf exactly."""
+    Tq, Hq, D = q.shape
+    og = o_gpu.float()
+    lg = lse_gpu
+    assert torch.isfinite(og).all(), "non-finite values in O"
+    assert not torch.isnan(lg).any() and not (lg == math.inf).any(), "NaN or +inf in LSE"
+    toks = np.arange(Tq) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    o_ref, l_ref = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=scale, is_causal=causal, tokens=toks)
+    o_g = og.numpy().astype(np.float64)[toks]
+    l_g = lg.numpy().astype(np.float64)[:, toks]
+    dead = ~np.isfinite(l_ref)
+    assert np.array_equal(np.isfinite(l_g), ~dead), "LSE finiteness differs from the oracle"
+    assert np.all(l_g[dead] == -math.inf)
+    assert np.all(o_g.transpose(1, 0, 2)[dead] == 0), "rows with no visible key must be 0"
+    err = np.abs(o_g - o_ref)
+    max_abs = float(err.max()) if err.size else 0.0
+    ref_norm = float(np.linalg.norm(o_ref))
+    rel_l2 = float(np.linalg.norm(o_g - o_ref) / ref_norm) if ref_norm > 0 else float(np.linalg.norm(o_g))
+    lse_err = float(np.abs(l_g[~dead] - l_ref[~dead]).max()) if (~dead).any() else 0.0
+    m = dict(tokens=int(toks.size), o_max_abs=max_abs, o_rel_l2=rel_l2, lse_max_abs=lse_err,
+             dead_rows=int(dead.sum()))
+    assert max_abs <= O_MAX_ABS, m
+    assert rel_l2 <= O_REL_L2, m
+    assert lse_err <= LSE_MAX_ABS, m
+    return m

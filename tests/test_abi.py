@@ -139,3 +139,76 @@ def test_python_layer_rejects_before_the_library():
     kb = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):  # not on a GPU
         ffpa.attn(qb, kb, kb, enable_gqa=True)
+
+
+# ---- packed variable-length entry (ffpa_fwd_varlen)
+CQ, CK = 0x70_0000_0000, 0x80_0000_0000
+
+
+def vcheck(B=3, Hq=4, Hkv=2, Tq=300, Tk=500, mq=200, mk=300, D=512, scale=math.nan, causal=False,
+           dtype=ffpa.FFPA_BF16, q=Q, k=K, v=V, cq=CQ, ck=CK, o=O, lse=L):
+    return ffpa.ffpa_check_varlen_args(q, k, v, cq, ck, o, lse, B, Hq, Hkv, Tq, Tk, mq, mk, D, scale, causal, dtype)
+
+
+def test_varlen_valid_arguments_pass():
+    assert vcheck() == ffpa.OK and detail() == ""
+    for D in range(64, 1025, 64):
+        assert vcheck(D=D) == ffpa.OK, D
+    assert vcheck(causal=True, mq=500, mk=10) == ffpa.OK   # fewer keys than queries is allowed
+    assert vcheck(Tq=0, Tk=0, mq=0, mk=0, q=None, k=None, v=None, o=None) == ffpa.OK
+    assert vcheck(Tk=0, mk=0, k=None, v=None) == ffpa.OK
+    assert vcheck(cq=CQ, ck=CQ) == ffpa.OK  # self-attention shares one offset array
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), ffpa.ERR_TYPE),
+    (dict(B=0), ffpa.ERR_VALUE),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE),
+    (dict(Tq=-1), ffpa.ERR_VALUE),
+    (dict(mk=-1), ffpa.ERR_VALUE),
+    (dict(causal=2), ffpa.ERR_VALUE),
+    (dict(scale=math.inf), ffpa.ERR_VALUE),
+    (dict(cq=None), ffpa.ERR_VALUE),
+    (dict(ck=CK + 2), ffpa.ERR_VALUE),
+    (dict(q=None), ffpa.ERR_VALUE),
+    (dict(o=O + 8), ffpa.ERR_VALUE),
+    (dict(o=Q + 64), ffpa.ERR_VALUE),          # o overlaps q
+    (dict(o=CQ - 64), ffpa.ERR_VALUE),         # o overlaps the offsets
+    (dict(D=96), ffpa.ERR_UNSUPPORTED),
+    (dict(mk=1 << 20, Hkv=4, Hq=4, D=1024), ffpa.ERR_UNSUPPORTED),  # one sequence's K rows beyond 2 GiB
+])
+def test_varlen_argument_errors(kw, status):
+    assert vcheck(**kw) == status, kw
+    assert detail() != ""
+
+
+def test_cu_seqlens_host_check():
+    assert ffpa.ffpa_check_cu_seqlens([0, 3, 3, 10], 10, 7) == ffpa.OK
+    assert ffpa.ffpa_check_cu_seqlens([1, 3, 10], 10, 7) == ffpa.ERR_VALUE
+    assert ffpa.ffpa_check_cu_seqlens([0, 5, 3, 10], 10, 7) == ffpa.ERR_VALUE
+    assert ffpa.ffpa_check_cu_seqlens([0, 3, 9], 10, 7) == ffpa.ERR_VALUE
+    assert ffpa.ffpa_check_cu_seqlens([0, 3, 10], 10, 6) == ffpa.ERR_VALUE   # a sequence longer than max
+    assert "max_seqlen" in detail()
+
+
+def test_varlen_python_layer_rejects_before_the_library():
+    import torch
+
+    q = torch.zeros(10, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(NotImplementedError):
+        ffpa.attn_varlen(q, q, q, cu, cu, 6, 6, dropout_p=0.1)
+    with pytest.raises(NotImplementedError):
+        ffpa.attn_varlen(q, q, q, cu, cu, 6, 6, softcap=1.0)
+    with pytest.raises(TypeError):
+        ffpa.attn_varlen(q, q, q, cu.long(), cu, 6, 6)
+    with pytest.raises(TypeError):
+        ffpa.attn_varlen(q.float(), q.float(), q.float(), cu, cu, 6, 6)
+    with pytest.raises(ValueError):  # malformed offsets
+        ffpa.attn_varlen(q, q, q, torch.tensor([0, 7, 4], dtype=torch.int32), None, 7, 7)
+    with pytest.raises(ValueError):  # max_seqlen below a sequence's length
+        ffpa.attn_varlen(q, q, q, cu, None, 5, 5)
+    with pytest.raises(ValueError):  # Hq != Hkv without enable_gqa
+        ffpa.attn_varlen(q, q[:, :1], q[:, :1], cu, cu, 6, 6)
+    with pytest.raises(ValueError):  # not on a GPU
+        ffpa.attn_varlen(q, q, q, cu, None, 6, 6)
