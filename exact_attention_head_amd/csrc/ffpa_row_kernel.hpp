@@ -297,10 +297,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const int total = a.B * a.Hq * nqt;
   int id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  // packed: head-major order, so that each XCD's share holds whole heads over every sequence (the
+  // sequences' lengths differ; the heads' work does not)
   int qt = id % nqt;
   const int bh = id / nqt;
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
+  const int hq = VL ? bh / a.B : bh % a.Hq;
+  const int b = VL ? bh % a.B : bh / a.Hq;
   if (a.causal) qt = nqt - 1 - qt;  // heaviest tiles first
   const int hk = hq / a.group;
   const int r0 = qt * BR;
