@@ -21,7 +21,7 @@ import os
 from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
-           "ffpa_check_cu_seqlens", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
+           "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,13 +32,20 @@ MASK_NONE, MASK_BOOL_U8, MASK_ADD_F32, MASK_ADD_BF16, MASK_ADD_FP16 = 0, 1, 2, 3
 OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
-            "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens")
+            "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
+            "ffpa_fwd_strided", "ffpa_check_strided_args")
 
 
 class MaskDesc(ctypes.Structure):
     """ffpa_mask_t: element (b, h, r, k) at data + b*stride_b + h*stride_h + r*stride_q + k*stride_k."""
     _fields_ = [("data", ctypes.c_void_p), ("kind", ctypes.c_int32), ("stride_b", ctypes.c_int64),
                 ("stride_h", ctypes.c_int64), ("stride_q", ctypes.c_int64), ("stride_k", ctypes.c_int64)]
+
+
+class LayoutDesc(ctypes.Structure):
+    """ffpa_layout_t: element strides {batch, head, row} of Q, K, V and O (head-dim stride 1)."""
+    _fields_ = [("q", ctypes.c_int64 * 3), ("k", ctypes.c_int64 * 3), ("v", ctypes.c_int64 * 3),
+                ("o", ctypes.c_int64 * 3)]
 
 
 _lib = None
@@ -74,6 +81,12 @@ def library() -> ctypes.CDLL:
     lib.ffpa_check_varlen_args.restype = i32
     lib.ffpa_check_cu_seqlens.argtypes = [ctypes.POINTER(ctypes.c_int32), i64, i64, i64]
     lib.ffpa_check_cu_seqlens.restype = i32
+    sargs = [p, p, p, ctypes.POINTER(MaskDesc), p, p, i64, i64, i64, i64, i64, i64, ctypes.POINTER(LayoutDesc), f32,
+             i32, i32]
+    lib.ffpa_fwd_strided.argtypes = sargs + [p]
+    lib.ffpa_fwd_strided.restype = i32
+    lib.ffpa_check_strided_args.argtypes = sargs
+    lib.ffpa_check_strided_args.restype = i32
     _lib = lib
     return lib
 
@@ -100,6 +113,36 @@ def ffpa_check_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, N
     m = ctypes.byref(mask) if mask is not None else None
     return library().ffpa_check_args(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
                                      int(is_causal), dtype)
+
+
+def ffpa_fwd_strided(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, layout: LayoutDesc, scale,
+                     is_causal, dtype, stream) -> int:
+    """The raw strided entry point: pointers are integers (device addresses), returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_fwd_strided(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.byref(layout),
+                                      ctypes.c_float(scale), int(is_causal), dtype, stream)
+
+
+def ffpa_check_strided_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, layout, scale,
+                            is_causal, dtype) -> int:
+    m = ctypes.byref(mask) if mask is not None else None
+    lay = ctypes.byref(layout) if layout is not None else None
+    return library().ffpa_check_strided_args(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, lay, ctypes.c_float(scale),
+                                             int(is_causal), dtype)
+
+
+def _strides3(t):
+    """{batch, head, row} element strides of a [B, H, N, D] tensor usable in place (head-dim stride 1,
+    16-byte aligned, strides multiples of 8, rows not overlapping), else None.  A batch or head
+    dimension of size 1 counts as stride 0 and a single row as stride D."""
+    D = t.shape[3]
+    if t.stride(3) != 1 and D > 1:
+        return None
+    st = [0 if t.shape[0] == 1 else t.stride(0), 0 if t.shape[1] == 1 else t.stride(1),
+          D if t.shape[2] == 1 else t.stride(2)]
+    if t.data_ptr() % 16 or any(x % 8 or x < 0 for x in st) or st[2] < D:
+        return None
+    return st
 
 
 def ffpa_fwd_varlen(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D, scale, is_causal, dtype,
@@ -161,6 +204,8 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     """SDPA-aligned forward.  query [B, Hq, Nq, D]; key/value [B, Hkv, Nkv, D]; bf16 or fp16.
 
     Returns O [B, Hq, Nq, D] (dtype of query), or (O, LSE [B, Hq, Nq] float32) with return_lse.
+    Strided views (for instance a [B, N, H, D] tensor transposed to [B, H, N, D]) are read in place
+    through ffpa_fwd_strided when their strides allow it, and so is a strided ``out``.
     """
     import torch
 
@@ -183,22 +228,41 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
         raise ValueError("query and key disagree on batch or head dim")
     if Hq != Hkv and not enable_gqa:
         raise ValueError("Hq != Hkv needs enable_gqa=True")
-    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+    # strided views (e.g. [B, N, H, D] storage seen as [B, H, N, D]) are read in place when the
+    # kernels can address them; anything else is made contiguous first
+    sq, sk, sv = _strides3(query), _strides3(key), _strides3(value)
+    in_place = sq is not None and sk is not None and sv is not None and sk[2] == sv[2]
+    if in_place:
+        q, k, v = query, key, value
+    else:
+        q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+        sq, sk, sv = _strides3(q), _strides3(k), _strides3(v)
     dtype = FFPA_BF16 if query.dtype == torch.bfloat16 else FFPA_FP16
     if out is None:
         o = torch.empty((B, Hq, Nq, D), dtype=query.dtype, device=query.device)
     else:
-        if tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != query.dtype or not out.is_contiguous():
-            raise ValueError("out must be a contiguous [B, Hq, Nq, D] tensor of the query dtype")
+        if tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != query.dtype or _strides3(out) is None:
+            raise ValueError("out must be a [B, Hq, Nq, D] tensor of the query dtype, unit stride along D, "
+                             "16-byte aligned, other strides multiples of 8")
         o = out
+    so = _strides3(o)
+    contiguous = all(t.is_contiguous() for t in (q, k, v, o))
+    if not contiguous and None in (sq, sk, sv):
+        raise ValueError("query, key and value must be 16-byte aligned")
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=query.device) if return_lse else None
     desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(query.device), B, Hq, Nq, Nkv)
     sc = math.nan if scale is None else float(scale)
     with torch.cuda.device(query.device):
         stream = torch.cuda.current_stream(query.device).cuda_stream
-        st = ffpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(),
-                      lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal),
-                      dtype, stream)
+        lp = lse.data_ptr() if lse is not None else None
+        if contiguous:
+            st = ffpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(), lp, B, Hq, Hkv, Nq, Nkv, D,
+                          sc, bool(is_causal), dtype, stream)
+        else:
+            lay = LayoutDesc((ctypes.c_int64 * 3)(*sq), (ctypes.c_int64 * 3)(*sk), (ctypes.c_int64 * 3)(*sv),
+                             (ctypes.c_int64 * 3)(*so))
+            st = ffpa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(), lp, B, Hq, Hkv, Nq,
+                                  Nkv, D, lay, sc, bool(is_causal), dtype, stream)
     del keep
     if st != OK:
         _raise(st)

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <utility>
 
 #include "../../include/ffpa.h"
 #include "ffpa_kernel.hpp"
@@ -55,9 +56,55 @@ int rows_for(int64_t D) {
   }
 }
 
+// Elements from a tensor's first element to one past its last: (B-1)*sb + (H-1)*sh + (N-1)*sn + D.
+int64_t extent(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t D) {
+  return (B - 1) * st[0] + (H - 1) * st[1] + (N - 1) * st[2] + D;
+}
+
+// True when no two elements of a [B, H, N, D] tensor with strides st (and unit head-dim stride)
+// share an address: the dimensions of size > 1, sorted by stride, each step past the whole span of
+// the smaller ones.
+bool non_overlapping(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t D) {
+  int64_t dims[4][2] = {{1, D}, {st[2], N}, {st[1], H}, {st[0], B}};
+  for (int i = 1; i < 4; ++i)
+    for (int j = i; j > 0 && dims[j][0] < dims[j - 1][0]; --j) {
+      std::swap(dims[j][0], dims[j - 1][0]);
+      std::swap(dims[j][1], dims[j - 1][1]);
+    }
+  int64_t span = 0;  // elements covered by the smaller dimensions, minus one
+  for (int i = 0; i < 4; ++i) {
+    if (dims[i][1] <= 1) continue;
+    if (dims[i][0] <= span) return false;
+    span += (dims[i][1] - 1) * dims[i][0];
+  }
+  return true;
+}
+
+// Layout rules of ffpa_fwd_strided: strides in elements, >= 0, multiples of 8 (16-byte rows for the
+// 128-bit loads), K and V sharing their row stride, O not overlapping itself, and the row spans of
+// one head within the kernels' 32-bit offsets.
+int check_layout(const ffpa_layout_t* lay, int64_t Hq, int64_t Nq, int64_t Nkv, int64_t D, int64_t B) {
+  const int64_t* all[4] = {lay->q, lay->k, lay->v, lay->o};
+  for (int t = 0; t < 4; ++t)
+    for (int i = 0; i < 3; ++i) {
+      if (all[t][i] < 0) return fail(FFPA_ERR_VALUE, "strides must be >= 0");
+      if (all[t][i] % 8 != 0) return fail(FFPA_ERR_VALUE, "strides must be multiples of 8 elements (16 bytes)");
+    }
+  if (lay->k[2] != lay->v[2]) return fail(FFPA_ERR_UNSUPPORTED, "K and V must share their row stride");
+  // rows past a head's last one must fall outside its load range (they read as zero)
+  if (lay->q[2] < D || lay->k[2] < D || lay->o[2] < D)
+    return fail(FFPA_ERR_UNSUPPORTED, "row strides must be at least D (rows may not overlap)");
+  if (lay->q[2] >= (1LL << 30) || lay->k[2] >= (1LL << 30) || lay->o[2] >= (1LL << 30))
+    return fail(FFPA_ERR_UNSUPPORTED, "row strides beyond the 32-bit indexing of the kernels");
+  if ((Nq + 256) * lay->q[2] * 2 >= (1LL << 31) || (Nkv + 256) * lay->k[2] * 2 >= (1LL << 31))
+    return fail(FFPA_ERR_UNSUPPORTED, "one head's Q or K/V rows must span below 2 GiB (buffer addressing)");
+  if (!non_overlapping(lay->o, B, Hq, Nq, D)) return fail(FFPA_ERR_VALUE, "the strides of o make elements overlap");
+  return FFPA_OK;
+}
+
 int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o, const float* lse,
           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
-          int dtype) {
+          int dtype, const ffpa_layout_t* lay = nullptr) {
   g_detail[0] = '\0';
   if (dtype != FFPA_BF16 && dtype != FFPA_FP16) return fail(FFPA_ERR_TYPE, "dtype %d is neither bf16 nor fp16", dtype);
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
@@ -84,14 +131,26 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
     return fail(FFPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit row indexing of the kernels");
   if (Nq * D * 2 >= (1LL << 31) || Nkv * D * 2 >= (1LL << 31))
     return fail(FFPA_ERR_UNSUPPORTED, "one head of Q or K/V must stay below 2 GiB (buffer addressing)");
+  if (lay != nullptr) {
+    const int st = check_layout(lay, Hq, Nq, Nkv, D, B);
+    if (st != FFPA_OK) return st;
+  }
   const size_t esz = 2;
-  const size_t qbytes = (size_t)(B * Hq * Nq * D) * esz, kvbytes = (size_t)(B * Hkv * Nkv * D) * esz;
-  const size_t obytes = qbytes, lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
-  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kvbytes) ||
-      ranges_overlap(o, obytes, v, kvbytes) || ranges_overlap(o, obytes, lse, lbytes))
+  // byte extents of the tensors (for a strided layout: from the first to one past the last element)
+  size_t qbytes = (size_t)(B * Hq * Nq * D) * esz, kbytes = (size_t)(B * Hkv * Nkv * D) * esz;
+  size_t vbytes = kbytes, obytes = qbytes;
+  if (lay != nullptr) {
+    qbytes = (size_t)extent(lay->q, B, Hq, Nq, D) * esz;
+    kbytes = (size_t)extent(lay->k, B, Hkv, Nkv, D) * esz;
+    vbytes = (size_t)extent(lay->v, B, Hkv, Nkv, D) * esz;
+    obytes = (size_t)extent(lay->o, B, Hq, Nq, D) * esz;
+  }
+  const size_t lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
+  if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kbytes) ||
+      ranges_overlap(o, obytes, v, vbytes) || ranges_overlap(o, obytes, lse, lbytes))
     return fail(FFPA_ERR_VALUE, "o must not overlap q, k, v or lse");
-  if (lse != nullptr && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kvbytes) ||
-                         ranges_overlap(lse, lbytes, v, kvbytes)))
+  if (lse != nullptr && (ranges_overlap(lse, lbytes, q, qbytes) || ranges_overlap(lse, lbytes, k, kbytes) ||
+                         ranges_overlap(lse, lbytes, v, vbytes)))
     return fail(FFPA_ERR_VALUE, "lse must not overlap q, k or v");
   if (mask != nullptr) {
     if (mask->kind == FFPA_MASK_NONE) {
@@ -100,7 +159,6 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
       const size_t msz = mask_elem_size(mask->kind);
       if (msz == 0) return fail(FFPA_ERR_TYPE, "unknown mask kind %d", (int)mask->kind);
       if (mask->data == nullptr) return fail(FFPA_ERR_VALUE, "mask data is null");
-      if (is_causal) return fail(FFPA_ERR_VALUE, "an explicit mask cannot be combined with is_causal");
       if (mask->stride_k != 1) return fail(FFPA_ERR_UNSUPPORTED, "mask stride_k must be 1");
       if (mask->stride_b < 0 || mask->stride_h < 0 || mask->stride_q < 0)
         return fail(FFPA_ERR_VALUE, "mask strides must be >= 0");
@@ -182,12 +240,31 @@ int ffpa_check_args(const void* q, const void* k, const void* v, const ffpa_mask
   return check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
 }
 
-int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse, int64_t B,
-             int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype,
-             void* stream) {
-  const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
-  if (st != FFPA_OK) return st;
+static int launch_dense(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+                        int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                        const ffpa_layout_t* lay, float scale, int is_causal, int dtype, void* stream) {
   ffpa::FwdArgs a{};
+  if (lay == nullptr) {  // contiguous [B, H, N, D]
+    a.q_sb = a.o_sb = Hq * Nq * D;
+    a.q_sh = a.o_sh = Nq * D;
+    a.k_sb = a.v_sb = Hkv * Nkv * D;
+    a.k_sh = a.v_sh = Nkv * D;
+    a.q_sr = a.kv_sr = a.o_sr = (int)D;
+    a.strided = 0;
+  } else {
+    a.q_sb = lay->q[0];
+    a.q_sh = lay->q[1];
+    a.q_sr = (int)lay->q[2];
+    a.k_sb = lay->k[0];
+    a.k_sh = lay->k[1];
+    a.v_sb = lay->v[0];
+    a.v_sh = lay->v[1];
+    a.kv_sr = (int)lay->k[2];
+    a.o_sb = lay->o[0];
+    a.o_sh = lay->o[1];
+    a.o_sr = (int)lay->o[2];
+    a.strided = 1;
+  }
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
   a.v = (const uint16_t*)v;
@@ -218,6 +295,30 @@ int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mas
   const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FFPA_OK;
+}
+
+int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse, int64_t B,
+             int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype,
+             void* stream) {
+  const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  return launch_dense(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, nullptr, scale, is_causal, dtype, stream);
+}
+
+int ffpa_check_strided_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                            const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                            const ffpa_layout_t* layout, float scale, int is_causal, int dtype) {
+  if (layout == nullptr) return fail(FFPA_ERR_VALUE, "layout must be non-null");
+  return check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, layout);
+}
+
+int ffpa_fwd_strided(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     const ffpa_layout_t* layout, float scale, int is_causal, int dtype, void* stream) {
+  const int st = ffpa_check_strided_args(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, layout, scale, is_causal,
+                                         dtype);
+  if (st != FFPA_OK) return st;
+  return launch_dense(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, layout, scale, is_causal, dtype, stream);
 }
 
 int ffpa_check_varlen_args(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -256,6 +357,9 @@ int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
   a.cu_k = cu_seqlens_k;
   a.Tq = (int)Tq;
   a.Tk = (int)Tk;
+  a.q_sh = a.k_sh = a.v_sh = a.o_sh = D;  // [T, H, D]: no batch stride
+  a.q_sr = a.o_sr = (int)(Hq * D);
+  a.kv_sr = (int)(Hkv * D);
   const hipStream_t s = (hipStream_t)stream;
   const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

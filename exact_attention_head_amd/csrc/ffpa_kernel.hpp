@@ -94,6 +94,12 @@ struct FwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int Tq, Tk;
+  // Element strides (batch, head, row; the head-dim stride is 1) of Q, of K and V, and of O.  The
+  // contiguous dense variants of the row kernel use their compile-time equivalents instead; a
+  // packed batch has no batch stride (its sequences start at the offsets above).
+  int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
+  int q_sr, kv_sr, o_sr;
+  int strided;  // 1: the dense layout is not contiguous (the runtime-layout variants serve it)
 };
 
 // Tokens of sequence b of a packed batch.  The offsets are clamped to the packed tensors and the
@@ -638,18 +644,21 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   const int hk = hq / a.group;
   const int r0 = qt * BR;              // first query row of the workgroup
   int Nq = a.Nq, Nkv = a.Nkv;
-  int64_t q_base = (int64_t)(b * a.Hq + hq) * Nq * D, kv_base = (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  // element offsets of this item's first Q/K/V/O row, from the strides (a packed sequence adds its
+  // first token's row instead of a batch stride)
+  int64_t q_base = b * a.q_sb + hq * a.q_sh, k_base = b * a.k_sb + hk * a.k_sh;
+  int64_t v_base = b * a.v_sb + hk * a.v_sh, o_base = b * a.o_sb + hq * a.o_sh;
   int64_t lse_base = (int64_t)(b * a.Hq + hq) * Nq;
-  int q_rs = D, kv_rs = D;             // row strides (elements)
+  const int q_rs = a.q_sr, kv_rs = a.kv_sr, o_rs = a.o_sr;  // row strides (elements)
   if (packed) {
     const SeqRange sr = seq_range(a, b);
     Nq = sr.nq;
     Nkv = sr.nkv;
-    q_base = (int64_t)sr.q0 * a.Hq * D + hq * D;
-    kv_base = (int64_t)sr.k0 * a.Hkv * D + hk * D;
+    q_base = (int64_t)sr.q0 * q_rs + hq * a.q_sh;
+    k_base = (int64_t)sr.k0 * kv_rs + hk * a.k_sh;
+    v_base = (int64_t)sr.k0 * kv_rs + hk * a.v_sh;
+    o_base = (int64_t)sr.q0 * o_rs + hq * a.o_sh;
     lse_base = (int64_t)hq * a.Tq + sr.q0;
-    q_rs = a.Hq * D;
-    kv_rs = a.Hkv * D;
     if (r0 >= Nq) return;
   }
   const int rw0 = r0 + rg * R;         // first query row of this wave
@@ -657,8 +666,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   const int off = Nkv - Nq;            // tail alignment of the causal rule
 
   const uint16_t* qg = a.q + q_base;
-  const uint16_t* kg = a.k + kv_base;
-  const uint16_t* vg = a.v + kv_base;
+  const uint16_t* kg = a.k + k_base;
+  const uint16_t* vg = a.v + v_base;
 
   int kv_end = Nkv;
   if (a.causal) {
@@ -975,7 +984,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
     if (row < Nq) {
       const float l = l_run[rb];
       const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* orow = a.o + q_base + (int64_t)row * q_rs + col0;
+      uint16_t* orow = a.o + o_base + (int64_t)row * o_rs + col0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -1035,11 +1044,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     const bool staged_mask = a.mask_kind == kMaskAddF32 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
                              a.msq % 32 == 0 &&
                              ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq * 4 + (int64_t)a.Nkv * 4 < (1LL << 31);
-    // packed batches: the lengths live on the device, so whole and partial tiles are told apart
-    // in the kernel
-    if (packed && plain)
+    // packed batches and strided layouts take the runtime-layout variants (for packed batches the
+    // lengths live on the device, so whole and partial tiles are told apart in the kernel)
+    const bool runtime_layout = packed || a.strided;
+    if (runtime_layout && plain)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    else if (packed)
+    else if (runtime_layout)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
                          a);
     else if (staged_mask)

@@ -238,8 +238,9 @@ constexpr bool row_barrier_within(int first, int last, int EM, int PF) {
   return false;
 }
 
-// VL: a packed variable-length batch (FwdArgs::cu_q): row strides of heads x D elements and
-// per-sequence lengths, offsets and LSE layout; the dense layout keeps them compile-time.
+// VL: runtime layouts: a packed variable-length batch (FwdArgs::cu_q: per-sequence lengths, offsets
+// and LSE layout) or a strided dense one, both with runtime strides; the contiguous dense layout
+// keeps them compile-time.
 template <typename T, int D, int MODE, bool VL>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   using RT = RowTiling<D>;
@@ -301,32 +302,44 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   // sequences' lengths differ; the heads' work does not)
   int qt = id % nqt;
   const int bh = id / nqt;
-  const int hq = VL ? bh / a.B : bh % a.Hq;
-  const int b = VL ? bh % a.B : bh / a.Hq;
+  const bool head_major = VL && a.cu_q != nullptr;
+  const int hq = head_major ? bh / a.B : bh % a.Hq;
+  const int b = head_major ? bh % a.B : bh / a.Hq;
   if (a.causal) qt = nqt - 1 - qt;  // heaviest tiles first
   const int hk = hq / a.group;
   const int r0 = qt * BR;
   int Nq = a.Nq, Nkv = a.Nkv;
-  int64_t q_base = (int64_t)(b * a.Hq + hq) * Nq * D, kv_base = (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  const int q_rs = VL ? a.q_sr : D;    // row strides (elements)
+  const int kv_rs = VL ? a.kv_sr : D;
+  const int o_rs = VL ? a.o_sr : D;
+  int64_t q_base = (int64_t)(b * a.Hq + hq) * Nq * D, k_base = (int64_t)(b * a.Hkv + hk) * Nkv * D;
+  int64_t v_base = k_base, o_base = q_base;
   int64_t lse_base = (int64_t)(b * a.Hq + hq) * Nq;
   if constexpr (VL) {
-    const SeqRange sr = seq_range(a, b);
-    Nq = sr.nq;
-    Nkv = sr.nkv;
-    q_base = (int64_t)sr.q0 * a.Hq * D + hq * D;
-    kv_base = (int64_t)sr.k0 * a.Hkv * D + hk * D;
-    lse_base = (int64_t)hq * a.Tq + sr.q0;
-    if (r0 >= Nq) return;
+    if (a.cu_q != nullptr) {
+      const SeqRange sr = seq_range(a, b);
+      Nq = sr.nq;
+      Nkv = sr.nkv;
+      q_base = (int64_t)sr.q0 * q_rs + hq * a.q_sh;
+      k_base = (int64_t)sr.k0 * kv_rs + hk * a.k_sh;
+      v_base = (int64_t)sr.k0 * kv_rs + hk * a.v_sh;
+      o_base = (int64_t)sr.q0 * o_rs + hq * a.o_sh;
+      lse_base = (int64_t)hq * a.Tq + sr.q0;
+      if (r0 >= Nq) return;
+    } else {
+      q_base = b * a.q_sb + hq * a.q_sh;
+      k_base = b * a.k_sb + hk * a.k_sh;
+      v_base = b * a.v_sb + hk * a.v_sh;
+      o_base = b * a.o_sb + hq * a.o_sh;
+    }
   }
-  const int q_rs = VL ? a.Hq * D : D;    // row strides (elements)
-  const int kv_rs = VL ? a.Hkv * D : D;
   const int rw0 = r0 + rg * 32;  // first row of this wave
   const int row = rw0 + l32;     // this lane's row
   const int col0 = dg * DW;
   const int off = Nkv - Nq;
   const uint16_t* qg = a.q + q_base;
-  const uint16_t* kg = a.k + kv_base;
-  const uint16_t* vg = a.v + kv_base;
+  const uint16_t* kg = a.k + k_base;
+  const uint16_t* vg = a.v + v_base;
   int kv_end = Nkv;
   if (a.causal) {
     const int lim = r0 + BR + off;
@@ -755,7 +768,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const float l = sum_halves(l_lane);
   if (row < Nq) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* orow = a.o + q_base + (int64_t)row * q_rs + col0;
+    uint16_t* orow = a.o + o_base + (int64_t)row * o_rs + col0;
     static_for<NSUB>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
 #pragma unroll

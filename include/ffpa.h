@@ -71,7 +71,8 @@ enum {
  *   q    device, [B, Hq, Nq, D], contiguous row-major, dtype elements
  *   k, v device, [B, Hkv, Nkv, D], contiguous row-major, dtype elements
  *   mask NULL for none, else a host pointer to a descriptor of a device mask
- *        (read during this call only); cannot be combined with is_causal
+ *        (read during this call only); with is_causal, a key takes part only
+ *        where both the mask and the causal rule admit it
  *   o    device, [B, Hq, Nq, D], contiguous, dtype elements; written
  *   lse  device, [B, Hq, Nq] float32, natural log; written; NULL skips it
  *   B, Hq, Hkv, Nq, Nkv >= 1; Hq % Hkv == 0; 64 <= D <= 1024 with D % 64 == 0
@@ -89,6 +90,42 @@ enum {
 int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
              int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
              int is_causal, int dtype, void* stream);
+
+/* Element strides of the tensors of ffpa_fwd_strided: {batch, head, row} for
+ * each of Q, K, V and O (the head-dim stride is 1).  Element (b, h, n, d) of
+ * Q is at q + b*q[0] + h*q[1] + n*q[2] + d, and likewise for the others. */
+typedef struct {
+  int64_t q[3], k[3], v[3], o[3];
+} ffpa_layout_t;
+
+/*
+ * ffpa_fwd_strided -- ffpa_fwd over tensors laid out by `layout` (a host
+ * pointer, read during this call only) instead of contiguously: views such
+ * as a [B, N, H, D] tensor seen as [B, H, N, D], or heads sliced out of a
+ * fused projection, are read and written in place (the "zero-copy" layouts
+ * of the ffpa-attn pages).  The operation, the other arguments and the
+ * errors are those of ffpa_fwd, plus:
+ *   - every stride is >= 0 and a multiple of 8 elements (16-byte rows), and
+ *     every row stride is at least D (FFPA_ERR_UNSUPPORTED otherwise; a
+ *     dimension of size 1 may take any such stride);
+ *   - K and V share their row stride (their batch and head strides may
+ *     differ);
+ *   - the strides of O give every element its own address;
+ *   - (Nq + 256) x the Q row stride and (Nkv + 256) x the K/V row stride,
+ *     in bytes, stay below 2 GiB (FFPA_ERR_UNSUPPORTED otherwise).
+ * LSE stays contiguous [B, Hq, Nq].  O must not overlap q, k, v, mask or lse
+ * (checked on the address ranges from each tensor's first to its last
+ * element).
+ */
+int ffpa_fwd_strided(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     const ffpa_layout_t* layout, float scale, int is_causal, int dtype, void* stream);
+
+/* The host-side argument check ffpa_fwd_strided performs, without enqueuing
+ * anything. */
+int ffpa_check_strided_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                            const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                            const ffpa_layout_t* layout, float scale, int is_causal, int dtype);
 
 /* The host-side argument check ffpa_fwd performs, without enqueuing anything
  * and without touching the memory the pointers refer to. */

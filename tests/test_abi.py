@@ -1,5 +1,6 @@
 """The C-ABI boundary on the host: the library loads, exports what include/ffpa.h declares, and
 checks arguments before any HIP call (these tests never touch a GPU)."""
+import ctypes
 import math
 import os
 import re
@@ -91,7 +92,8 @@ def test_mask_descriptor_rules():
     assert check(mask=mdesc(kind=ffpa.MASK_NONE, data=0)) == ffpa.OK
     assert check(mask=mdesc(kind=7)) == ffpa.ERR_TYPE
     assert check(mask=mdesc(data=0)) == ffpa.ERR_VALUE
-    assert check(mask=mdesc(), causal=True) == ffpa.ERR_VALUE
+    assert check(mask=mdesc(), causal=True) == ffpa.OK  # both apply
+    assert check(mask=mdesc(), causal=True, Nq=131, Nkv=130) == ffpa.ERR_VALUE
     assert check(mask=mdesc(sk=2)) == ffpa.ERR_UNSUPPORTED
     assert check(mask=mdesc(sk=0)) == ffpa.ERR_UNSUPPORTED
     assert check(mask=mdesc(sq=-130)) == ffpa.ERR_VALUE
@@ -212,3 +214,48 @@ def test_varlen_python_layer_rejects_before_the_library():
         ffpa.attn_varlen(q, q[:, :1], q[:, :1], cu, cu, 6, 6)
     with pytest.raises(ValueError):  # not on a GPU
         ffpa.attn_varlen(q, q, q, cu, None, 6, 6)
+
+
+# ---- strided layouts (ffpa_fwd_strided)
+def layout(q=None, k=None, v=None, o=None, B=1, Hq=2, Hkv=1, Nq=100, Nkv=130, D=512):
+    """Default: [B, N, H, D] storage (NHD) seen as [B, H, N, D]."""
+    nhd = lambda H, N: [N * H * D, D, H * D]
+    return ffpa.LayoutDesc((ctypes.c_int64 * 3)(*(q or nhd(Hq, Nq))), (ctypes.c_int64 * 3)(*(k or nhd(Hkv, Nkv))),
+                           (ctypes.c_int64 * 3)(*(v or nhd(Hkv, Nkv))), (ctypes.c_int64 * 3)(*(o or nhd(Hq, Nq))))
+
+
+def scheck(lay, B=1, Hq=2, Hkv=1, Nq=100, Nkv=130, D=512, causal=False, q=Q, k=K, v=V, o=O, lse=L):
+    return ffpa.ffpa_check_strided_args(q, k, v, None, o, lse, B, Hq, Hkv, Nq, Nkv, D, lay, math.nan, causal,
+                                        ffpa.FFPA_BF16)
+
+
+def test_strided_layouts_pass():
+    assert scheck(layout()) == ffpa.OK and detail() == ""
+    assert scheck(layout(B=2), B=2) == ffpa.OK
+    # K and V broadcast over the batch, heads sliced out of a fused [N, 3, H, D] projection
+    assert scheck(layout(k=[0, 512, 3 * 512], v=[0, 512, 3 * 512]), B=3) == ffpa.OK
+    assert scheck(layout(o=[2 * 100 * 512, 100 * 512, 512])) == ffpa.OK  # contiguous O
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=[1024 * 100, 512, 1020]), ffpa.ERR_VALUE),        # row stride not a multiple of 8
+    (dict(k=[0, 512, -512]), ffpa.ERR_VALUE),                 # negative stride
+    (dict(k=[0, 512, 1024], v=[0, 512, 2048]), ffpa.ERR_UNSUPPORTED),  # K and V row strides differ
+    (dict(o=[0, 256, 1024]), ffpa.ERR_VALUE),                 # O rows of both heads overlap
+    (dict(o=[0, 512, 512]), ffpa.ERR_VALUE),                  # row 1 of head 0 is row 0 of head 1
+    (dict(k=[0, 0, 1 << 24], v=[0, 0, 1 << 24]), ffpa.ERR_UNSUPPORTED),  # K rows span beyond 2 GiB
+    (dict(k=[0, 512, 0], v=[0, 512, 0]), ffpa.ERR_UNSUPPORTED),          # K/V expanded along N
+    (dict(q=[0, 0, 256]), ffpa.ERR_UNSUPPORTED),                         # overlapping Q rows
+])
+def test_strided_layout_errors(kw, status):
+    assert scheck(layout(**kw)) == status, kw
+    assert detail() != ""
+
+
+def test_strided_layout_overlap_uses_extents():
+    # O placed right after Q's last element is fine; one element earlier it overlaps
+    ext = ((1 - 1) * 100 * 2 * 512 + (2 - 1) * 512 + (100 - 1) * 2 * 512 + 512) * 2
+    assert scheck(layout(), o=Q + ext) == ffpa.OK
+    assert scheck(layout(), o=Q + ext - 16) == ffpa.ERR_VALUE
+    assert ffpa.ffpa_check_strided_args(Q, K, V, None, O, L, 1, 2, 1, 100, 130, 512, None, math.nan, False,
+                                        ffpa.FFPA_BF16) == ffpa.ERR_VALUE  # no layout

@@ -161,6 +161,26 @@ def pin_mask_algebra(fault=0):
     return ok
 
 
+def pin_mask_with_causal(fault=0):
+    """A mask together with the causal rule equals that mask combined by hand with the tail-aligned
+    causal mask (bool: AND; additive: -inf where the causal rule excludes), Nq < Nkv."""
+    B, H, Nq, Nkv, D = 2, 2, 4, 7, 8
+    q, k, v = random_qkv(B, H, H, Nq, Nkv, D, seed=71)
+    g = torch.Generator().manual_seed(72)
+    vis = torch.arange(Nkv).view(1, Nkv) <= torch.arange(Nq).view(Nq, 1) + (Nkv - Nq)
+    keep = torch.rand(B, 1, Nq, Nkv, generator=g) < 0.7
+    keep[..., 0] = True
+    bias = torch.randn(B, 1, Nq, Nkv, generator=g)
+    ok = True
+    O1, L1 = _full(q, k, v, fault=fault, mask=keep, is_causal=True)
+    O2, L2 = _full(q, k, v, fault=fault, mask=keep & vis)
+    ok &= bool(np.array_equal(O1, O2)) and bool(np.array_equal(L1, L2))
+    O1, L1 = _full(q, k, v, fault=fault, mask=bias, is_causal=True)
+    O2, L2 = _full(q, k, v, fault=fault, mask=bias.masked_fill(~vis, float("-inf")))
+    ok &= bool(np.array_equal(O1, O2)) and bool(np.array_equal(L1, L2))
+    return ok
+
+
 def pin_one_and_two_keys(fault=0):
     """Nkv = 1: O = v_0, LSE = s_0.  Nkv = 2: O = sigmoid(s0-s1) v0 + sigmoid(s1-s0) v1 and
     LSE = s0 + log(1 + exp(s1 - s0))."""
@@ -272,8 +292,8 @@ def pin_brute_force(fault=0):
 
 
 PINS = [pin_probs_sum_to_one, pin_identical_v_rows, pin_zero_query_uniform, pin_weighted_by_mask,
-        pin_causal_locality, pin_gqa_is_repeat, pin_scale, pin_mask_algebra, pin_one_and_two_keys, pin_torch_sdpa,
-        pin_brute_force]
+        pin_causal_locality, pin_gqa_is_repeat, pin_scale, pin_mask_algebra, pin_mask_with_causal,
+        pin_one_and_two_keys, pin_torch_sdpa, pin_brute_force]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])

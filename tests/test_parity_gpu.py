@@ -108,6 +108,23 @@ def test_fp32_mask_staged_shapes(shape, D):
     _log(f"staged mask shape {shape} D={D}", compare(o, l, q, k, v, mask=mask))
 
 
+@pytest.mark.parametrize("kind", ["bool", "f32"])
+@pytest.mark.parametrize("D", [64, 256, 512, 1024])
+@pytest.mark.parametrize("Nq,Nkv", [(130, 200), (64, 64), (100, 333)])
+def test_mask_and_causal(kind, D, Nq, Nkv):
+    """A mask together with the tail-aligned causal rule: a key takes part only where both admit it."""
+    B, H = 2, 2
+    q, k, v = _case(B, H, H, Nq, Nkv, D, seed=D + Nq + (kind == "bool"))
+    bias = _bias((B, 1, Nq, Nkv), seed=D * 5 + Nkv)
+    if kind == "bool":
+        mask = bias > -0.5
+        mask[..., 0] = True
+    else:
+        mask = bias
+    o, l = run_gpu(q, k, v, mask=mask, is_causal=True)
+    _log(f"mask {kind} + causal D={D} Nq={Nq} Nkv={Nkv}", compare(o, l, q, k, v, mask=mask, is_causal=True))
+
+
 def test_fully_masked_rows():
     """Rows with every key excluded: O = 0 and LSE = -inf (the convention of the oracle)."""
     q, k, v = _case(1, 2, 2, 70, 90, 512, seed=8)
