@@ -206,6 +206,23 @@ def test_deterministic_and_in_bounds():
     assert (lbig[:pad] == 12345.0).all() and (lbig[pad + B * Hq * Nq:] == 12345.0).all(), "LSE guard band written"
 
 
+def test_largest_head_at_the_offset_limit():
+    """One K/V head just under the 2 GiB the kernels' 32-bit buffer offsets allow (D = 1024,
+    1,048,448 keys, K and V 2 GiB each), with a ragged query count: every key's offset is formed and
+    range-checked near the top of the range, and the rows are compared with the oracle."""
+    import exact_attention_head_amd as ffpa
+
+    D, Nq, Nkv = 1024, 65, (1 << 20) - 128
+    assert Nkv * D * 2 < (1 << 31) and (Nkv + 128) * D * 2 >= (1 << 31)
+    q, k, v = _case(1, 1, 1, Nq, Nkv, D, seed=77)
+    fake = [(i + 1) << 36 for i in range(4)]  # aligned stand-ins: the check never dereferences them
+    assert ffpa.ffpa_check_args(fake[0], fake[1], fake[2], None, fake[3], None, 1, 1, 1, Nq, Nkv + 128, D,
+                                float("nan"), False, ffpa.FFPA_BF16) == ffpa.ERR_UNSUPPORTED
+    o, l = run_gpu(q, k, v)
+    _log(f"offset limit Nkv={Nkv} D={D}", compare(o, l, q, k, v))
+    del q, k, v
+
+
 # ---- the five full-size workloads, in the benchmark's launch configuration, on sampled rows
 @pytest.mark.parametrize("name", ["tiny", "large_d_self", "gqa_causal", "cross_mask"])
 def test_full_size_workloads(name):
