@@ -242,3 +242,64 @@ def attention_varlen(q, k, v, cu_q: Sequence[int], cu_k: Optional[Sequence[int]]
     if fault == VL_FAULT_LSE_TOKEN_MAJOR:
         L = np.ascontiguousarray(L.T).reshape(Hq, want.size)
     return O, L
+
+
+# Planted-mistake switches of the backward (tests of the pins only).
+BWD_FAULT_NONE = 0
+BWD_FAULT_NO_DELTA = 1        # dS = P * dP, the row term dropped
+BWD_FAULT_DK_UNSCALED = 2     # dK without the scale factor
+BWD_FAULT_GQA_LAST_HEAD = 3   # a KV head's gradient from the last head of its group only
+
+
+def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is_causal: bool = False,
+                       fault: int = BWD_FAULT_NONE):
+    """Gradients of the attention output with respect to Q, K and V in fp64 (the mask is a constant).
+
+    q [B, Hq, Nq, D]; k, v [B, Hkv, Nkv, D]; do (the output's gradient) like q; torch bf16/fp16 or
+    float tensors, widened exactly.  With logits s = scale q.k + bias (-inf where excluded),
+    P = softmax over the keys and dP = dO V^T per head:
+
+        dV = sum over the group's heads of P^T dO
+        dS = P * (dP - rowsum(P * dP))          (the softmax's Jacobian applied to dP)
+        dQ = scale dS K,   dK = scale * sum over the group's heads of dS^T Q
+
+    A row with every key excluded contributes nothing.  Returns (dQ, dK, dV) as float64 arrays.
+    """
+    import torch
+
+    B, Hq, Nq, D = (int(x) for x in q.shape)
+    Hkv, Nkv = int(k.shape[1]), int(k.shape[2])
+    G = Hq // Hkv
+    if scale is None or (isinstance(scale, float) and math.isnan(scale)):
+        scale = 1.0 / math.sqrt(D)
+    Q, K, V, dO = (t.detach().cpu().double().numpy() for t in (q, k, v, do))
+    bias = np.zeros((B, Hq, Nq, Nkv))
+    if mask is not None:
+        m = mask.detach().cpu()
+        if m.dtype == torch.bool:
+            m = torch.where(m, torch.zeros((), dtype=torch.float64), torch.full((), -math.inf, dtype=torch.float64))
+        bias = bias + m.double().numpy()  # broadcasts to [B, Hq, Nq, Nkv]
+    if is_causal:
+        keep = np.arange(Nkv)[None, :] <= np.arange(Nq)[:, None] + (Nkv - Nq)
+        bias = np.where(keep, bias, -np.inf)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // G
+            if fault == BWD_FAULT_GQA_LAST_HEAD and h % G != G - 1:
+                continue
+            s = scale * (Q[b, h] @ K[b, hk].T) + bias[b, h]
+            mx = s.max(axis=1, keepdims=True)
+            live = np.isfinite(mx[:, 0])
+            mx[~live] = 0.0
+            e = np.exp(s - mx)
+            P = e / np.where(live, e.sum(axis=1), 1.0)[:, None]
+            P[~live] = 0.0
+            dP = dO[b, h] @ V[b, hk].T
+            dS = P * dP if fault == BWD_FAULT_NO_DELTA else P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dQ[b, h] = scale * (dS @ K[b, hk])
+            dK[b, hk] += (1.0 if fault == BWD_FAULT_DK_UNSCALED else scale) * (dS.T @ Q[b, h])
+            dV[b, hk] += P.T @ dO[b, h]
+    return dQ, dK, dV
