@@ -21,7 +21,8 @@ import os
 from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
-           "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
+           "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
+           "ffpa_bwd_workspace_size", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +34,7 @@ OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
-            "ffpa_fwd_strided", "ffpa_check_strided_args")
+            "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size")
 
 
 class MaskDesc(ctypes.Structure):
@@ -87,6 +88,11 @@ def library() -> ctypes.CDLL:
     lib.ffpa_fwd_strided.restype = i32
     lib.ffpa_check_strided_args.argtypes = sargs
     lib.ffpa_check_strided_args.restype = i32
+    lib.ffpa_bwd.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, i64, i64, i64, i64, i64, i64, f32,
+                             i32, i32, p, ctypes.c_size_t, p]
+    lib.ffpa_bwd.restype = i32
+    lib.ffpa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.ffpa_bwd_workspace_size.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -343,3 +349,91 @@ def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seql
     if st != OK:
         _raise(st)
     return (o, lse) if return_lse else o
+
+
+def ffpa_bwd(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal,
+             dtype, workspace, workspace_bytes, stream) -> int:
+    """The raw backward entry point: pointers are integers (device addresses), returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_bwd(q, k, v, o, dout, lse, m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
+                              int(is_causal), dtype, workspace, workspace_bytes, stream)
+
+
+def ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D) -> int:
+    return int(library().ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D))
+
+
+def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_causal: bool = False,
+                  scale: Optional[float] = None):
+    """Gradients (dQ, dK, dV) of ``attn`` at (query, key, value), given its output ``out``, its LSE and
+    the output's gradient.  Tensors [B, H, N, D] as for ``attn``; the mask gets no gradient."""
+    import torch
+
+    q, k, v, o, do = (t.contiguous() for t in (query, key, value, out, grad_out))
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    if tuple(o.shape) != tuple(q.shape) or tuple(do.shape) != tuple(q.shape):
+        raise ValueError("out and grad_out must have the query's shape")
+    if do.dtype != q.dtype or o.dtype != q.dtype:
+        raise TypeError("out and grad_out must have the query's dtype")
+    lse = lse.contiguous()
+    if tuple(lse.shape) != (B, Hq, Nq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be the forward's float32 [B, Hq, Nq] LSE")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(q.device), B, Hq, Nq, Nkv)
+    dtype = FFPA_BF16 if q.dtype == torch.bfloat16 else FFPA_FP16
+    sc = math.nan if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        st = ffpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), desc,
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal), dtype,
+                      ws.data_ptr(), nbytes, stream)
+    del keep
+    if st != OK:
+        _raise(st)
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class AttnFunction(torch.autograd.Function):
+        """Forward through ffpa_fwd (keeping O and the LSE), backward through ffpa_bwd."""
+
+        @staticmethod
+        def forward(ctx, query, key, value, attn_mask, is_causal, scale, enable_gqa):
+            o, lse = attn(query, key, value, attn_mask=attn_mask, is_causal=is_causal, scale=scale,
+                          enable_gqa=enable_gqa, return_lse=True)
+            ctx.save_for_backward(query, key, value, o, lse)
+            ctx.attn_mask, ctx.is_causal, ctx.scale = attn_mask, is_causal, scale
+            ctx.mark_non_differentiable(lse)
+            return o, lse
+
+        @staticmethod
+        def backward(ctx, grad_o, grad_lse):
+            query, key, value, o, lse = ctx.saved_tensors
+            dq, dk, dv = attn_backward(query, key, value, o, grad_o, lse, attn_mask=ctx.attn_mask,
+                                       is_causal=ctx.is_causal, scale=ctx.scale)
+            return dq, dk, dv, None, None, None, None
+
+    return AttnFunction
+
+
+class _Lazy:
+    fn = None
+
+
+def AttnFunction():
+    """The torch.autograd.Function class (created on first use, so importing needs no torch)."""
+    if _Lazy.fn is None:
+        _Lazy.fn = _autograd_function()
+    return _Lazy.fn
+
+
+def attn_with_grad(query, key, value, attn_mask=None, is_causal: bool = False, scale: Optional[float] = None,
+                   enable_gqa: bool = False):
+    """``attn`` recorded for autograd: O is differentiable in query, key and value."""
+    o, _ = AttnFunction().apply(query, key, value, attn_mask, is_causal, scale, enable_gqa)
+    return o

@@ -66,7 +66,8 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     t0 = time.time()
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or max(1, min(16, os.cpu_count() or 4))
-    tasks = [(os.path.join(CSRC, "ffpa_api.hip"), os.path.join(BUILD, "ffpa_api.o"), [])]
+    tasks = [(os.path.join(CSRC, "ffpa_api.hip"), os.path.join(BUILD, "ffpa_api.o"), []),
+             (os.path.join(CSRC, "ffpa_bwd.hip"), os.path.join(BUILD, "ffpa_bwd.o"), [])]
     for tag in ("Bf16", "Fp16"):
         for d in head_dims():
             tasks.append((os.path.join(CSRC, "ffpa_inst.hip"), os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}.o"),
@@ -95,7 +96,10 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     if hazards:
         raise RuntimeError("MFMA / LDS hazards in the generated code:\n" + "\n".join(hazards[:20]))
     tmp = LIB + ".tmp"
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+    # the backward's matrix products use the ROCm GEMM library
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, f"-L{rocm_lib}",
+                        "-lrocblas", f"-Wl,-rpath,{rocm_lib}"],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")

@@ -232,6 +232,11 @@ hipError_t dispatch(int64_t D, const ffpa::FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+namespace ffpa {
+int report_failure(int status, const char* msg) { return fail(status, "%s", msg); }
+void clear_failure() { g_detail[0] = '\0'; }
+}  // namespace ffpa
+
 extern "C" {
 
 int ffpa_check_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,

@@ -25,6 +25,7 @@
 #ifndef FFPA_H_
 #define FFPA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -126,6 +127,43 @@ int ffpa_fwd_strided(const void* q, const void* k, const void* v, const ffpa_mas
 int ffpa_check_strided_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
                             const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
                             const ffpa_layout_t* layout, float scale, int is_causal, int dtype);
+
+/*
+ * ffpa_bwd -- enqueue the backward of ffpa_fwd on `stream`: the gradients of
+ * O with respect to Q, K and V, given dout = dL/dO (the ffpa-attn "API
+ * Reference" page supports the backward of ffpa_attn_func; the mask is a
+ * constant and gets no gradient).  With P the softmax of the forward's
+ * logits and Delta[r] = <dout[r], o[r]>:
+ *   dV = sum over a KV head's group of P^T dout
+ *   dS = P * (dout V^T - Delta),  dQ = scale dS K,
+ *   dK = scale * sum over the group of dS^T Q.
+ *
+ *   q, k, v, mask, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype: as given
+ *        to ffpa_fwd (same layouts and rules)
+ *   o    device, [B, Hq, Nq, D]: the forward's output
+ *   dout device, [B, Hq, Nq, D]: the gradient of the output
+ *   lse  device, [B, Hq, Nq] float32: the forward's LSE (required)
+ *   dq   device, [B, Hq, Nq, D]; dk, dv device, [B, Hkv, Nkv, D]; written,
+ *        in the input dtype
+ *   workspace  device, 256-byte aligned, at least ffpa_bwd_workspace_size()
+ *        bytes, owned by the caller; its contents are scratch
+ *
+ * The products run as library GEMMs (bf16/fp16 in, fp32 accumulate) on the
+ * score matrix of one KV group at a time, held in the workspace; the softmax
+ * recompute, the Delta term and the group sums run in this library's kernels.
+ * On the first call on a device the GEMM library creates a handle (and its own
+ * device workspace), kept until the process ends; calls are serialised on it.
+ * Errors as for ffpa_fwd; FFPA_ERR_VALUE also for a missing or short workspace.
+ */
+int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+             int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Bytes of workspace ffpa_bwd needs for these sizes: about 10 * (Hq/Hkv) *
+ * Nq * Nkv + 4 * B * Hq * Nq + 8 * (Hq/Hkv) * Nkv * D.  0 for invalid sizes.
+ * Host-only. */
+size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D);
 
 /* The host-side argument check ffpa_fwd performs, without enqueuing anything
  * and without touching the memory the pointers refer to. */

@@ -1,0 +1,100 @@
+"""Parity of the backward (ffpa_bwd, through the C ABI) with the fp64 oracle's gradients, on the GPU.
+
+The forward runs first (its O and LSE feed the backward, as in training); the gradients are compared
+element by element with the oracle's exact gradients of the same inputs.  The bar, derived from the
+arithmetic: P and dS are rounded once to 16 bits for the products (2^-9 relative in bf16) and the
+outputs once more, so each gradient is expected near 3-4e-3 relative L2; the test allows rel-L2
+<= 1e-2 and a largest element error <= 2e-2 of the largest reference magnitude.
+"""
+import json
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_head_amd as ffpa
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+
+
+def _grads_gpu(q, k, v, do, mask=None, is_causal=False, scale=None):
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    md = mask.to(DEV) if mask is not None else None
+    o, lse = ffpa.attn(qd, kd, vd, attn_mask=md, is_causal=is_causal, scale=scale,
+                       enable_gqa=q.shape[1] != k.shape[1], return_lse=True)
+    dq, dk, dv = ffpa.attn_backward(qd, kd, vd, o, dod, lse, attn_mask=md, is_causal=is_causal, scale=scale)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def _compare(got, q, k, v, do, **kw):
+    want = oracle.attention_backward(q, k, v, do, **kw)
+    m = {}
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        g = g.double().numpy()
+        assert np.isfinite(g).all(), f"non-finite values in {name}"
+        rel = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+        mx = float(np.abs(g - w).max() / max(np.abs(w).max(), 1e-30))
+        m[name] = dict(rel_l2=round(rel, 6), max_rel=round(mx, 6))
+        assert rel <= REL_L2 and mx <= MAX_REL, (name, m)
+    return m
+
+
+def _case(B, Hq, Hkv, Nq, Nkv, D, dtype=torch.bfloat16, seed=0):
+    q, k, v = W.random_qkv(B, Hq, Hkv, Nq, Nkv, D, dtype=dtype, seed=seed)
+    do = torch.randn(B, Hq, Nq, D, generator=torch.Generator().manual_seed(seed + 1)).to(dtype)
+    return q, k, v, do
+
+
+def _log(name, m):
+    print(f"[bwd] {name}: {json.dumps(m)}", flush=True)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256, 320, 512, 640, 1024])
+def test_backward_head_dims(D):
+    q, k, v, do = _case(1, 2, 2, 130, 200, D, seed=D)
+    _log(f"D={D}", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
+
+
+@pytest.mark.parametrize("Nq,Nkv", [(64, 64), (100, 333), (257, 260)])
+@pytest.mark.parametrize("D", [128, 512])
+def test_backward_causal_gqa(Nq, Nkv, D):
+    q, k, v, do = _case(2, 4, 2, Nq, Nkv, D, seed=Nq + D)
+    _log(f"causal GQA Nq={Nq} Nkv={Nkv} D={D}",
+         _compare(_grads_gpu(q, k, v, do, is_causal=True), q, k, v, do, is_causal=True))
+
+
+@pytest.mark.parametrize("kind", ["bool", "f32"])
+def test_backward_masks(kind):
+    q, k, v, do = _case(2, 3, 1, 90, 150, 256, seed=7)
+    g = torch.Generator().manual_seed(8)
+    bias = torch.randn(2, 1, 90, 150, generator=g)
+    bias[torch.rand(2, 1, 90, 150, generator=g) < 0.1] = float("-inf")
+    bias[..., 0] = 0.0
+    mask = bias > -0.5 if kind == "bool" else bias
+    if kind == "bool":
+        mask[..., 0] = True
+    _log(f"mask {kind}", _compare(_grads_gpu(q, k, v, do, mask=mask), q, k, v, do, mask=mask))
+
+
+def test_backward_fp16_and_scale():
+    q, k, v, do = _case(1, 2, 1, 70, 90, 512, dtype=torch.float16, seed=9)
+    _log("fp16 scale 0.05", _compare(_grads_gpu(q, k, v, do, scale=0.05), q, k, v, do, scale=0.05))
+
+
+def test_autograd_function_matches():
+    """attn_with_grad + torch autograd gives the gradients of attn_backward."""
+    q, k, v, do = _case(1, 4, 2, 100, 120, 512, seed=11)
+    qd, kd, vd = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    o = ffpa.attn_with_grad(qd, kd, vd, is_causal=True, enable_gqa=True)
+    o.backward(do.to(DEV))
+    got = (qd.grad.cpu(), kd.grad.cpu(), vd.grad.cpu())
+    want = _grads_gpu(q, k, v, do, is_causal=True)
+    for g, w in zip(got, want):
+        assert torch.equal(g, w)
+    _log("autograd", _compare(got, q, k, v, do, is_causal=True))
