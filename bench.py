@@ -98,6 +98,49 @@ def time_varlen(w, steps: int, warmup: int):
     return e0.elapsed_time(e1) / steps
 
 
+def time_backward(w, steps: int, warmup: int):
+    """Times ffpa_bwd (dQ, dK, dV) of a dense workload after one forward for its O and LSE; returns ms
+    per backward launch sequence (the whole ffpa_bwd call)."""
+    import torch
+
+    import exact_attention_head_amd as ffpa
+    import workloads as W
+
+    q, k, v, mask = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    md = mask.to(dev) if mask is not None else None
+    gqa = w.Hq != w.Hkv
+    o, lse = ffpa.attn(qd, kd, vd, attn_mask=md, is_causal=w.causal, enable_gqa=gqa, return_lse=True)
+    do = torch.randn(qd.shape, generator=torch.Generator(device=dev).manual_seed(w.seed + 5), device=dev,
+                     dtype=torch.float32).to(w.dtype)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    nbytes = ffpa.ffpa_bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    desc, keep = (None, None) if md is None else ffpa._mask_desc(md, w.B, w.Hq, w.Nq, w.Nkv)
+    dtype = ffpa.FFPA_BF16 if w.dtype == torch.bfloat16 else ffpa.FFPA_FP16
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = ffpa.ffpa_bwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                           desc, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                           float("nan"), w.causal, dtype, ws.data_ptr(), nbytes, stream.cuda_stream)
+        if st != ffpa.OK:
+            raise RuntimeError(f"ffpa_bwd returned {st}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del keep
+    return e0.elapsed_time(e1) / steps
+
+
 def cpu_baseline(w, inputs, outputs, seconds: float):
     """Times the fp64 oracle on a bounded sample of rows of the same workload (all host threads it
     uses), scales to TFLOPS by the metric's FLOP count, and compares those rows with the GPU output."""
@@ -251,18 +294,26 @@ def main() -> int:
     if args.sweep:
         names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
     else:
-        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal"]
+        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "bwd:large_d_self",
+                 "bwd:sweep:1024"]
     if not args.no_secondary and args.workload == "large_d_self":
         for name in names:
-            w2 = pick(name)
-            if isinstance(w2, W.VarlenWorkload):
-                ms2 = time_varlen(w2, max(5, args.steps // 5), 2)
+            backward = name.startswith("bwd:")
+            w2 = pick(name[4:] if backward else name)
+            if backward:
+                # the backward's five products: 10*B*Hq*Nq*Nkv*D FLOPs (2.5x the forward), halved for causal
+                ms2 = time_backward(w2, max(3, args.steps // 10), 1)
+                flops2 = 2.5 * w2.flops
+            elif isinstance(w2, W.VarlenWorkload):
+                ms2, flops2 = time_varlen(w2, max(5, args.steps // 5), 2), w2.flops
             else:
-                ms2, _, _ = time_workload(w2, max(5, args.steps // 5), 2)
-            tf2 = w2.flops / (ms2 * 1e-3) / 1e12
-            log(f"{w2.name}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
-            secondary.append(dict(workload=w2.name, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
-                                  kernel=ffpa.kernel_name(w2.D), ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
+                (ms2, _, _), flops2 = time_workload(w2, max(5, args.steps // 5), 2), w2.flops
+            tf2 = flops2 / (ms2 * 1e-3) / 1e12
+            tag = ("backward " if backward else "") + w2.name
+            log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
+            secondary.append(dict(workload=tag, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
+                                  kernel="ffpa_bwd (library GEMMs + HIP kernels)" if backward else ffpa.kernel_name(w2.D),
+                                  ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
                                   frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
 
     cpu, parity = None, None
