@@ -54,9 +54,10 @@ struct RingPlan {
 constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes) {
   RingPlan best{0, 0};
   int best_score = -1;
-  const int ems[3] = {32, 16, 8};
-  for (int i = 0; i < 3; ++i) {
+  const int ems[4] = {32, 16, 8, 4};
+  for (int i = 0; i < 4; ++i) {
     const int em = ems[i];
+    if (em == 4 && best.em != 0) break;  // four-product epochs only where nothing longer fits (D = 64)
     if (MPT % em != 0) continue;
     const int bi = em / 4;  // groups per epoch (four products per wave per group)
     for (int ng = 40; ng >= bi; --ng) {
@@ -101,10 +102,11 @@ struct RowTiling {
   static constexpr int LDS_BYTES = RING + EXCH;  // + MASKB when the mask is staged
 };
 
-// The head dims that run the row kernel (the others keep the column-split kernels).
+// The head dims that run the row kernel: every D with a ring plan and an even number of 32-column
+// steps per wave (576, 704, 832 and 960 keep the shared-staging kernel).
 template <int D>
 constexpr bool use_row_kernel() {
-  return RowTiling<D>::OK && D >= 256;
+  return RowTiling<D>::OK;
 }
 
 // s_waitcnt lgkmcnt(N) before a product whose operand fragments were read by inline assembly.
