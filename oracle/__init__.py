@@ -303,3 +303,43 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
             dK[b, hk] += (1.0 if fault == BWD_FAULT_DK_UNSCALED else scale) * (dS.T @ Q[b, h])
             dV[b, hk] += P.T @ dO[b, h]
     return dQ, dK, dV
+
+
+# Planted-mistake switches of the dropout form (tests of the pins only).
+DROP_FAULT_NONE = 0
+DROP_FAULT_SCALE_BY_KEEP = 1   # kept weights scaled by (1 - p) instead of 1 / (1 - p)
+DROP_FAULT_BIT_REVERSED = 2    # key i of a word read from bit 31 - i
+DROP_FAULT_LSE_DROPPED = 3     # LSE taken over the kept weights only
+
+
+def attention_dropout_rows(q, k, v, rows: Sequence[int], keep_bits, p: float, mask=None,
+                           scale: Optional[float] = None, is_causal: bool = False, fault: int = DROP_FAULT_NONE):
+    """Selected rows of attention with SDPA-style dropout on the attention weights, in fp64.
+
+    The weights are the softmax of the logits (as in ``attention_rows``); dropout keeps weight
+    (r, k) where the keep bitmask says so and multiplies the kept ones by 1 / (1 - p); the output is
+    the dropped-out weights times V.  The LSE is that of the logits, untouched by dropout.
+    ``keep_bits`` is [B, Hq, Nq, ceil(Nkv / 32)] uint32: bit i of word w keeps key 32 w + i
+    (``oracle.philox`` draws it).  p is taken as its float32 value, the precision of the C ABI.
+    Returns (O [n, D] float64, LSE [n] float64).
+    """
+    B, Hq, Nq, D = (int(x) for x in q.shape)
+    Hkv, Nkv = int(k.shape[1]), int(k.shape[2])
+    G = Hq // Hkv
+    O_plain, L, P = attention_rows(q, k, v, rows, mask=mask, scale=scale, is_causal=is_causal, want_probs=True)
+    kb = np.asarray(keep_bits, dtype=np.uint64).reshape(B * Hq * Nq, -1)
+    rows_arr = np.asarray(rows, dtype=np.int64)
+    key = np.arange(Nkv)
+    bit = (31 - key % 32) if fault == DROP_FAULT_BIT_REVERSED else key % 32
+    Z = ((kb[rows_arr][:, key // 32] >> bit.astype(np.uint64)) & np.uint64(1)).astype(np.float64)
+    p64 = float(np.float32(p))
+    factor = (1.0 - p64) if fault == DROP_FAULT_SCALE_BY_KEEP else 1.0 / (1.0 - p64)
+    V = v.detach().cpu().double().numpy()
+    O = np.zeros((rows_arr.size, D))
+    for i, idx in enumerate(rows_arr):
+        b, h = int(idx) // (Nq * Hq), (int(idx) // Nq) % Hq
+        O[i] = ((P[i] * Z[i]) @ V[b, h // G]) * factor
+    if fault == DROP_FAULT_LSE_DROPPED:
+        with np.errstate(divide="ignore"):
+            L = L + np.log((P * Z).sum(axis=1))
+    return O, L
