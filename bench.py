@@ -60,6 +60,46 @@ def time_workload(w, steps: int, warmup: int):
     return ms, (q, k, v, mask), (o.cpu(), lse.cpu())
 
 
+def time_dropout(w, p: float, steps: int, warmup: int):
+    """Times the forward with attention dropout (ffpa_fwd_dropout, keep words drawn once beforehand) and,
+    separately, the keep-word generator (ffpa_dropout_keep); returns (forward ms, generator ms)."""
+    import torch
+
+    import exact_attention_head_amd as ffpa
+    import workloads as W
+
+    q, k, v, mask = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    md = mask.to(dev) if mask is not None else None
+    o = torch.empty_like(qd)
+    keep = ffpa.dropout_keep(w.B, w.Hq, w.Nq, w.Nkv, p, seed=w.seed, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        return ffpa.attn(qd, kd, vd, attn_mask=md, dropout_p=p, dropout_keep=keep, is_causal=w.causal,
+                         enable_gqa=w.Hq != w.Hkv, return_lse=True, out=o)
+
+    def gen():
+        st = ffpa.ffpa_dropout_keep(keep.data_ptr(), w.B, w.Hq, w.Nq, w.Nkv, p, w.seed, 0, stream.cuda_stream)
+        if st != ffpa.OK:
+            raise RuntimeError(f"ffpa_dropout_keep returned {st}")
+
+    out = []
+    for fn in (fwd, gen):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps)
+    return out[0], out[1]
+
+
 def time_varlen(w, steps: int, warmup: int):
     """As time_workload, for a packed variable-length batch (one ffpa_fwd_varlen launch per step)."""
     import torch
@@ -296,13 +336,19 @@ def main() -> int:
     if args.sweep:
         names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
     else:
-        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "bwd:large_d_self",
-                 "bwd:sweep:1024"]
+        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "drop:large_d_self",
+                 "drop:sweep:1024", "bwd:large_d_self", "bwd:sweep:1024"]
     if not args.no_secondary and args.workload == "large_d_self":
         for name in names:
             backward = name.startswith("bwd:")
-            w2 = pick(name[4:] if backward else name)
-            if backward:
+            dropout = name.startswith("drop:")
+            w2 = pick(name[5:] if dropout else (name[4:] if backward else name))
+            if dropout:
+                # forward with attention dropout at p = 0.1: same FLOP count; the keep-word generator apart
+                ms2, gen_ms = time_dropout(w2, 0.1, max(5, args.steps // 5), 2)
+                flops2 = w2.flops
+                log(f"dropout keep words {w2.name}: {gen_ms:.4f} ms/launch")
+            elif backward:
                 # the backward's five products: 10*B*Hq*Nq*Nkv*D FLOPs (2.5x the forward), halved for causal
                 ms2 = time_backward(w2, max(3, args.steps // 10), 1)
                 flops2 = 2.5 * w2.flops
@@ -311,10 +357,11 @@ def main() -> int:
             else:
                 (ms2, _, _), flops2 = time_workload(w2, max(5, args.steps // 5), 2), w2.flops
             tf2 = flops2 / (ms2 * 1e-3) / 1e12
-            tag = ("backward " if backward else "") + w2.name
+            tag = ("backward " if backward else ("dropout p=0.1 " if dropout else "")) + w2.name
             log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
             secondary.append(dict(workload=tag, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
                                   kernel="ffpa_bwd (library GEMMs + HIP kernels)" if backward else ffpa.kernel_name(w2.D),
+                                  **({"keep_words_ms": round(gen_ms, 4)} if dropout else {}),
                                   ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
                                   frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
 

@@ -4,7 +4,8 @@
 with the semantics of ffpa_attn_func on the ffpa-attn "API Reference" page: SDPA-style layout
 [B, H, N, D], GQA/MQA through enable_gqa, cross-attention (Nq != Nkv), tail-aligned causal masking
 (row r sees keys k <= r + Nkv - Nq, requiring Nkv >= Nq), boolean masks (True takes part) and
-additive floating masks, and scale = 1/sqrt(D) by default.  ``attn_varlen`` is the packed
+additive floating masks, scale = 1/sqrt(D) by default, and SDPA-style attention dropout
+(dropout_p: keep decisions drawn on the GPU by Philox4x32-10, or given).  ``attn_varlen`` is the packed
 variable-length form of ffpa_attn_varlen_func on the same page: THD tensors [T, H, D], cumulative
 sequence offsets, the longest lengths, and an [Hq, Tq] LSE.
 
@@ -22,7 +23,8 @@ from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
-           "ffpa_bwd_workspace_size", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
+           "ffpa_bwd_workspace_size", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
+           "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,7 +36,8 @@ OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
-            "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size")
+            "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
+            "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args")
 
 
 class MaskDesc(ctypes.Structure):
@@ -93,6 +96,12 @@ def library() -> ctypes.CDLL:
     lib.ffpa_bwd.restype = i32
     lib.ffpa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.ffpa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ffpa_dropout_keep.argtypes = [p, i64, i64, i64, i64, f32, ctypes.c_uint64, ctypes.c_uint32, p]
+    lib.ffpa_dropout_keep.restype = i32
+    lib.ffpa_fwd_dropout.argtypes = args + [p, f32, p]
+    lib.ffpa_fwd_dropout.restype = i32
+    lib.ffpa_check_dropout_args.argtypes = args + [p, f32]
+    lib.ffpa_check_dropout_args.restype = i32
     _lib = lib
     return lib
 
@@ -112,6 +121,42 @@ def ffpa_fwd(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, 
     m = ctypes.byref(mask) if mask is not None else None
     return library().ffpa_fwd(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale), int(is_causal),
                               dtype, stream)
+
+
+def ffpa_dropout_keep(keep, B, Hq, Nq, Nkv, p, seed, offset, stream) -> int:
+    """The raw C entry point drawing dropout keep bits into keep (a device address)."""
+    return library().ffpa_dropout_keep(keep, B, Hq, Nq, Nkv, ctypes.c_float(p), seed & (2**64 - 1),
+                                       offset & 0xFFFFFFFF, stream)
+
+
+def ffpa_fwd_dropout(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype,
+                     keep, dropout_p, stream) -> int:
+    """The raw C entry point of the forward with dropout: pointers are integers, returns the status."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_fwd_dropout(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
+                                      int(is_causal), dtype, keep, ctypes.c_float(dropout_p), stream)
+
+
+def ffpa_check_dropout_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal,
+                            dtype, keep, dropout_p) -> int:
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_check_dropout_args(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale),
+                                             int(is_causal), dtype, keep, ctypes.c_float(dropout_p))
+
+
+def dropout_keep(B: int, Hq: int, Nq: int, Nkv: int, p: float, seed: int, offset: int = 0, device=None):
+    """Keep bits of attention dropout, drawn on the GPU: int32 [B, Hq, Nq, ceil(Nkv / 32)] holding
+    the uint32 words of ffpa_dropout_keep (bit i of word w keeps key 32 w + i)."""
+    import torch
+
+    device = torch.device("cuda") if device is None else torch.device(device)
+    keep = torch.empty((B, Hq, Nq, (Nkv + 31) // 32), dtype=torch.int32, device=device)
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        st = ffpa_dropout_keep(keep.data_ptr(), B, Hq, Nq, Nkv, float(p), int(seed), int(offset), stream)
+    if st != OK:
+        _raise(st)
+    return keep
 
 
 def ffpa_check_args(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal,
@@ -206,17 +251,26 @@ def _mask_desc(attn_mask, B, Hq, Nq, Nkv):
 
 
 def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False,
-         scale: Optional[float] = None, enable_gqa: bool = False, return_lse: bool = False, out=None):
+         scale: Optional[float] = None, enable_gqa: bool = False, return_lse: bool = False, out=None,
+         dropout_seed: Optional[int] = None, dropout_keep=None, return_dropout_keep: bool = False):
     """SDPA-aligned forward.  query [B, Hq, Nq, D]; key/value [B, Hkv, Nkv, D]; bf16 or fp16.
 
     Returns O [B, Hq, Nq, D] (dtype of query), or (O, LSE [B, Hq, Nq] float32) with return_lse.
     Strided views (for instance a [B, N, H, D] tensor transposed to [B, H, N, D]) are read in place
     through ffpa_fwd_strided when their strides allow it, and so is a strided ``out``.
+
+    Dropout (0 < dropout_p < 1, SDPA-style: each softmax weight kept with probability 1 - p, kept
+    ones scaled by 1 / (1 - p); the LSE is unchanged): the keep bits are drawn on the GPU by
+    ffpa_dropout_keep with seed ``dropout_seed`` (default: drawn from torch's CPU generator) and
+    offset 0, or taken from ``dropout_keep`` (int32 [B, Hq, Nq, ceil(Nkv / 32)] words, any bits;
+    dropout_p then sets the scaling).  ``return_dropout_keep`` appends the keep words to the result.
+    Dropout runs on contiguous tensors (others are copied first).
     """
     import torch
 
-    if dropout_p != 0.0:
-        raise NotImplementedError("attention dropout is not implemented (dropout_p must be 0)")
+    if not (0.0 <= float(dropout_p) < 1.0):
+        raise ValueError("dropout_p must lie in [0, 1)")
+    dropping = dropout_p != 0.0 or dropout_keep is not None
     for name, t in (("query", query), ("key", key), ("value", value)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
             raise ValueError(f"{name} must be a 4-D tensor [B, H, N, D]")
@@ -258,6 +312,9 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=query.device) if return_lse else None
     desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(query.device), B, Hq, Nq, Nkv)
     sc = math.nan if scale is None else float(scale)
+    if dropping:
+        return _attn_dropout(q, k, v, o, out, lse, desc, keep, B, Hq, Hkv, Nq, Nkv, D, sc, is_causal, dtype,
+                             float(dropout_p), dropout_seed, dropout_keep, return_lse, return_dropout_keep)
     with torch.cuda.device(query.device):
         stream = torch.cuda.current_stream(query.device).cuda_stream
         lp = lse.data_ptr() if lse is not None else None
@@ -273,6 +330,38 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     if st != OK:
         _raise(st)
     return (o, lse) if return_lse else o
+
+
+def _attn_dropout(q, k, v, o, out, lse, desc, mask_keep, B, Hq, Hkv, Nq, Nkv, D, sc, is_causal, dtype, p, seed,
+                  keep, return_lse, return_keep):
+    """attn with dropout: contiguous tensors, keep bits drawn (or given), ffpa_fwd_dropout."""
+    import torch
+
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    o_c = o if o.is_contiguous() else torch.empty((B, Hq, Nq, D), dtype=q.dtype, device=q.device)
+    W = (Nkv + 31) // 32
+    if keep is None:
+        if seed is None:
+            seed = int(torch.randint(0, 2**62, (1,)).item())
+        keep = dropout_keep(B, Hq, Nq, Nkv, p, seed, 0, q.device)
+    else:
+        if not isinstance(keep, torch.Tensor) or keep.dtype != torch.int32 or tuple(keep.shape) != (B, Hq, Nq, W):
+            raise ValueError(f"dropout_keep must be an int32 tensor of shape {(B, Hq, Nq, W)}")
+        keep = keep.to(q.device).contiguous()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        lp = lse.data_ptr() if lse is not None else None
+        st = ffpa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o_c.data_ptr(), lp, B, Hq, Hkv, Nq, Nkv,
+                              D, sc, bool(is_causal), dtype, keep.data_ptr(), p, stream)
+    del mask_keep
+    if st != OK:
+        _raise(st)
+    if o_c is not o:
+        o.copy_(o_c)
+    res = (o, lse) if return_lse else (o,)
+    if return_keep:
+        res = res + (keep,)
+    return res if len(res) > 1 else res[0]
 
 
 # keyword arguments of ffpa_attn_varlen_func that this forward rejects when given a non-default value

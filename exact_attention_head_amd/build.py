@@ -67,19 +67,21 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or max(1, min(16, os.cpu_count() or 4))
     tasks = [(os.path.join(CSRC, "ffpa_api.hip"), os.path.join(BUILD, "ffpa_api.o"), []),
-             (os.path.join(CSRC, "ffpa_bwd.hip"), os.path.join(BUILD, "ffpa_bwd.o"), [])]
+             (os.path.join(CSRC, "ffpa_bwd.hip"), os.path.join(BUILD, "ffpa_bwd.o"), []),
+             (os.path.join(CSRC, "ffpa_dropout.hip"), os.path.join(BUILD, "ffpa_dropout.o"), [])]
     for tag in ("Bf16", "Fp16"):
         for d in head_dims():
             tasks.append((os.path.join(CSRC, "ffpa_inst.hip"), os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}.o"),
                           [f"-DFFPA_INST_T={tag}", f"-DFFPA_INST_D={d}"]))
     # largest kernels first
-    tasks.sort(key=lambda t: -int(re.search(r"_d(\d+)", t[1]).group(1)) if "_d" in t[1] else 0)
+    kd = lambda path: re.search(r"_d(\d+)\.o$", path)  # per-head-dim kernel objects
+    tasks.sort(key=lambda t: -int(kd(t[1]).group(1)) if kd(t[1]) else 0)
     resources = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_compile, s, o, d, report) for s, o, d in tasks]
         for f in cf.as_completed(futs):
             obj, err = f.result()
-            if report and "_d" in obj:
+            if report and kd(obj):
                 resources[os.path.basename(obj)[:-2]] = resource_summary(err)
     objs = [o for _, o, _ in tasks]
     # the kernels' inline assembly relies on rules the compiler does not check: verify them
@@ -91,7 +93,7 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
 
     hazards = []
     for o in objs:
-        if "_d" in os.path.basename(o):
+        if kd(o):
             hazards += check_hazards(o[:-2] + ".s")
     if hazards:
         raise RuntimeError("MFMA / LDS hazards in the generated code:\n" + "\n".join(hazards[:20]))

@@ -247,8 +247,14 @@ int ffpa_check_args(const void* q, const void* k, const void* v, const ffpa_mask
 
 static int launch_dense(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
                         int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
-                        const ffpa_layout_t* lay, float scale, int is_causal, int dtype, void* stream) {
+                        const ffpa_layout_t* lay, float scale, int is_causal, int dtype, void* stream,
+                        const uint32_t* keep = nullptr, float dropout_p = 0.f) {
   ffpa::FwdArgs a{};
+  if (keep != nullptr) {
+    a.keep = keep;
+    a.keep_w = (int)((Nkv + 31) / 32);
+    a.drop_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+  }
   if (lay == nullptr) {  // contiguous [B, H, N, D]
     a.q_sb = a.o_sb = Hq * Nq * D;
     a.q_sh = a.o_sh = Nq * D;
@@ -308,6 +314,31 @@ int ffpa_fwd(const void* q, const void* k, const void* v, const ffpa_mask_t* mas
   const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
   if (st != FFPA_OK) return st;
   return launch_dense(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, nullptr, scale, is_causal, dtype, stream);
+}
+
+int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                            const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                            float scale, int is_causal, int dtype, const uint32_t* keep, float dropout_p) {
+  const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  if (!(dropout_p >= 0.f && dropout_p < 1.f)) return fail(FFPA_ERR_VALUE, "dropout probability must lie in [0, 1)");
+  if (keep == nullptr || ((uintptr_t)keep & 3)) return fail(FFPA_ERR_VALUE, "keep must be non-null and 4-byte aligned");
+  if (B * Hq * Nq * ((Nkv + 31) / 32) >= (1LL << 40)) return fail(FFPA_ERR_UNSUPPORTED, "keep mask too large");
+  const size_t kbytes = (size_t)(B * Hq * Nq * ((Nkv + 31) / 32)) * 4;
+  const size_t obytes = (size_t)(B * Hq * Nq * D) * 2, lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
+  if (ranges_overlap(o, obytes, keep, kbytes) || ranges_overlap(lse, lbytes, keep, kbytes))
+    return fail(FFPA_ERR_VALUE, "o and lse must not overlap the keep mask");
+  return FFPA_OK;
+}
+
+int ffpa_fwd_dropout(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
+                     int is_causal, int dtype, const uint32_t* keep, float dropout_p, void* stream) {
+  const int st = ffpa_check_dropout_args(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, keep,
+                                         dropout_p);
+  if (st != FFPA_OK) return st;
+  return launch_dense(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, nullptr, scale, is_causal, dtype, stream, keep,
+                      dropout_p);
 }
 
 int ffpa_check_strided_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,

@@ -100,6 +100,12 @@ struct FwdArgs {
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_sr, kv_sr, o_sr;
   int strided;  // 1: the dense layout is not contiguous (the runtime-layout variants serve it)
+  // Attention dropout (null keep: none; dense contiguous layout only).  keep is [B, Hq, Nq, keep_w]
+  // 32-bit words: bit i of word w set keeps the weight of key 32 w + i for that query row; kept
+  // weights are scaled by drop_scale = 1 / (1 - p) (applied to O with the 1/l normalisation).
+  const uint32_t* keep;
+  int keep_w;
+  float drop_scale;
 };
 
 // Tokens of sequence b of a packed batch.  The offsets are clamped to the packed tensors and the
@@ -607,6 +613,9 @@ struct ChunkLoader {
   }
 };
 
+// Attention dropout (FwdArgs::keep set; dense contiguous layout): a weight whose keep bit is clear is
+// left out of P V, and O is scaled by 1 / (1 - p) at the end; row sums and LSE keep every weight.
+// The launch-uniform branches on it cost the other launches one scalar test per tile.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   using K = FwdKernel<T, D>;
@@ -736,6 +745,22 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   }
 
   for (int j = 0; j < ntiles; ++j) {
+    // dropout: the keep words of this wave's keys (key0 + 64/DG * dg + 8g + 4hi + e) for each of its
+    // row blocks, requested before the products so that they have arrived by the softmax (a row past
+    // Nq reads row Nq - 1 and a word past the row's last one reads the last: never used)
+    constexpr int NKW = 2 / DG;  // 32-key words owned per row
+    const bool drop = a.keep != nullptr;
+    uint32_t kw[RB][NKW];
+    if (drop) {
+      const int w0 = (j * BC + (BC / DG) * dg) >> 5, wl = a.keep_w - 1;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = rw0 + rb * 32 + l32;
+        const uint32_t* kr = a.keep + ((int64_t)(b * a.Hq + hq) * Nq + (row < Nq ? row : Nq - 1)) * a.keep_w;
+#pragma unroll
+        for (int w = 0; w < NKW; ++w) kw[rb][w] = kr[w0 + w < wl ? w0 + w : wl];
+      }
+    }
     // ================= S^T = K Q^T over this wave's columns (Split-D chunks) =================
     f32x16 s_acc[RB][2];
 
@@ -900,6 +925,18 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
           p[g][e] = __builtin_amdgcn_exp2f(t4[rb][g][e] - mref);
           rs += p[g][e];
         }
+      if (drop) {
+        // key 8g + 4hi + e of the owned keys: bit 8(g % 4) + 4hi + e of word g / 4
+#pragma unroll
+        for (int g = 0; g < NQ; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // (through a scalar: a bit cast of the vector element itself would read element 0)
+            const int sel = -(int)((kw[rb][g >> 2] >> (8 * (g & 3) + 4 * hi + e)) & 1u);
+            const float pe = p[g][e];
+            p[g][e] = __builtin_bit_cast(float, sel & __builtin_bit_cast(int, pe));
+          }
+      }
 #pragma unroll
       for (int k2 = 0; k2 < OWN_KS; ++k2) {
         i32x4 w;
@@ -983,7 +1020,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
     const int row = rw0 + rb * 32 + l32;
     if (row < Nq) {
       const float l = l_run[rb];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float inv = l > 0.f ? 1.f / l : 0.f;
+      if (a.keep != nullptr) inv *= a.drop_scale;
       uint16_t* orow = a.o + o_base + (int64_t)row * o_rs + col0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -1032,6 +1070,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const bool packed = a.cu_q != nullptr;
   if (a.group < 1 || a.Hkv < 1 || a.Hq != a.group * a.Hkv || a.B < 1 || a.Nq < 1 || a.Nkv < (packed ? 0 : 1))
     return hipErrorInvalidValue;
+  // dropout: the dense contiguous layout, with a keep word for every 32 keys of a row
+  const bool drop = a.keep != nullptr;
+  if (drop && (packed || a.strided || a.keep_w != (a.Nkv + 31) / 32)) return hipErrorInvalidValue;
   // a packed batch has both offset arrays and no mask
   if (packed && (a.cu_k == nullptr || a.mask_kind != kMaskNone || a.Tq < 0 || a.Tk < 0)) return hipErrorInvalidValue;
   constexpr int BR = rows_per_block<D>();
@@ -1047,7 +1088,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     // packed batches and strided layouts take the runtime-layout variants (for packed batches the
     // lengths live on the device, so whole and partial tiles are told apart in the kernel)
     const bool runtime_layout = packed || a.strided;
-    if (runtime_layout && plain)
+    if (drop)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowDrop, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else if (runtime_layout && plain)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (runtime_layout)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, true>), dim3((unsigned)blocks), dim3(256), 0, stream,

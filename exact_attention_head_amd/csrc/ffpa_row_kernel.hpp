@@ -206,8 +206,10 @@ constexpr int row_load_slot(int bs, int q, int step, int MPT) {
 // diagonal, a partial last tile) explicit, in two successive loops), kRowMaskF32 (every tile
 // explicit, with an fp32 additive mask whose rows are
 // staged through LDS: whole 128-byte lines per direct-to-LDS load, one tile ahead, instead of
-// scattered 16-byte loads per lane).  The launcher picks the variant.
-enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3 };
+// scattered 16-byte loads per lane), kRowDrop (kRowGeneral with attention dropout: each weight
+// whose keep bit is clear is left out of P V, and O is scaled by 1 / (1 - p) at the end; the row
+// sums and the LSE keep every weight).  The launcher picks the variant.
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3, kRowDrop = 4 };
 
 // Loads (per wave) issued in slot x of a tile: load q of the refill after the barrier at slot
 // e*EM - PF goes to row_load_slot(...).
@@ -267,6 +269,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   static_assert(1 + (NL - 1) * LSTEP < EM, "the loads after a barrier end before the next one");
 
   constexpr bool MASK_LDS = MODE == kRowMaskF32;
+  constexpr bool DROP = MODE == kRowDrop;
+  static_assert(!DROP || !VL, "dropout runs on the contiguous dense layout");
   constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // the partner's partial of block 0 is read (after a barrier, complete PF products later) before
@@ -337,6 +341,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   }
   const int rw0 = r0 + rg * 32;  // first row of this wave
   const int row = rw0 + l32;     // this lane's row
+  // dropout: this lane's row of keep words (a row past Nq reads row Nq - 1; it is never stored)
+  const uint32_t* keep_row = nullptr;
+  if constexpr (DROP) keep_row = a.keep + ((int64_t)(b * a.Hq + hq) * Nq + (row < Nq ? row : Nq - 1)) * a.keep_w;
   const int col0 = dg * DW;
   const int off = Nkv - Nq;
   const uint16_t* qg = a.q + q_base;
@@ -545,6 +552,14 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     if (!RAW && !MASK_LDS && has_mask)
       load_bias_dispatch<1, 4>(*reinterpret_cast<f32x4(*)[1][4]>(&bias[0][0]), ctx, key0, a.mask_kind,
                                a.mask_vec && !tail);
+    // dropout: the keep words of the tile's two 32-key blocks (a block past the row's last word reads
+    // the last word; its keys are excluded anyway)
+    uint32_t kw[2] = {0u, 0u};
+    if constexpr (DROP) {
+      const int wl = a.keep_w - 1, w0 = key0 >> 5;
+      kw[0] = keep_row[w0 < wl ? w0 : wl];
+      kw[1] = keep_row[w0 + 1 < wl ? w0 + 1 : wl];
+    }
 
     float mt[2], m_old[2], mref[2], pv[2][2];
     // softmax micro-piece k of block kb (see row_sm_pieces)
@@ -599,6 +614,10 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         alpha[kb] = need[kb] ? __builtin_amdgcn_exp2f(m_old[kb] - m_new[kb]) : 1.f;
         psum[kb] = 0.f;
         asm volatile("" : "+v"(alpha[kb]), "+v"(psum[kb]));
+        if constexpr (DROP) {
+          kw[kb] >>= 4 * hi;  // this lane's keys 8g + 4hi + e sit at bits 8g + e
+          asm volatile("" : "+v"(kw[kb]));
+        }
       } else {
         const int i = k - NLP - 3;  // key 0..15 of this lane's 16 in the block
         const int g = i >> 2, e = i & 3;
@@ -606,11 +625,17 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         const float x = RAW ? __builtin_fmaf(sv, a.scale_log2, -mref[kb]) : sv - mref[kb];
         const float p = __builtin_amdgcn_exp2f(x);
         psum[kb] += p;
+        float pd = p;  // the weight that enters P V
+        if constexpr (DROP) {
+          // all ones when the key's keep bit is set, zero otherwise
+          const int sel = -(int)((kw[kb] >> (8 * g + e)) & 1u);
+          pd = __builtin_bit_cast(float, sel & __builtin_bit_cast(int, p));
+        }
         if ((e & 1) == 0) {
-          pv[kb][0] = p;
+          pv[kb][0] = pd;
           asm volatile("" : "+v"(pv[kb][0]), "+v"(psum[kb]));
         } else {
-          pk[kb][g >> 1][2 * (g & 1) + (e >> 1)] = (int)pack2<T>(pv[kb][0], p);
+          pk[kb][g >> 1][2 * (g & 1) + (e >> 1)] = (int)pack2<T>(pv[kb][0], pd);
           asm volatile("" : "+v"(pk[kb][g >> 1]), "+v"(psum[kb]));
         }
       }
@@ -750,7 +775,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   };
   if constexpr (MODE == kRowRaw) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
-  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32) {
+  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32 || MODE == kRowDrop) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
   } else {
     static_assert(MODE == kRowSplit, "tile mode");
@@ -769,7 +794,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   mma_guard_all<NSUB>(o_acc);
   const float l = sum_halves(l_lane);
   if (row < Nq) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float inv = l > 0.f ? 1.f / l : 0.f;
+    if constexpr (DROP) inv *= a.drop_scale;
     uint16_t* orow = a.o + o_base + (int64_t)row * o_rs + col0;
     static_for<NSUB>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;

@@ -129,6 +129,57 @@ int ffpa_check_strided_args(const void* q, const void* k, const void* v, const f
                             const ffpa_layout_t* layout, float scale, int is_causal, int dtype);
 
 /*
+ * ffpa_dropout_keep -- enqueue the drawing of attention-dropout keep
+ * decisions on `stream` (the ffpa-attn "API Reference" page, parameter
+ * "dropout_p" of ffpa_attn_func: SDPA-style dropout keeps each attention
+ * weight independently with probability 1 - p).
+ *
+ *   keep    device, [B, Hq, Nq, W] uint32, W = ceil(Nkv / 32), contiguous,
+ *           4-byte aligned; written.  Bit i of word w set keeps key 32 w + i
+ *           for that query row; bits of keys >= Nkv are 0.
+ *   B, Hq, Nq, Nkv >= 1
+ *   p       drop probability, 0 <= p < 1
+ *   seed, offset  select the stream: the decisions are a pure function of
+ *           (seed, offset, p, b, h, r, key) and of Hq, Nq (the row index
+ *           (b Hq + h) Nq + r); they come from Philox4x32-10 (Salmon et al.,
+ *           SC 2011) with key (seed mod 2^32, seed div 2^32) and, for word w of
+ *           row index R and block j < 8, counter (8 w + j, R mod 2^32,
+ *           R div 2^32, offset); output i of block j decides key 32 w + 4 j + i,
+ *           kept when it is at least floor(p 2^32).
+ *   stream  hipStream_t, NULL for the null stream
+ *
+ * Errors: FFPA_ERR_VALUE for sizes < 1, p outside [0, 1) or a null or
+ * misaligned keep; FFPA_ERR_UNSUPPORTED for a mask beyond 2^40 words;
+ * FFPA_ERR_HIP if the launch fails.  Allocates nothing.
+ */
+int ffpa_dropout_keep(uint32_t* keep, int64_t B, int64_t Hq, int64_t Nq, int64_t Nkv, float p, uint64_t seed,
+                      uint32_t offset, void* stream);
+
+/*
+ * ffpa_fwd_dropout -- ffpa_fwd with SDPA-style attention dropout on the
+ * softmax weights (same page, parameter "dropout_p"):
+ *
+ *   O[b,h,r,:] = sum_k P[r,k] * keep[r,k] / (1 - dropout_p) * V[b,g(h),k,:]
+ *
+ * with P the softmax weights of ffpa_fwd and keep[r,k] the bit of `keep`
+ * (device, [B, Hq, Nq, ceil(Nkv / 32)] uint32 in the layout of
+ * ffpa_dropout_keep, read only; any bits may be given).  The LSE is that of
+ * the logits, as in ffpa_fwd: dropout does not change it.  Tensors are
+ * contiguous as in ffpa_fwd; every other argument, rule and error is that of
+ * ffpa_fwd, plus FFPA_ERR_VALUE for dropout_p outside [0, 1), a null or
+ * misaligned keep, or o / lse overlapping keep.
+ */
+int ffpa_fwd_dropout(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
+                     int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
+                     int is_causal, int dtype, const uint32_t* keep, float dropout_p, void* stream);
+
+/* The host-side argument check ffpa_fwd_dropout performs, without enqueuing
+ * anything. */
+int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o,
+                            const float* lse, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                            float scale, int is_causal, int dtype, const uint32_t* keep, float dropout_p);
+
+/*
  * ffpa_bwd -- enqueue the backward of ffpa_fwd on `stream`: the gradients of
  * O with respect to Q, K and V, given dout = dL/dO (the ffpa-attn "API
  * Reference" page supports the backward of ffpa_attn_func; the mask is a

@@ -133,8 +133,9 @@ def test_python_layer_rejects_before_the_library():
     import torch
 
     q = torch.zeros(1, 2, 4, 64, dtype=torch.float32)
-    with pytest.raises(NotImplementedError):
-        ffpa.attn(q, q, q, dropout_p=0.1)
+    for p in (1.0, -0.1, 1.5):  # dropout probability outside [0, 1)
+        with pytest.raises(ValueError):
+            ffpa.attn(q, q, q, dropout_p=p)
     with pytest.raises(TypeError):
         ffpa.attn(q, q, q)
     qb = q.to(torch.bfloat16)
@@ -259,3 +260,40 @@ def test_strided_layout_overlap_uses_extents():
     assert scheck(layout(), o=Q + ext - 16) == ffpa.ERR_VALUE
     assert ffpa.ffpa_check_strided_args(Q, K, V, None, O, L, 1, 2, 1, 100, 130, 512, None, math.nan, False,
                                         ffpa.FFPA_BF16) == ffpa.ERR_VALUE  # no layout
+
+
+# ---- attention dropout (ffpa_fwd_dropout, ffpa_dropout_keep): host-side checks only
+KEEP = 0x90_0000_0000
+
+
+def dcheck(p=0.1, keep=KEEP, o=O, lse=L, Nkv=300, **kw):
+    args = dict(B=2, Hq=4, Hkv=2, Nq=200, D=512, scale=math.nan, causal=False, dtype=ffpa.FFPA_BF16)
+    args.update(kw)
+    return ffpa.ffpa_check_dropout_args(Q, K, V, None, o, lse, args["B"], args["Hq"], args["Hkv"], args["Nq"], Nkv,
+                                        args["D"], args["scale"], args["causal"], args["dtype"], keep, p)
+
+
+def test_dropout_valid_arguments_pass():
+    assert dcheck() == ffpa.OK
+    assert dcheck(p=0.0) == ffpa.OK
+    assert dcheck(p=0.999) == ffpa.OK
+    assert dcheck(D=576) == ffpa.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(p=1.0), ffpa.ERR_VALUE), (dict(p=-0.5), ffpa.ERR_VALUE), (dict(p=float("nan")), ffpa.ERR_VALUE),
+    (dict(keep=None), ffpa.ERR_VALUE), (dict(keep=KEEP + 2), ffpa.ERR_VALUE),
+    (dict(keep=O), ffpa.ERR_VALUE),            # o overlaps the keep words
+    (dict(dtype=5), ffpa.ERR_TYPE), (dict(D=80), ffpa.ERR_UNSUPPORTED), (dict(Hkv=3), ffpa.ERR_VALUE),
+])
+def test_dropout_argument_errors(kw, status):
+    assert dcheck(**kw) == status
+
+
+def test_dropout_keep_rejects_before_launching():
+    lib = ffpa.library()
+    for args in ((KEEP, 0, 1, 1, 1, 0.1), (KEEP, 1, 1, 1, 1, 1.0), (KEEP, 1, 1, 1, 1, -0.1), (None, 1, 1, 1, 1, 0.1),
+                 (KEEP + 1, 1, 1, 1, 1, 0.1)):
+        assert ffpa.ffpa_dropout_keep(*args, 0, 0, None) == ffpa.ERR_VALUE
+    ffpa.ffpa_dropout_keep(KEEP, 1, 1, 1, 1, 1.0, 0, 0, None)
+    assert b"[0, 1)" in lib.ffpa_last_error_detail()
