@@ -71,33 +71,35 @@ def drop_threshold(p: float) -> int:
     return int(p32 * 4294967296.0)
 
 
-def dropout_keep_bits(B: int, Hq: int, Nq: int, Nkv: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
-    """Keep bitmask [B, Hq, Nq, ceil(Nkv / 32)] uint32 of the layout in the module docstring."""
+def dropout_keep_rows(rows, Nkv: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """Keep words [len(rows), ceil(Nkv / 32)] uint32 of the given row indices R = (b * Hq + h) * Nq + r."""
     W = (Nkv + 31) // 32
     thr = np.uint64(drop_threshold(p))
-    R = np.arange(B * Hq * Nq, dtype=np.uint64)[:, None, None]          # row index
+    R = np.asarray(rows, dtype=np.uint64)[:, None, None]
     w = np.arange(W, dtype=np.uint64)[None, :, None]
     j = np.arange(8, dtype=np.uint64)[None, None, :]
-    shape = (B * Hq * Nq, W, 8)
+    shape = (R.shape[0], W, 8)
     c0 = np.broadcast_to(np.uint64(8) * w + j, shape)
     c1 = np.broadcast_to(R & np.uint64(_MASK32), shape)
     c2 = np.broadcast_to(R >> np.uint64(32), shape)
     c3 = np.full(shape, offset & _MASK32, dtype=np.uint64)
     u = philox4x32_10_np(c0, c1, c2, c3, seed & _MASK32, (seed >> 32) & _MASK32)
-    keep = np.zeros((B * Hq * Nq, W), dtype=np.uint64)
+    keep = np.zeros((R.shape[0], W), dtype=np.uint64)
     for jj in range(8):
         for i in range(4):
-            bit = 4 * jj + i
-            keep |= (u[i][:, :, jj] >= thr).astype(np.uint64) << np.uint64(bit)
+            keep |= (u[i][:, :, jj] >= thr).astype(np.uint64) << np.uint64(4 * jj + i)
     # keys at or past Nkv are never kept
-    key = np.arange(W * 32).reshape(W, 32)
     valid = np.zeros(W, dtype=np.uint64)
-    for ww in range(W):
-        for i in range(32):
-            if key[ww, i] < Nkv:
-                valid[ww] |= np.uint64(1) << np.uint64(i)
+    for key in range(Nkv):
+        valid[key // 32] |= np.uint64(1) << np.uint64(key % 32)
     keep &= valid[None, :]
-    return keep.astype(np.uint32).reshape(B, Hq, Nq, W)
+    return keep.astype(np.uint32)
+
+
+def dropout_keep_bits(B: int, Hq: int, Nq: int, Nkv: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """Keep bitmask [B, Hq, Nq, ceil(Nkv / 32)] uint32 of the layout in the module docstring."""
+    keep = dropout_keep_rows(np.arange(B * Hq * Nq), Nkv, p, seed, offset)
+    return keep.reshape(B, Hq, Nq, keep.shape[-1])
 
 
 def keep_matrix(keep_bits: np.ndarray, Nkv: int) -> np.ndarray:
