@@ -23,7 +23,7 @@ from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
-           "ffpa_bwd_workspace_size", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
+           "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
            "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
@@ -37,7 +37,7 @@ OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
-            "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args")
+            "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout")
 
 
 class MaskDesc(ctypes.Structure):
@@ -94,6 +94,9 @@ def library() -> ctypes.CDLL:
     lib.ffpa_bwd.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, i64, i64, i64, i64, i64, i64, f32,
                              i32, i32, p, ctypes.c_size_t, p]
     lib.ffpa_bwd.restype = i32
+    lib.ffpa_bwd_dropout.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, i64, i64, i64, i64, i64, i64,
+                                     f32, i32, i32, p, f32, p, ctypes.c_size_t, p]
+    lib.ffpa_bwd_dropout.restype = i32
     lib.ffpa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.ffpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffpa_dropout_keep.argtypes = [p, i64, i64, i64, i64, f32, ctypes.c_uint64, ctypes.c_uint32, p]
@@ -448,14 +451,24 @@ def ffpa_bwd(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv, B, Hq,
                               int(is_causal), dtype, workspace, workspace_bytes, stream)
 
 
+def ffpa_bwd_dropout(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+                     is_causal, dtype, keep, dropout_p, workspace, workspace_bytes, stream) -> int:
+    """The raw backward entry point of the forward with dropout; returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_bwd_dropout(q, k, v, o, dout, lse, m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D,
+                                      ctypes.c_float(scale), int(is_causal), dtype, keep, ctypes.c_float(dropout_p),
+                                      workspace, workspace_bytes, stream)
+
+
 def ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D) -> int:
     return int(library().ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D))
 
 
 def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_causal: bool = False,
-                  scale: Optional[float] = None):
+                  scale: Optional[float] = None, dropout_p: float = 0.0, dropout_keep=None):
     """Gradients (dQ, dK, dV) of ``attn`` at (query, key, value), given its output ``out``, its LSE and
-    the output's gradient.  Tensors [B, H, N, D] as for ``attn``; the mask gets no gradient."""
+    the output's gradient.  Tensors [B, H, N, D] as for ``attn``; the mask gets no gradient.  After a
+    forward with dropout, pass its dropout_p and keep words (``return_dropout_keep``)."""
     import torch
 
     q, k, v, o, do = (t.contiguous() for t in (query, key, value, out, grad_out))
@@ -474,11 +487,24 @@ def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_caus
     desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(q.device), B, Hq, Nq, Nkv)
     dtype = FFPA_BF16 if q.dtype == torch.bfloat16 else FFPA_FP16
     sc = math.nan if scale is None else float(scale)
+    if dropout_keep is not None:
+        W = (Nkv + 31) // 32
+        if dropout_keep.dtype != torch.int32 or tuple(dropout_keep.shape) != (B, Hq, Nq, W):
+            raise ValueError(f"dropout_keep must be an int32 tensor of shape {(B, Hq, Nq, W)}")
+        dropout_keep = dropout_keep.to(q.device).contiguous()
+    elif dropout_p != 0.0:
+        raise ValueError("a backward with dropout needs the forward's keep words (dropout_keep)")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        st = ffpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), desc,
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal), dtype,
-                      ws.data_ptr(), nbytes, stream)
+        if dropout_keep is None:
+            st = ffpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), desc,
+                          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal),
+                          dtype, ws.data_ptr(), nbytes, stream)
+        else:
+            st = ffpa_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), desc, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq,
+                                  Nkv, D, sc, bool(is_causal), dtype, dropout_keep.data_ptr(), float(dropout_p),
+                                  ws.data_ptr(), nbytes, stream)
     del keep
     if st != OK:
         _raise(st)
@@ -489,14 +515,22 @@ def _autograd_function():
     import torch
 
     class AttnFunction(torch.autograd.Function):
-        """Forward through ffpa_fwd (keeping O and the LSE), backward through ffpa_bwd."""
+        """Forward through ffpa_fwd or ffpa_fwd_dropout (keeping O, the LSE and the keep words),
+        backward through ffpa_bwd or ffpa_bwd_dropout."""
 
         @staticmethod
-        def forward(ctx, query, key, value, attn_mask, is_causal, scale, enable_gqa):
-            o, lse = attn(query, key, value, attn_mask=attn_mask, is_causal=is_causal, scale=scale,
-                          enable_gqa=enable_gqa, return_lse=True)
+        def forward(ctx, query, key, value, attn_mask, is_causal, scale, enable_gqa, dropout_p=0.0, dropout_seed=None):
+            keep = None
+            if dropout_p != 0.0:
+                o, lse, keep = attn(query, key, value, attn_mask=attn_mask, is_causal=is_causal, scale=scale,
+                                    enable_gqa=enable_gqa, return_lse=True, dropout_p=dropout_p,
+                                    dropout_seed=dropout_seed, return_dropout_keep=True)
+            else:
+                o, lse = attn(query, key, value, attn_mask=attn_mask, is_causal=is_causal, scale=scale,
+                              enable_gqa=enable_gqa, return_lse=True)
             ctx.save_for_backward(query, key, value, o, lse)
             ctx.attn_mask, ctx.is_causal, ctx.scale = attn_mask, is_causal, scale
+            ctx.dropout_p, ctx.keep = dropout_p, keep
             ctx.mark_non_differentiable(lse)
             return o, lse
 
@@ -504,8 +538,9 @@ def _autograd_function():
         def backward(ctx, grad_o, grad_lse):
             query, key, value, o, lse = ctx.saved_tensors
             dq, dk, dv = attn_backward(query, key, value, o, grad_o, lse, attn_mask=ctx.attn_mask,
-                                       is_causal=ctx.is_causal, scale=ctx.scale)
-            return dq, dk, dv, None, None, None, None
+                                       is_causal=ctx.is_causal, scale=ctx.scale, dropout_p=ctx.dropout_p,
+                                       dropout_keep=ctx.keep)
+            return dq, dk, dv, None, None, None, None, None, None
 
     return AttnFunction
 
@@ -522,7 +557,8 @@ def AttnFunction():
 
 
 def attn_with_grad(query, key, value, attn_mask=None, is_causal: bool = False, scale: Optional[float] = None,
-                   enable_gqa: bool = False):
-    """``attn`` recorded for autograd: O is differentiable in query, key and value."""
-    o, _ = AttnFunction().apply(query, key, value, attn_mask, is_causal, scale, enable_gqa)
+                   enable_gqa: bool = False, dropout_p: float = 0.0, dropout_seed: Optional[int] = None):
+    """``attn`` recorded for autograd: O is differentiable in query, key and value (with dropout, the
+    keep words drawn by the forward are reused by the backward)."""
+    o, _ = AttnFunction().apply(query, key, value, attn_mask, is_causal, scale, enable_gqa, dropout_p, dropout_seed)
     return o

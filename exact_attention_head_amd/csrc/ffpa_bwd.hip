@@ -11,6 +11,9 @@
 //   dQ = dS K                     written as the output dtype (library GEMM)
 //   dK_g = dS^T Q                 [G, Nkv, D] f32  (library GEMM)
 //   dK, dV = sums over the group's G heads        (HIP kernel)
+// With attention dropout (ffpa_bwd_dropout: O = (P * M) V with M = keep / (1 - p) a constant), the
+// 16-bit copy of P that forms dV holds P * M, and the row term is applied to dP * M:
+// dS = scale P (dP M - Delta), with Delta = rowsum(dO * O) of the dropped-out O.
 // The matrix products are plain dense GEMMs (rocBLAS strided-batched, bf16/fp16 in, fp32
 // accumulate); the softmax recompute, the row term and the group sums are the kernels below.
 #include <hip/hip_fp16.h>
@@ -90,7 +93,16 @@ struct GroupArgs {
   const void* mask;
   int mask_kind;
   int64_t msb, msh, msq;
+  const uint32_t* keep;  // dropout keep words [B, Hq, Nq, keep_w] (null: no dropout)
+  int keep_w;
+  float drop_scale;      // 1 / (1 - p)
 };
+
+// The dropout factor M of (row r of query head h, key k): keep bit / (1 - p).
+__device__ inline float drop_factor(const GroupArgs& g, int h, int r, int k) {
+  const uint32_t w = g.keep[(((int64_t)g.b * g.Hq + h) * g.Nq + r) * g.keep_w + (k >> 5)];
+  return ((w >> (k & 31)) & 1u) ? g.drop_scale : 0.f;
+}
 
 // P = exp(scale S + bias - LSE) over [G, Nq, Nkv] in place (f32), plus its 16-bit copy.
 __global__ __launch_bounds__(256) void bwd_probs_kernel(float* __restrict__ s, uint16_t* __restrict__ p16, GroupArgs g) {
@@ -110,7 +122,7 @@ __global__ __launch_bounds__(256) void bwd_probs_kernel(float* __restrict__ s, u
     p = exp2f((x - lse) * kLog2eB);
   }
   s[i] = p;
-  p16[i] = store16(p, g.is_fp16);
+  p16[i] = store16(g.keep != nullptr ? p * drop_factor(g, h, r, k) : p, g.is_fp16);
 }
 
 // dS = scale P (dP - Delta) as 16-bit, over [G, Nq, Nkv].
@@ -123,7 +135,8 @@ __global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ p
   const int r = (int)(gr % g.Nq);
   const int h = g.hk * g.G + (int)(gr / g.Nq);
   const float dl = g.delta[((int64_t)g.b * g.Hq + h) * g.Nq + r];
-  ds16[i] = store16(g.scale * p[i] * (dp[i] - dl), g.is_fp16);
+  const float dpm = g.keep != nullptr ? dp[i] * drop_factor(g, h, r, (int)(i % g.Nkv)) : dp[i];
+  ds16[i] = store16(g.scale * p[i] * (dpm - dl), g.is_fp16);
 }
 
 // out[j] = 16-bit(sum over the G heads of acc[g * n + j]), j < n.
@@ -215,12 +228,10 @@ size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, i
   return layout(B, Hq, Hkv, Nq, Nkv, D).total;
 }
 
-int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-             const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
-             int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace, size_t workspace_bytes,
-             void* stream) {
-  int st = bwd_check(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
-  if (st != FFPA_OK) return st;
+static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                    int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace,
+                    size_t workspace_bytes, void* stream, const uint32_t* keep, float dropout_p) {
   const Workspace w = layout(B, Hq, Hkv, Nq, Nkv, D);
   if (workspace == nullptr || workspace_bytes < w.total || ((uintptr_t)workspace & 255))
     return bfail(FFPA_ERR_VALUE, "workspace must be 256-byte aligned and hold ffpa_bwd_workspace_size() = %zu bytes",
@@ -270,6 +281,11 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
       const uint16_t* Kh = (const uint16_t*)k + (b * Hkv + hk) * kh;
       const uint16_t* Vh = (const uint16_t*)v + (b * Hkv + hk) * kh;
       GroupArgs ga{(int)b, (int)hk, G, (int)Hq, n, m, (float)sc, is_causal, is_fp16, lse, delta, nullptr, 0, 0, 0, 0};
+      if (keep != nullptr) {
+        ga.keep = keep;
+        ga.keep_w = (int)((Nkv + 31) / 32);
+        ga.drop_scale = (float)(1.0 / (1.0 - (double)dropout_p));
+      }
       if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
         ga.mask = mask->data;
         ga.mask_kind = mask->kind;
@@ -304,6 +320,28 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
     }
   }
   return FFPA_OK;
+}
+
+int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+             int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  const int st = bwd_check(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, workspace,
+                  workspace_bytes, stream, nullptr, 0.f);
+}
+
+int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, const uint32_t* keep,
+                     float dropout_p, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = bwd_check(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  if (!(dropout_p >= 0.f && dropout_p < 1.f)) return bfail(FFPA_ERR_VALUE, "dropout probability must lie in [0, 1)");
+  if (keep == nullptr || ((uintptr_t)keep & 3)) return bfail(FFPA_ERR_VALUE, "keep must be non-null and 4-byte aligned");
+  return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, workspace,
+                  workspace_bytes, stream, keep, dropout_p);
 }
 
 }  // extern "C"

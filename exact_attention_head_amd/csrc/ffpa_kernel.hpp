@@ -1088,8 +1088,15 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     // packed batches and strided layouts take the runtime-layout variants (for packed batches the
     // lengths live on the device, so whole and partial tiles are told apart in the kernel)
     const bool runtime_layout = packed || a.strided;
-    if (drop)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowDrop, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    if (drop && plain && !a.causal && a.Nkv % 64 == 0)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+    else if (drop && plain)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+    else if (drop)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
     else if (runtime_layout && plain)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (runtime_layout)

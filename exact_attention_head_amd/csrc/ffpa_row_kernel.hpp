@@ -206,10 +206,11 @@ constexpr int row_load_slot(int bs, int q, int step, int MPT) {
 // diagonal, a partial last tile) explicit, in two successive loops), kRowMaskF32 (every tile
 // explicit, with an fp32 additive mask whose rows are
 // staged through LDS: whole 128-byte lines per direct-to-LDS load, one tile ahead, instead of
-// scattered 16-byte loads per lane), kRowDrop (kRowGeneral with attention dropout: each weight
-// whose keep bit is clear is left out of P V, and O is scaled by 1 / (1 - p) at the end; the row
-// sums and the LSE keep every weight).  The launcher picks the variant.
-enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3, kRowDrop = 4 };
+// scattered 16-byte loads per lane).  The launcher picks the variant.  Attention dropout is a
+// separate flag (DROP) on the raw, split and general variants: each weight whose keep bit is clear is
+// left out of P V, and O is scaled by 1 / (1 - p) at the end; the row sums and the LSE keep every
+// weight.
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3 };
 
 // Loads (per wave) issued in slot x of a tile: load q of the refill after the barrier at slot
 // e*EM - PF goes to row_load_slot(...).
@@ -245,7 +246,7 @@ constexpr bool row_barrier_within(int first, int last, int EM, int PF) {
 // VL: runtime layouts: a packed variable-length batch (FwdArgs::cu_q: per-sequence lengths, offsets
 // and LSE layout) or a strided dense one, both with runtime strides; the contiguous dense layout
 // keeps them compile-time.
-template <typename T, int D, int MODE, bool VL>
+template <typename T, int D, int MODE, bool VL, bool DROP = false>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   using RT = RowTiling<D>;
   using E = Elem<T>;
@@ -269,8 +270,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   static_assert(1 + (NL - 1) * LSTEP < EM, "the loads after a barrier end before the next one");
 
   constexpr bool MASK_LDS = MODE == kRowMaskF32;
-  constexpr bool DROP = MODE == kRowDrop;
-  static_assert(!DROP || !VL, "dropout runs on the contiguous dense layout");
+  static_assert(!DROP || (!VL && MODE != kRowMaskF32), "dropout runs on the contiguous dense layout");
   constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // the partner's partial of block 0 is read (after a barrier, complete PF products later) before
@@ -775,7 +775,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   };
   if constexpr (MODE == kRowRaw) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
-  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32 || MODE == kRowDrop) {
+  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
   } else {
     static_assert(MODE == kRowSplit, "tile mode");

@@ -211,6 +211,22 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/*
+ * ffpa_bwd_dropout -- the backward of ffpa_fwd_dropout: as ffpa_bwd, with
+ * the forward's keep words `keep` (device, [B, Hq, Nq, ceil(Nkv / 32)]
+ * uint32, read only) and dropout_p.  With M = keep / (1 - dropout_p) a
+ * constant, the output was O = (P * M) V, so
+ *   dV = sum over the group of (P * M)^T dout,
+ *   dS = P * (dout V^T * M - Delta) with Delta[r] = <dout[r], o[r]>,
+ * and dQ, dK as in ffpa_bwd.  `o` is the dropout forward's output.  Errors
+ * as for ffpa_bwd, plus FFPA_ERR_VALUE for dropout_p outside [0, 1) or a
+ * null or misaligned keep.  The workspace is ffpa_bwd_workspace_size().
+ */
+int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, const uint32_t* keep,
+                     float dropout_p, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of workspace ffpa_bwd needs for these sizes: about 10 * (Hq/Hkv) *
  * Nq * Nkv + 4 * B * Hq * Nq + 8 * (Hq/Hkv) * Nkv * D.  0 for invalid sizes.
  * Host-only. */

@@ -252,7 +252,7 @@ BWD_FAULT_GQA_LAST_HEAD = 3   # a KV head's gradient from the last head of its g
 
 
 def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is_causal: bool = False,
-                       fault: int = BWD_FAULT_NONE):
+                       fault: int = BWD_FAULT_NONE, keep_bits=None, dropout_p: float = 0.0):
     """Gradients of the attention output with respect to Q, K and V in fp64 (the mask is a constant).
 
     q [B, Hq, Nq, D]; k, v [B, Hkv, Nkv, D]; do (the output's gradient) like q; torch bf16/fp16 or
@@ -264,6 +264,10 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
         dQ = scale dS K,   dK = scale * sum over the group's heads of dS^T Q
 
     A row with every key excluded contributes nothing.  Returns (dQ, dK, dV) as float64 arrays.
+
+    With dropout (keep_bits [B, Hq, Nq, ceil(Nkv / 32)] uint32 words, ``oracle.philox`` layout, and
+    dropout_p), the output is O = (P * M) V with M = keep / (1 - p) a constant; then
+    dV = sum of (P * M)^T dO and the softmax's Jacobian is applied to dP = (dO V^T) * M.
     """
     import torch
 
@@ -285,6 +289,11 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
+    Mdrop = None
+    if keep_bits is not None:
+        from .philox import keep_matrix
+
+        Mdrop = keep_matrix(keep_bits, Nkv) / (1.0 - float(np.float32(dropout_p)))  # [B, Hq, Nq, Nkv]
     for b in range(B):
         for h in range(Hq):
             hk = h // G
@@ -297,11 +306,12 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
             e = np.exp(s - mx)
             P = e / np.where(live, e.sum(axis=1), 1.0)[:, None]
             P[~live] = 0.0
-            dP = dO[b, h] @ V[b, hk].T
+            Md = 1.0 if Mdrop is None else Mdrop[b, h]
+            dP = (dO[b, h] @ V[b, hk].T) * Md
             dS = P * dP if fault == BWD_FAULT_NO_DELTA else P * (dP - (P * dP).sum(axis=1, keepdims=True))
             dQ[b, h] = scale * (dS @ K[b, hk])
             dK[b, hk] += (1.0 if fault == BWD_FAULT_DK_UNSCALED else scale) * (dS.T @ Q[b, h])
-            dV[b, hk] += P.T @ dO[b, h]
+            dV[b, hk] += (P * Md).T @ dO[b, h]
     return dQ, dK, dV
 
 

@@ -170,3 +170,65 @@ def test_dropout_argument_errors():
     st = ffpa.ffpa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), None, torch.empty_like(q).data_ptr(), None,
                                1, 1, 1, 8, 8, 64, math.nan, False, ffpa.FFPA_BF16, None, 0.5, None)
     assert st == 2  # null keep
+
+
+# ---- the backward of the forward with dropout (ffpa_bwd_dropout), against the oracle's gradients.
+# Bar of the plain backward: P and dS rounded once to 16 bits, the outputs once more; rel-L2 <= 1e-2
+# and a largest element error <= 2e-2 of the largest reference magnitude.
+def _bwd_compare(got, want, name):
+    m = {}
+    for nm, g, w in zip(("dq", "dk", "dv"), got, want):
+        g = g.double().numpy()
+        assert np.isfinite(g).all(), f"non-finite values in {nm}"
+        rel = float(np.linalg.norm(g - w) / max(np.linalg.norm(w), 1e-30))
+        mx = float(np.abs(g - w).max() / max(np.abs(w).max(), 1e-30))
+        m[nm] = dict(rel_l2=rel, max_rel=mx)
+        assert rel <= 1e-2 and mx <= 2e-2, (nm, m)
+    _log(name, m)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("D", [128, 512, 576, 1024])
+def test_backward_dropout(D, causal):
+    B, Hq, Hkv, Nq, Nkv, p = 1, 4, 2, 96, 160, 0.2
+    q, k, v = W.random_qkv(B, Hq, Hkv, Nq, Nkv, D, seed=31 + D)
+    do = torch.randn(B, Hq, Nq, D, generator=torch.Generator().manual_seed(D)).to(torch.bfloat16)
+    words = dropout_keep_bits(B, Hq, Nq, Nkv, p, seed=D + 5)
+    keep = _as_int32(words).to(DEV)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = ffpa.attn(qd, kd, vd, dropout_p=p, dropout_keep=keep, is_causal=causal, enable_gqa=True,
+                       return_lse=True)
+    got = ffpa.attn_backward(qd, kd, vd, o, dod, lse, is_causal=causal, dropout_p=p, dropout_keep=keep)
+    torch.cuda.synchronize()
+    want = oracle.attention_backward(q, k, v, do, is_causal=causal, keep_bits=words, dropout_p=p)
+    _bwd_compare([t.cpu() for t in got], want, f"backward D={D} causal={causal}")
+
+
+def test_backward_dropout_with_mask():
+    B, Hq, Nq, Nkv, D, p = 2, 2, 64, 100, 256, 0.3
+    q, k, v = W.random_qkv(B, Hq, Hq, Nq, Nkv, D, seed=41)
+    do = torch.randn(B, Hq, Nq, D, generator=torch.Generator().manual_seed(41)).to(torch.bfloat16)
+    mask = torch.randn(B, 1, Nq, Nkv, generator=torch.Generator().manual_seed(42))
+    words = dropout_keep_bits(B, Hq, Nq, Nkv, p, seed=43)
+    keep = _as_int32(words).to(DEV)
+    qd, kd, vd, dod, md = (t.to(DEV) for t in (q, k, v, do, mask))
+    o, lse = ffpa.attn(qd, kd, vd, attn_mask=md, dropout_p=p, dropout_keep=keep, return_lse=True)
+    got = ffpa.attn_backward(qd, kd, vd, o, dod, lse, attn_mask=md, dropout_p=p, dropout_keep=keep)
+    torch.cuda.synchronize()
+    want = oracle.attention_backward(q, k, v, do, mask=mask, keep_bits=words, dropout_p=p)
+    _bwd_compare([t.cpu() for t in got], want, "backward with mask")
+
+
+def test_autograd_with_dropout():
+    """attn_with_grad draws its keep words from the seed; the gradients match the oracle's for the
+    oracle's own words of that seed."""
+    B, Hq, Nq, Nkv, D, p, seed = 1, 2, 80, 130, 320, 0.25, 99
+    q, k, v = W.random_qkv(B, Hq, Hq, Nq, Nkv, D, seed=51)
+    do = torch.randn(B, Hq, Nq, D, generator=torch.Generator().manual_seed(52)).to(torch.bfloat16)
+    qd, kd, vd = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    o = ffpa.attn_with_grad(qd, kd, vd, dropout_p=p, dropout_seed=seed)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    words = dropout_keep_bits(B, Hq, Nq, Nkv, p, seed)
+    want = oracle.attention_backward(q, k, v, do, keep_bits=words, dropout_p=p)
+    _bwd_compare([qd.grad.cpu(), kd.grad.cpu(), vd.grad.cpu()], want, "autograd with dropout")

@@ -187,3 +187,58 @@ def test_dropout_unbiased():
 def test_dropout_planted_mistakes_are_caught():
     for fault in (oracle.DROP_FAULT_SCALE_BY_KEEP, oracle.DROP_FAULT_BIT_REVERSED, oracle.DROP_FAULT_LSE_DROPPED):
         assert not (pin_brute(fault) and pin_closed_forms(fault) and pin_unbiased(fault)), fault
+
+
+def _torch_dropout_grads(q, k, v, do, words, p, mask=None, is_causal=False):
+    """Autograd in float64 through softmax(scale q.k + bias) * keep / (1 - p) @ V (keep a constant),
+    with K/V repeated per group (repeat_interleave) for GQA."""
+    B, Hq, Nq, D = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    qd, kd, vd = (t.double().requires_grad_(True) for t in (q, k, v))
+    kr, vr = kd.repeat_interleave(G, dim=1), vd.repeat_interleave(G, dim=1)
+    s = (qd @ kr.transpose(-1, -2)) / math.sqrt(D)
+    if mask is not None:
+        s = s + mask.double()
+    if is_causal:
+        vis = torch.arange(Nkv).view(1, Nkv) <= torch.arange(Nq).view(Nq, 1) + (Nkv - Nq)
+        s = s.masked_fill(~vis, -math.inf)
+    Z = torch.from_numpy(keep_matrix(words, Nkv))
+    o = (torch.softmax(s, dim=-1) * Z / (1.0 - float(np.float32(p)))) @ vr
+    return [g.numpy() for g in torch.autograd.grad(o, (qd, kd, vd), do.double())]
+
+
+def pin_backward_dropout(fault=oracle.BWD_FAULT_NONE):
+    ok = True
+    g = torch.Generator().manual_seed(31)
+    for (B, Hq, Hkv, Nq, Nkv, D, causal, p, seed) in [(1, 2, 2, 5, 40, 8, False, 0.3, 1),
+                                                      (2, 4, 2, 4, 9, 8, True, 0.5, 2)]:
+        q, k, v = random_qkv(B, Hq, Hkv, Nq, Nkv, D, seed=seed)
+        do = torch.randn(B, Hq, Nq, D, generator=g).to(torch.bfloat16)
+        words = dropout_keep_bits(B, Hq, Nq, Nkv, p, seed=seed + 3)
+        mask = None if causal else torch.randn(B, 1, Nq, Nkv, generator=g)
+        want = _torch_dropout_grads(q, k, v, do, words, p, mask=mask, is_causal=causal)
+        got = oracle.attention_backward(q, k, v, do, mask=mask, is_causal=causal, fault=fault, keep_bits=words,
+                                        dropout_p=p)
+        for a, b in zip(got, want):
+            ok &= bool(np.all(np.abs(a - b) <= 1e-10 * max(1.0, np.abs(b).max())))
+    return ok
+
+
+def test_backward_dropout_against_autograd():
+    assert pin_backward_dropout()
+
+
+def test_backward_dropout_all_kept_at_zero_p():
+    q, k, v = random_qkv(1, 2, 1, 6, 70, 16, seed=4)
+    do = torch.randn(1, 2, 6, 16, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    ones = np.full((1, 2, 6, 3), 0xFFFFFFFF, dtype=np.uint32)
+    plain = oracle.attention_backward(q, k, v, do)
+    drop = oracle.attention_backward(q, k, v, do, keep_bits=ones, dropout_p=0.0)
+    for a, b in zip(plain, drop):
+        assert np.array_equal(a, b)
+
+
+def test_backward_dropout_planted_mistakes_are_caught():
+    for fault in (oracle.BWD_FAULT_NO_DELTA, oracle.BWD_FAULT_DK_UNSCALED, oracle.BWD_FAULT_GQA_LAST_HEAD):
+        assert not pin_backward_dropout(fault), fault
