@@ -1085,6 +1085,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     const bool staged_mask = a.mask_kind == kMaskAddF32 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
                              a.msq % 32 == 0 &&
                              ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq * 4 + (int64_t)a.Nkv * 4 < (1LL << 31);
+    // the same for a boolean byte mask (4-byte aligned row starts for the 4-byte loads)
+    const bool staged_bool = a.mask_kind == kMaskBoolU8 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
+                             a.msq % 32 == 0 &&
+                             ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq + (int64_t)a.Nkv < (1LL << 31);
     // packed batches and strided layouts take the runtime-layout variants (for packed batches the
     // lengths live on the device, so whole and partial tiles are told apart in the kernel)
     const bool runtime_layout = packed || a.strided;
@@ -1104,6 +1108,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
                          a);
     else if (staged_mask)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+    else if (staged_bool)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskU8, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                          a);
     else if (plain && !a.causal && a.Nkv % 64 == 0)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

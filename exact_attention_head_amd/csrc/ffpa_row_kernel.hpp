@@ -206,11 +206,12 @@ constexpr int row_load_slot(int bs, int q, int step, int MPT) {
 // diagonal, a partial last tile) explicit, in two successive loops), kRowMaskF32 (every tile
 // explicit, with an fp32 additive mask whose rows are
 // staged through LDS: whole 128-byte lines per direct-to-LDS load, one tile ahead, instead of
-// scattered 16-byte loads per lane).  The launcher picks the variant.  Attention dropout is a
+// scattered 16-byte loads per lane), kRowMaskU8 (the same staging for a boolean byte mask: 32-byte
+// row blocks, a zero byte excludes the key).  The launcher picks the variant.  Attention dropout is a
 // separate flag (DROP) on the raw, split and general variants: each weight whose keep bit is clear is
 // left out of P V, and O is scaled by 1 / (1 - p) at the end; the row sums and the LSE keep every
 // weight.
-enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3 };
+enum RowMode { kRowGeneral = 0, kRowRaw = 1, kRowSplit = 2, kRowMaskF32 = 3, kRowMaskU8 = 4 };
 
 // Loads (per wave) issued in slot x of a tile: load q of the refill after the barrier at slot
 // e*EM - PF goes to row_load_slot(...).
@@ -269,8 +270,11 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   constexpr int LSTEP = row_load_step(EM, NL);
   static_assert(1 + (NL - 1) * LSTEP < EM, "the loads after a barrier end before the next one");
 
-  constexpr bool MASK_LDS = MODE == kRowMaskF32;
-  static_assert(!DROP || (!VL && MODE != kRowMaskF32), "dropout runs on the contiguous dense layout");
+  constexpr bool MASK_LDS = MODE == kRowMaskF32 || MODE == kRowMaskU8;  // staged mask rows
+  constexpr bool MASK_U8 = MODE == kRowMaskU8;
+  constexpr int MESZ = MASK_U8 ? 1 : 4;  // bytes per staged mask element
+  constexpr int MROWB = 32 * MESZ;       // bytes of one row's 32-key block
+  static_assert(!DROP || (!VL && !MASK_LDS), "dropout runs on the contiguous dense layout");
   constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // the partner's partial of block 0 is read (after a barrier, complete PF products later) before
@@ -477,32 +481,37 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const uint32_t ex_mine = ring_addr + RT::RING + wave * 4096 + lane * 16;
   const uint32_t ex_partner = ring_addr + RT::RING + (wave ^ 1) * 4096 + lane * 16;
 
-  // ---- staged fp32 mask: block kb of the workgroup's rows at MASK_OFF + kb * BR * 128, row r's 32
-  // keys as eight 16-byte chunks swizzled like the K/V sub-tiles.  Wave w loads rows 8(w + 4i) ..
-  // +7 (i < BR/32); keys are whole tiles (Nkv % 64 == 0), rows past Nq read as zero through the
-  // descriptor (their results are never stored).
+  // ---- staged mask: block kb of the workgroup's rows at MASK_OFF + kb * BR * MROWB, row r's 32 keys
+  // in MROWB bytes, as eight chunks of four keys (one per lane of a load).  fp32: 16-byte chunks
+  // swizzled like the K/V sub-tiles.  Bytes: 4-byte chunks reordered so that chunk position
+  // 4 hi + g holds keys 8g + 4hi .. +3, i.e. the 16 keys of one half-wave are one 16-byte read.
+  // Wave w loads rows 8(w + 4i) .. +7 (i < BR/32); keys are whole tiles (Nkv % 64 == 0), rows past
+  // Nq read as zero through the descriptor (their results are never stored).
   constexpr int MASK_OFF = RT::RING + RT::EXCH;
   constexpr int MLOADS = BR / 32;  // loads per wave per block
-  const int mask_bytes = MASK_LDS ? (int)(((int64_t)(Nq - 1) * a.msq + Nkv) * 4) : 0;
+  const int mask_bytes = MASK_LDS ? (int)(((int64_t)(Nq - 1) * a.msq + Nkv) * MESZ) : 0;
   const __amdgpu_buffer_rsrc_t rsrc_m =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const float*)a.mask + (MASK_LDS ? mask_bh : 0)), (short)0,
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.mask + (MASK_LDS ? mask_bh * MESZ : 0)), (short)0,
                                         mask_bytes, 0x00020000);
   const int mrow0 = 8 * wave + (lane >> 3);  // row of load i: mrow0 + 32 i (same swizzle phase)
-  const uint32_t mvoff = (uint32_t)(((int64_t)(r0 + mrow0) * a.msq + ((lane & 7) ^ pi7((mrow0 >> 1) & 7)) * 4) * 4);
-  const uint32_t mrow_step = (uint32_t)(32 * a.msq * 4);
+  const int mchunk = MASK_U8 ? 2 * (lane & 3) + ((lane >> 2) & 1) : ((lane & 7) ^ pi7((mrow0 >> 1) & 7));
+  const uint32_t mvoff = (uint32_t)(((int64_t)(r0 + mrow0) * a.msq + mchunk * 4) * MESZ);
+  const uint32_t mrow_step = (uint32_t)(32 * a.msq * MESZ);
   // rows of tile jt's block kb into the staging buffer
   auto issue_mask = [&](int jt, int kb) {
-    const uint32_t kofs = (uint32_t)((jt * BC + 32 * kb) * 4);
+    const uint32_t kofs = (uint32_t)((jt * BC + 32 * kb) * MESZ);
 #pragma unroll
-    for (int i = 0; i < MLOADS; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_m,
-                                               (FFPA_LDS void*)(smem + MASK_OFF + kb * BR * 128 + (wave + 4 * i) * 1024),
-                                               16, mvoff + i * mrow_step + kofs, 0, 0, 0);
+    for (int i = 0; i < MLOADS; ++i) {
+      FFPA_LDS void* dst = (FFPA_LDS void*)(smem + MASK_OFF + kb * BR * MROWB + (wave + 4 * i) * 8 * MROWB);
+      // bytes per lane: a literal (the builtin checks it before the template is instantiated)
+      if constexpr (MASK_U8) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_m, dst, 4, mvoff + i * mrow_step + kofs, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_m, dst, 16, mvoff + i * mrow_step + kofs, 0, 0, 0);
+    }
   };
-  // this lane's 16 biases of block kb (keys 8g + 4hi + e): 4 reads, complete once a fragment read
-  // issued after them has been waited for
+  // this lane's 16 biases of block kb (keys 8g + 4hi + e): 4 reads (bytes: 1), complete once a
+  // fragment read issued after them has been waited for
   const int mr = rg * 32 + l32;  // the lane's row within the workgroup
-  const uint32_t mrd = ring_addr + MASK_OFF + mr * 128;
+  const uint32_t mrd = ring_addr + MASK_OFF + mr * MROWB;
   const int mswz = pi7((mr >> 1) & 7);
 
   // ---- prologue: the first tile's mask rows and epochs 0 .. LA-1 in flight, epoch 0 (and the
@@ -589,7 +598,14 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
             float x = s_acc[kb][4 * g + e];
             if constexpr (DG == 2) x += part[kb][g][e];
             x *= a.scale_log2;
-            if (has_mask) x = __builtin_fmaf(bias[kb][g][e], kLog2e, x);
+            if constexpr (MASK_U8) {
+              // byte e of word g: nonzero takes part (through a scalar: a bit cast of the vector
+              // element itself would read element 0)
+              const float wf = bias[kb][0][g];
+              x = ((__builtin_bit_cast(uint32_t, wf) >> (8 * e)) & 0xffu) ? x : kNegInf;
+            } else if (has_mask) {
+              x = __builtin_fmaf(bias[kb][g][e], kLog2e, x);
+            }
             if (edge) x = 8 * g + e > lim ? kNegInf : x;
             mx = __builtin_fmaxf(mx, x);
             s_acc[kb][4 * g + e] = x;
@@ -738,11 +754,15 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb) {
           const int first = row_sm_first(kb, DG, PH, EM, PF);
           if (m == first - PF) {
-            const uint32_t base = mrd + kb * BR * 128;
-            bias[kb][0] = lds_read_f4_async<0>(base + ((0 + hi) ^ mswz) * 16);
-            bias[kb][1] = lds_read_f4_async<0>(base + ((2 + hi) ^ mswz) * 16);
-            bias[kb][2] = lds_read_f4_async<0>(base + ((4 + hi) ^ mswz) * 16);
-            bias[kb][3] = lds_read_f4_async<0>(base + ((6 + hi) ^ mswz) * 16);
+            const uint32_t base = mrd + kb * BR * MROWB;
+            if constexpr (MASK_U8) {
+              bias[kb][0] = lds_read_f4_async<0>(base + hi * 16);  // key bytes, as four raw words
+            } else {
+              bias[kb][0] = lds_read_f4_async<0>(base + ((0 + hi) ^ mswz) * 16);
+              bias[kb][1] = lds_read_f4_async<0>(base + ((2 + hi) ^ mswz) * 16);
+              bias[kb][2] = lds_read_f4_async<0>(base + ((4 + hi) ^ mswz) * 16);
+              bias[kb][3] = lds_read_f4_async<0>(base + ((6 + hi) ^ mswz) * 16);
+            }
           }
           int nb = first;
           while ((nb + PF) % EM != 0) ++nb;
@@ -775,7 +795,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   };
   if constexpr (MODE == kRowRaw) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
-  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32) {
+  } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32 || MODE == kRowMaskU8) {
     for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
   } else {
     static_assert(MODE == kRowSplit, "tile mode");

@@ -108,6 +108,29 @@ def test_fp32_mask_staged_shapes(shape, D):
     _log(f"staged mask shape {shape} D={D}", compare(o, l, q, k, v, mask=mask))
 
 
+@pytest.mark.parametrize("shape", [(130, 256), (1, 1, 130, 256), (2, 1, 1, 256), (1, 3, 1, 256), (2, 3, 130, 256)])
+@pytest.mark.parametrize("D", [128, 256, 512, 1024])
+def test_bool_mask_staged_shapes(shape, D):
+    """Boolean byte masks over whole 64-key tiles (staged through LDS by the row kernel), with
+    broadcast batch, head and row strides and a partial last query tile."""
+    q, k, v = _case(2, 3, 3, 130, 256, D, seed=D + 2 * len(shape))
+    mask = _bias(shape, seed=D * 11 + sum(shape), drop=0.3) > -0.5
+    mask[..., 0] = True
+    o, l = run_gpu(q, k, v, mask=mask)
+    _log(f"staged bool mask shape {shape} D={D}", compare(o, l, q, k, v, mask=mask))
+
+
+@pytest.mark.parametrize("D", [64, 512, 1024])
+def test_bool_mask_staged_dead_rows(D):
+    """Rows whose mask admits no key get O = 0 and LSE = -inf on the staged path too."""
+    q, k, v = _case(1, 2, 2, 100, 128, D, seed=D + 77)
+    mask = _bias((1, 2, 100, 128), seed=D + 78, drop=0.3) > -0.5
+    mask[:, :, ::7] = False
+    o, l = run_gpu(q, k, v, mask=mask)
+    _log(f"staged bool mask dead rows D={D}", compare(o, l, q, k, v, mask=mask))
+    assert torch.all(l[:, :, ::7] == -math.inf) and torch.all(o[:, :, ::7] == 0)
+
+
 @pytest.mark.parametrize("kind", ["bool", "f32"])
 @pytest.mark.parametrize("D", [64, 256, 512, 1024])
 @pytest.mark.parametrize("Nq,Nkv", [(130, 200), (64, 64), (100, 333)])
