@@ -17,10 +17,14 @@
  * the page's varlen entry returns.  A row whose keys are all excluded gets
  * O = 0 and LSE = -inf.
  *
- * Every computation step runs in hand-written HIP kernels on the caller's
- * stream.  The library allocates nothing, keeps no pointer after a call
- * returns and needs no workspace; its only state is a thread-local error
- * message, so calls from several host threads are safe.
+ * Every step of the forward entries and of the dropout keep-bit generator
+ * runs in hand-written HIP kernels on the caller's stream; they allocate
+ * nothing, keep no pointer after a call returns and need no workspace.  The
+ * backward entries (ffpa_bwd, ffpa_bwd_dropout) run their matrix products as
+ * ROCm library GEMMs over a caller-provided workspace, and the GEMM library
+ * keeps one handle per device, created on first use.  Apart from those
+ * handles the only state is a thread-local error message, so calls from
+ * several host threads are safe.
  */
 #ifndef FFPA_H_
 #define FFPA_H_
