@@ -1,7 +1,9 @@
 // Backward of the attention forward (ffpa-attn "API Reference": ffpa_attn_func's backward, which
 // the pages run as SDPA's backward): dQ, dK, dV from Q, K, V, O, dO and the forward's fp32 LSE.
 //
-// One KV group at a time (a KV head with its G query heads), over a caller-provided workspace:
+// One chunk of query heads at a time, over a caller-provided workspace: a KV group (a KV head with
+// its G query heads), or, without grouping (G = 1), as many consecutive heads as the workspace
+// bound allows, so that every product is one strided-batched call over the chunk:
 //   Delta = rowsum(dO * O)                         (HIP kernel, once for every row)
 //   S  = Q K^T                    [G, Nq, Nkv] f32 (library GEMM)
 //   P  = exp(scale S + bias - LSE), 0 where excluded; kept in f32 and as a 16-bit copy (HIP kernel)
@@ -84,8 +86,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restri
   if (lane == 0) delta[row] = acc;
 }
 
+// A chunk of nh consecutive query heads (flat index b * Hq + h), the first being fh0.
 struct GroupArgs {
-  int b, hk, G, Hq, Nq, Nkv;
+  int fh0, nh, Hq, Nq, Nkv;
   float scale;
   int causal, is_fp16;
   const float* lse;    // [B, Hq, Nq]
@@ -99,43 +102,44 @@ struct GroupArgs {
 };
 
 // The dropout factor M of (row r of query head h, key k): keep bit / (1 - p).
-__device__ inline float drop_factor(const GroupArgs& g, int h, int r, int k) {
-  const uint32_t w = g.keep[(((int64_t)g.b * g.Hq + h) * g.Nq + r) * g.keep_w + (k >> 5)];
+__device__ inline float drop_factor(const GroupArgs& g, int fh, int r, int k) {
+  const uint32_t w = g.keep[((int64_t)fh * g.Nq + r) * g.keep_w + (k >> 5)];
   return ((w >> (k & 31)) & 1u) ? g.drop_scale : 0.f;
 }
 
-// P = exp(scale S + bias - LSE) over [G, Nq, Nkv] in place (f32), plus its 16-bit copy.
+// P = exp(scale S + bias - LSE) over [nh, Nq, Nkv] in place (f32), plus its 16-bit copy.
 __global__ __launch_bounds__(256) void bwd_probs_kernel(float* __restrict__ s, uint16_t* __restrict__ p16, GroupArgs g) {
-  const int64_t total = (int64_t)g.G * g.Nq * g.Nkv;
+  const int64_t total = (int64_t)g.nh * g.Nq * g.Nkv;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const int k = (int)(i % g.Nkv);
   const int64_t gr = i / g.Nkv;
   const int r = (int)(gr % g.Nq);
-  const int h = g.hk * g.G + (int)(gr / g.Nq);
-  const float lse = g.lse[((int64_t)g.b * g.Hq + h) * g.Nq + r];
+  const int fh = g.fh0 + (int)(gr / g.Nq);  // flat query head
+  const int b = fh / g.Hq, h = fh % g.Hq;
+  const float lse = g.lse[(int64_t)fh * g.Nq + r];
   float p = 0.f;
   const bool visible = !g.causal || k <= r + (g.Nkv - g.Nq);
   if (visible && lse != -INFINITY) {
     float x = g.scale * s[i];
-    if (g.mask_kind != FFPA_MASK_NONE) x += mask_bias(g.mask, g.mask_kind, g.b * g.msb + h * g.msh + r * g.msq + k);
+    if (g.mask_kind != FFPA_MASK_NONE) x += mask_bias(g.mask, g.mask_kind, b * g.msb + h * g.msh + r * g.msq + k);
     p = exp2f((x - lse) * kLog2eB);
   }
   s[i] = p;
-  p16[i] = store16(g.keep != nullptr ? p * drop_factor(g, h, r, k) : p, g.is_fp16);
+  p16[i] = store16(g.keep != nullptr ? p * drop_factor(g, fh, r, k) : p, g.is_fp16);
 }
 
-// dS = scale P (dP - Delta) as 16-bit, over [G, Nq, Nkv].
+// dS = scale P (dP - Delta) as 16-bit, over [nh, Nq, Nkv].
 __global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ p, const float* __restrict__ dp,
                                                      uint16_t* __restrict__ ds16, GroupArgs g) {
-  const int64_t total = (int64_t)g.G * g.Nq * g.Nkv;
+  const int64_t total = (int64_t)g.nh * g.Nq * g.Nkv;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
   const int64_t gr = i / g.Nkv;
   const int r = (int)(gr % g.Nq);
-  const int h = g.hk * g.G + (int)(gr / g.Nq);
-  const float dl = g.delta[((int64_t)g.b * g.Hq + h) * g.Nq + r];
-  const float dpm = g.keep != nullptr ? dp[i] * drop_factor(g, h, r, (int)(i % g.Nkv)) : dp[i];
+  const int fh = g.fh0 + (int)(gr / g.Nq);  // flat query head
+  const float dl = g.delta[(int64_t)fh * g.Nq + r];
+  const float dpm = g.keep != nullptr ? dp[i] * drop_factor(g, fh, r, (int)(i % g.Nkv)) : dp[i];
   ds16[i] = store16(g.scale * p[i] * (dpm - dl), g.is_fp16);
 }
 
@@ -168,8 +172,19 @@ struct Workspace {
   size_t delta, s, dp, p16, dk, dv, total;
 };
 
-Workspace layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D) {
+// Query heads per chunk: a KV group (G > 1), or without grouping as many heads as keep the chunk's
+// score matrices and accumulators within 4 GiB (at least one).
+int64_t chunk_heads(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D) {
   const int64_t G = Hq / Hkv;
+  if (G > 1) return G;
+  const int64_t per_head = Nq * Nkv * 10 + Nkv * D * 8;
+  int64_t n = (4LL << 30) / per_head;
+  n = n < 1 ? 1 : n;
+  return n < B * Hq ? n : B * Hq;
+}
+
+Workspace layout(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D) {
+  const int64_t G = chunk_heads(B, Hq, Hkv, Nq, Nkv, D);  // heads per chunk
   Workspace w{};
   size_t off = 0;
   w.delta = off;
@@ -239,6 +254,7 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   const hipStream_t s = (hipStream_t)stream;
   const int is_fp16 = dtype == FFPA_FP16;
   const int G = (int)(Hq / Hkv);
+  const int64_t chunk = chunk_heads(B, Hq, Hkv, Nq, Nkv, D);
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   char* ws = (char*)workspace;
   float* delta = (float*)(ws + w.delta);
@@ -271,53 +287,70 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
                                            scs, C, ct, ldc, scs, batch, f32, rocblas_gemm_algo_standard, 0, 0);
   };
   const rocblas_operation N_ = rocblas_operation_none, T_ = rocblas_operation_transpose;
-  const unsigned eblocks = (unsigned)(((int64_t)G * sq + 255) / 256);
-  for (int64_t b = 0; b < B; ++b) {
-    for (int64_t hk = 0; hk < Hkv; ++hk) {
-      const int64_t h0 = hk * G;
-      const uint16_t* Qg = (const uint16_t*)q + (b * Hq + h0) * qh;
-      const uint16_t* dOg = (const uint16_t*)dout + (b * Hq + h0) * qh;
-      uint16_t* dQg = (uint16_t*)dq + (b * Hq + h0) * qh;
-      const uint16_t* Kh = (const uint16_t*)k + (b * Hkv + hk) * kh;
-      const uint16_t* Vh = (const uint16_t*)v + (b * Hkv + hk) * kh;
-      GroupArgs ga{(int)b, (int)hk, G, (int)Hq, n, m, (float)sc, is_causal, is_fp16, lse, delta, nullptr, 0, 0, 0, 0};
-      if (keep != nullptr) {
-        ga.keep = keep;
-        ga.keep_w = (int)((Nkv + 31) / 32);
-        ga.drop_scale = (float)(1.0 / (1.0 - (double)dropout_p));
-      }
-      if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
-        ga.mask = mask->data;
-        ga.mask_kind = mask->kind;
-        ga.msb = mask->stride_b;
-        ga.msh = mask->stride_h;
-        ga.msq = mask->stride_q;
-      }
-      rocblas_status r;
-      // S^T[Nkv x Nq] = K Q^T  (per head of the group; K shared: stride 0)
-      r = gemm(T_, N_, m, n, d, Kh, t16, d, 0, Qg, t16, d, qh, S, f32, m, sq, G);
-      if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM S failed (%d)", (int)r);
-      hipLaunchKernelGGL(bwd_probs_kernel, dim3(eblocks), dim3(256), 0, s, S, P16, ga);
-      // dV_g^T[D x Nkv] = dO^T P
-      r = gemm(N_, T_, d, m, n, dOg, t16, d, qh, P16, t16, m, sq, dVacc, f32, d, kh, G);
-      if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dV failed (%d)", (int)r);
-      // dP^T[Nkv x Nq] = V dO^T
-      r = gemm(T_, N_, m, n, d, Vh, t16, d, 0, dOg, t16, d, qh, dP, f32, m, sq, G);
-      if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dP failed (%d)", (int)r);
-      hipLaunchKernelGGL(bwd_ds_kernel, dim3(eblocks), dim3(256), 0, s, S, dP, P16, ga);
-      // dQ^T[D x Nq] = K^T dS^T, written in the output dtype
-      r = gemm(N_, N_, d, n, m, Kh, t16, d, 0, P16, t16, m, sq, dQg, t16, d, qh, G);
-      if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dQ failed (%d)", (int)r);
-      // dK_g^T[D x Nkv] = Q^T dS
-      r = gemm(N_, T_, d, m, n, Qg, t16, d, qh, P16, t16, m, sq, dKacc, f32, d, kh, G);
-      if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dK failed (%d)", (int)r);
-      const unsigned kblocks = (unsigned)((kh + 255) / 256);
-      hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(kblocks), dim3(256), 0, s, dKacc,
-                         (uint16_t*)dk + (b * Hkv + hk) * kh, kh, G, is_fp16);
-      hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(kblocks), dim3(256), 0, s, dVacc,
-                         (uint16_t*)dv + (b * Hkv + hk) * kh, kh, G, is_fp16);
-      if (hipGetLastError() != hipSuccess) return bfail(FFPA_ERR_HIP, "kernel launch failed");
+  // Chunks: one KV group (G > 1; its K/V shared by the group's heads through a zero stride), or,
+  // without grouping, `chunk` consecutive heads (head u reads KV head u, stride kh).
+  const int64_t units = B * Hq;  // flat query heads b * Hq + h
+  const int64_t step = G > 1 ? G : chunk;
+  const int64_t kvs = G > 1 ? 0 : kh;
+  for (int64_t u0 = 0; u0 < units; u0 += step) {
+    const int nh = (int)(units - u0 < step ? units - u0 : step);
+    const int64_t fkv = u0 / G;  // flat KV head of the chunk's first query head
+    const uint16_t* Qg = (const uint16_t*)q + u0 * qh;
+    const uint16_t* dOg = (const uint16_t*)dout + u0 * qh;
+    uint16_t* dQg = (uint16_t*)dq + u0 * qh;
+    const uint16_t* Kh = (const uint16_t*)k + fkv * kh;
+    const uint16_t* Vh = (const uint16_t*)v + fkv * kh;
+    GroupArgs ga{};
+    ga.fh0 = (int)u0;
+    ga.nh = nh;
+    ga.Hq = (int)Hq;
+    ga.Nq = n;
+    ga.Nkv = m;
+    ga.scale = (float)sc;
+    ga.causal = is_causal;
+    ga.is_fp16 = is_fp16;
+    ga.lse = lse;
+    ga.delta = delta;
+    if (keep != nullptr) {
+      ga.keep = keep;
+      ga.keep_w = (int)((Nkv + 31) / 32);
+      ga.drop_scale = (float)(1.0 / (1.0 - (double)dropout_p));
     }
+    if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
+      ga.mask = mask->data;
+      ga.mask_kind = mask->kind;
+      ga.msb = mask->stride_b;
+      ga.msh = mask->stride_h;
+      ga.msq = mask->stride_q;
+    }
+    const unsigned eblocks = (unsigned)(((int64_t)nh * sq + 255) / 256);
+    rocblas_status r;
+    // S^T[Nkv x Nq] = K Q^T  (per head of the chunk)
+    r = gemm(T_, N_, m, n, d, Kh, t16, d, kvs, Qg, t16, d, qh, S, f32, m, sq, nh);
+    if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM S failed (%d)", (int)r);
+    hipLaunchKernelGGL(bwd_probs_kernel, dim3(eblocks), dim3(256), 0, s, S, P16, ga);
+    // dV_h^T[D x Nkv] = dO^T P
+    r = gemm(N_, T_, d, m, n, dOg, t16, d, qh, P16, t16, m, sq, dVacc, f32, d, kh, nh);
+    if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dV failed (%d)", (int)r);
+    // dP^T[Nkv x Nq] = V dO^T
+    r = gemm(T_, N_, m, n, d, Vh, t16, d, kvs, dOg, t16, d, qh, dP, f32, m, sq, nh);
+    if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dP failed (%d)", (int)r);
+    hipLaunchKernelGGL(bwd_ds_kernel, dim3(eblocks), dim3(256), 0, s, S, dP, P16, ga);
+    // dQ^T[D x Nq] = K^T dS^T, written in the output dtype
+    r = gemm(N_, N_, d, n, m, Kh, t16, d, kvs, P16, t16, m, sq, dQg, t16, d, qh, nh);
+    if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dQ failed (%d)", (int)r);
+    // dK_h^T[D x Nkv] = Q^T dS
+    r = gemm(N_, T_, d, m, n, Qg, t16, d, qh, P16, t16, m, sq, dKacc, f32, d, kh, nh);
+    if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dK failed (%d)", (int)r);
+    // dK, dV: the group's G partials summed (G > 1), or the chunk's heads converted (G = 1)
+    const int64_t nout = G > 1 ? kh : (int64_t)nh * kh;
+    const int nsum = G > 1 ? G : 1;
+    const unsigned kblocks = (unsigned)((nout + 255) / 256);
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(kblocks), dim3(256), 0, s, dKacc, (uint16_t*)dk + fkv * kh, nout,
+                       nsum, is_fp16);
+    hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(kblocks), dim3(256), 0, s, dVacc, (uint16_t*)dv + fkv * kh, nout,
+                       nsum, is_fp16);
+    if (hipGetLastError() != hipSuccess) return bfail(FFPA_ERR_HIP, "kernel launch failed");
   }
   return FFPA_OK;
 }

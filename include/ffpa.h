@@ -204,7 +204,8 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
  *        bytes, owned by the caller; its contents are scratch
  *
  * The products run as library GEMMs (bf16/fp16 in, fp32 accumulate) on the
- * score matrix of one KV group at a time, held in the workspace; the softmax
+ * score matrices of one chunk of query heads at a time (a KV group, or
+ * several ungrouped heads), held in the workspace; the softmax
  * recompute, the Delta term and the group sums run in this library's kernels.
  * On the first call on a device the GEMM library creates a handle (and its own
  * device workspace), kept until the process ends; calls are serialised on it.
@@ -231,9 +232,11 @@ int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                      int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, const uint32_t* keep,
                      float dropout_p, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace ffpa_bwd needs for these sizes: about 10 * (Hq/Hkv) *
- * Nq * Nkv + 4 * B * Hq * Nq + 8 * (Hq/Hkv) * Nkv * D.  0 for invalid sizes.
- * Host-only. */
+/* Bytes of workspace ffpa_bwd and ffpa_bwd_dropout need for these sizes:
+ * about C * (10 * Nq * Nkv + 8 * Nkv * D) + 4 * B * Hq * Nq, where C, the
+ * query heads handled per step, is Hq/Hkv with grouped heads, and otherwise
+ * as many heads (at most B * Hq, at least one) as keep C * (10 * Nq * Nkv +
+ * 8 * Nkv * D) within 4 GiB.  0 for invalid sizes.  Host-only. */
 size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D);
 
 /* The host-side argument check ffpa_fwd performs, without enqueuing anything
