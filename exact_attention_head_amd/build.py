@@ -69,12 +69,16 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     tasks = [(os.path.join(CSRC, "ffpa_api.hip"), os.path.join(BUILD, "ffpa_api.o"), []),
              (os.path.join(CSRC, "ffpa_bwd.hip"), os.path.join(BUILD, "ffpa_bwd.o"), []),
              (os.path.join(CSRC, "ffpa_dropout.hip"), os.path.join(BUILD, "ffpa_dropout.o"), [])]
+    # per (element type, head dim): part 0 the launcher with the plain variants, 1 the dropout
+    # variants, 2 the staged-mask variants (compiled in parallel)
     for tag in ("Bf16", "Fp16"):
         for d in head_dims():
-            tasks.append((os.path.join(CSRC, "ffpa_inst.hip"), os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}.o"),
-                          [f"-DFFPA_INST_T={tag}", f"-DFFPA_INST_D={d}"]))
+            for part in (0, 1, 2):
+                tasks.append((os.path.join(CSRC, "ffpa_inst.hip"),
+                              os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}" + (f"_p{part}" if part else "") + ".o"),
+                              [f"-DFFPA_INST_T={tag}", f"-DFFPA_INST_D={d}", f"-DFFPA_INST_PART={part}"]))
     # largest kernels first
-    kd = lambda path: re.search(r"_d(\d+)\.o$", path)  # per-head-dim kernel objects
+    kd = lambda path: re.search(r"_d(\d+)(_p\d)?\.o$", path)  # per-head-dim kernel objects
     tasks.sort(key=lambda t: -int(kd(t[1]).group(1)) if kd(t[1]) else 0)
     resources = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:

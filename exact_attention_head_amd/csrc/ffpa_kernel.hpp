@@ -1062,6 +1062,42 @@ constexpr const char* kernel_name() {
   else return "ffpa_fwd_kernel";
 }
 
+// The row kernel's dropout and staged-mask variants, launched from launch_fwd.  Each group is
+// instantiated in a translation unit of its own (ffpa_inst.hip, FFPA_INST_PART), so that the
+// variants of one head dim compile in parallel.
+template <typename T, int D>
+hipError_t launch_fwd_drop(const FwdArgs& a, hipStream_t stream, long long blocks, bool plain) {
+  if constexpr (use_row_kernel<D>()) {
+    if (plain && !a.causal && a.Nkv % 64 == 0)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+    else if (plain)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+    else
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         stream, a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_staged(const FwdArgs& a, hipStream_t stream, long long blocks, bool bool_mask) {
+  if constexpr (use_row_kernel<D>()) {
+    if (bool_mask)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskU8, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   using K = FwdKernel<T, D>;
@@ -1092,25 +1128,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     // packed batches and strided layouts take the runtime-layout variants (for packed batches the
     // lengths live on the device, so whole and partial tiles are told apart in the kernel)
     const bool runtime_layout = packed || a.strided;
-    if (drop && plain && !a.causal && a.Nkv % 64 == 0)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false, true>), dim3((unsigned)blocks), dim3(256), 0,
-                         stream, a);
-    else if (drop && plain)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false, true>), dim3((unsigned)blocks), dim3(256), 0,
-                         stream, a);
-    else if (drop)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false, true>), dim3((unsigned)blocks), dim3(256), 0,
-                         stream, a);
-    else if (runtime_layout && plain)
+    if (drop) return launch_fwd_drop<T, D>(a, stream, blocks, plain);
+    if (!runtime_layout && (staged_mask || staged_bool)) return launch_fwd_staged<T, D>(a, stream, blocks, staged_bool);
+    if (runtime_layout && plain)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (runtime_layout)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                         a);
-    else if (staged_mask)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskF32, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
-                         a);
-    else if (staged_bool)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowMaskU8, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                          a);
     else if (plain && !a.causal && a.Nkv % 64 == 0)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

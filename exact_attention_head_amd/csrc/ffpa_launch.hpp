@@ -12,14 +12,22 @@ struct Fp16;
 
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+template <typename T, int D>
+hipError_t launch_fwd_drop(const FwdArgs& a, hipStream_t stream, long long blocks, bool plain);
+template <typename T, int D>
+hipError_t launch_fwd_staged(const FwdArgs& a, hipStream_t stream, long long blocks, bool bool_mask);
 
 // Head dims with a compiled kernel: 64, 128, ..., 1024.
 #define FFPA_FOR_EACH_D(X) \
   X(64) X(128) X(192) X(256) X(320) X(384) X(448) X(512) X(576) X(640) X(704) X(768) X(832) X(896) X(960) X(1024)
 
-#define FFPA_DECLARE(Dv)                                                        \
-  extern template hipError_t launch_fwd<Bf16, Dv>(const FwdArgs&, hipStream_t); \
-  extern template hipError_t launch_fwd<Fp16, Dv>(const FwdArgs&, hipStream_t);
+#define FFPA_DECLARE(Dv)                                                                                      \
+  extern template hipError_t launch_fwd<Bf16, Dv>(const FwdArgs&, hipStream_t);                               \
+  extern template hipError_t launch_fwd<Fp16, Dv>(const FwdArgs&, hipStream_t);                               \
+  extern template hipError_t launch_fwd_drop<Bf16, Dv>(const FwdArgs&, hipStream_t, long long, bool);         \
+  extern template hipError_t launch_fwd_drop<Fp16, Dv>(const FwdArgs&, hipStream_t, long long, bool);         \
+  extern template hipError_t launch_fwd_staged<Bf16, Dv>(const FwdArgs&, hipStream_t, long long, bool);       \
+  extern template hipError_t launch_fwd_staged<Fp16, Dv>(const FwdArgs&, hipStream_t, long long, bool);
 FFPA_FOR_EACH_D(FFPA_DECLARE)
 #undef FFPA_DECLARE
 
