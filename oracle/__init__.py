@@ -249,6 +249,8 @@ BWD_FAULT_NONE = 0
 BWD_FAULT_NO_DELTA = 1        # dS = P * dP, the row term dropped
 BWD_FAULT_DK_UNSCALED = 2     # dK without the scale factor
 BWD_FAULT_GQA_LAST_HEAD = 3   # a KV head's gradient from the last head of its group only
+BWD_FAULT_KEEP_BIT_REVERSED = 4  # dropout keep words decoded with key 32 w + i at bit 31 - i
+BWD_FAULT_KEEP_WORD_SHIFTED = 5  # dropout keep words decoded one word late
 
 
 def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is_causal: bool = False,
@@ -291,9 +293,11 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
     dV = np.zeros_like(V)
     Mdrop = None
     if keep_bits is not None:
-        from .philox import keep_matrix
+        from .philox import KEEP_FAULT_BIT_REVERSED, KEEP_FAULT_NONE, KEEP_FAULT_WORD_SHIFTED, keep_matrix
 
-        Mdrop = keep_matrix(keep_bits, Nkv) / (1.0 - float(np.float32(dropout_p)))  # [B, Hq, Nq, Nkv]
+        kf = {BWD_FAULT_KEEP_BIT_REVERSED: KEEP_FAULT_BIT_REVERSED,
+              BWD_FAULT_KEEP_WORD_SHIFTED: KEEP_FAULT_WORD_SHIFTED}.get(fault, KEEP_FAULT_NONE)
+        Mdrop = keep_matrix(keep_bits, Nkv, fault=kf) / (1.0 - float(np.float32(dropout_p)))  # [B, Hq, Nq, Nkv]
     for b in range(B):
         for h in range(Hq):
             hk = h // G

@@ -102,8 +102,19 @@ def dropout_keep_bits(B: int, Hq: int, Nq: int, Nkv: int, p: float, seed: int, o
     return keep.reshape(B, Hq, Nq, keep.shape[-1])
 
 
-def keep_matrix(keep_bits: np.ndarray, Nkv: int) -> np.ndarray:
+# Planted-mistake switches of keep_matrix (tests of the pins only).
+KEEP_FAULT_NONE = 0
+KEEP_FAULT_BIT_REVERSED = 1   # key 32 w + i read from bit 31 - i
+KEEP_FAULT_WORD_SHIFTED = 2   # key 32 w + i read from word w + 1 (the last word from word 0)
+
+
+def keep_matrix(keep_bits: np.ndarray, Nkv: int, fault: int = KEEP_FAULT_NONE) -> np.ndarray:
     """Unpacks [..., W] keep words into a [..., Nkv] 0/1 float64 array (bit i of word w = key 32 w + i)."""
     kb = np.asarray(keep_bits, dtype=np.uint64)
-    bits = (kb[..., :, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)
+    if fault == KEEP_FAULT_WORD_SHIFTED:
+        kb = np.roll(kb, -1, axis=-1)
+    shifts = np.arange(32, dtype=np.uint64)
+    if fault == KEEP_FAULT_BIT_REVERSED:
+        shifts = shifts[::-1].copy()
+    bits = (kb[..., :, None] >> shifts) & np.uint64(1)
     return bits.reshape(*kb.shape[:-1], kb.shape[-1] * 32)[..., :Nkv].astype(np.float64)

@@ -6,6 +6,10 @@ What pins what:
   scalar and the array form.
 - The keep-bit layout: the fraction of dropped keys against p within a binomial bound, p = 0
   keeping every key, keys past Nkv never kept, rows, words and offsets drawing distinct streams.
+- The keep-word decoding (oracle.philox.keep_matrix): against a reader that takes the bits one by
+  one, and against a hand-set word (bit 13 of word 1 keeps key 45 alone).  The dropout backward's
+  torch reference reads the bits one by one too, so a decoding mistake in the oracle's backward
+  fails that pin as well.
 - The dropout attention (oracle.attention_dropout_rows): a pure-Python math.fsum evaluation of
   SDPA-style dropout on tiny inputs (bits read one by one from the words); closed forms (every
   key kept gives the plain output over 1 - p; complementary masks add up to the plain output
@@ -20,7 +24,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.philox import dropout_keep_bits, drop_threshold, keep_matrix, philox4x32_10, philox4x32_10_np
+from oracle.philox import (KEEP_FAULT_BIT_REVERSED, KEEP_FAULT_NONE, KEEP_FAULT_WORD_SHIFTED, dropout_keep_bits,
+                           drop_threshold, keep_matrix, philox4x32_10, philox4x32_10_np)
 from workloads import random_qkv
 
 # Published known-answer vectors of Philox4x32 with 10 rounds: (counter, key) -> output.
@@ -203,7 +208,8 @@ def _torch_dropout_grads(q, k, v, do, words, p, mask=None, is_causal=False):
     if is_causal:
         vis = torch.arange(Nkv).view(1, Nkv) <= torch.arange(Nq).view(Nq, 1) + (Nkv - Nq)
         s = s.masked_fill(~vis, -math.inf)
-    Z = torch.from_numpy(keep_matrix(words, Nkv))
+    # keep flags read bit by bit from the words, not through keep_matrix, which this pins
+    Z = torch.tensor(bits_one_by_one(words, B, Hq, Nq, Nkv), dtype=torch.float64)
     o = (torch.softmax(s, dim=-1) * Z / (1.0 - float(np.float32(p)))) @ vr
     return [g.numpy() for g in torch.autograd.grad(o, (qd, kd, vd), do.double())]
 
@@ -240,5 +246,30 @@ def test_backward_dropout_all_kept_at_zero_p():
 
 
 def test_backward_dropout_planted_mistakes_are_caught():
-    for fault in (oracle.BWD_FAULT_NO_DELTA, oracle.BWD_FAULT_DK_UNSCALED, oracle.BWD_FAULT_GQA_LAST_HEAD):
+    for fault in (oracle.BWD_FAULT_NO_DELTA, oracle.BWD_FAULT_DK_UNSCALED, oracle.BWD_FAULT_GQA_LAST_HEAD,
+                  oracle.BWD_FAULT_KEEP_BIT_REVERSED, oracle.BWD_FAULT_KEEP_WORD_SHIFTED):
         assert not pin_backward_dropout(fault), fault
+
+
+def pin_keep_matrix(fault=KEEP_FAULT_NONE):
+    """keep_matrix against the bit-by-bit reader on random words (ragged Nkv, several words per row)
+    and on one hand-set word: word 1 = 1 << 13 keeps key 45 and nothing else of keys 32..63."""
+    ok = True
+    rng = np.random.default_rng(5)
+    for shape, Nkv in [((2, 3, 4, 3), 70), ((1, 1, 2, 4), 128), ((1, 2, 3, 1), 9)]:
+        words = rng.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32)
+        want = np.array(bits_one_by_one(words, *shape[:3], Nkv), dtype=np.float64)
+        ok &= bool(np.array_equal(keep_matrix(words, Nkv, fault=fault), want))
+    hand = np.array([[[[0, 1 << 13, 0]]]], dtype=np.uint32)
+    z = keep_matrix(hand, 96, fault=fault)[0, 0, 0]
+    ok &= bool(z[45] == 1.0 and z[44] == 0.0 and z.sum() == 1.0)
+    return ok
+
+
+def test_keep_matrix_bit_order():
+    assert pin_keep_matrix()
+
+
+def test_keep_matrix_planted_mistakes_are_caught():
+    for fault in (KEEP_FAULT_BIT_REVERSED, KEEP_FAULT_WORD_SHIFTED):
+        assert not pin_keep_matrix(fault), fault
