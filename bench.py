@@ -29,8 +29,110 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def time_workload(w, steps: int, warmup: int):
-    """Times `steps` launches after `warmup` untimed ones; returns (ms per launch, inputs, outputs)."""
+class ClockSampler:
+    """Samples the GPU's shader (gfx) clock through the AMD SMI library in a background thread while a
+    timed region runs; reports the median of the samples in MHz (None when the library is absent or
+    refuses, e.g. without a driver)."""
+
+    def __init__(self, period_s: float = 0.002):
+        self.period, self.samples, self._h, self._thread, self._stop = period_s, [], None, None, False
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            self._smi, self._h = amdsmi, (handles[0] if handles else None)
+        except Exception:
+            self._h = None
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if clks:
+            return sum(clks) / len(clks)
+        return float(self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.SYS)["clk"])
+
+    def _run(self):
+        import time as _t
+
+        while not self._stop:
+            try:
+                self.samples.append(self._read())
+            except Exception:
+                return
+            _t.sleep(self.period)
+
+    def __enter__(self):
+        if self._h is not None:
+            import threading
+
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop = True
+        if self._thread is not None:
+            self._thread.join()
+
+    def median(self):
+        if not self.samples:
+            return None
+        xs = sorted(self.samples)
+        return round(xs[len(xs) // 2], 1)
+
+
+def timed(fn, steps: int, warmup: int, clock: bool = False):
+    """Runs fn `warmup` times untimed, then `steps` times, each launch between its own pair of HIP
+    events on torch's current stream (the stream the library's calls enqueue on), with a device
+    synchronisation on both sides of the timed region.  Returns per-launch statistics in ms and, with
+    clock=True, the median shader clock sampled during the timed region."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    sampler = ClockSampler() if clock else None
+    ctx = sampler if sampler is not None else _Null()
+    with ctx:
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+    per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    total = ev[0][0].elapsed_time(ev[-1][1])
+    return dict(median_ms=per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
+                min_ms=per[0], max_ms=per[-1], mean_ms=total / steps,
+                sclk_mhz=sampler.median() if sampler is not None else None,
+                sclk_samples=len(sampler.samples) if sampler is not None else 0)
+
+
+class _Null:
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        return False
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def time_workload(w, steps: int, warmup: int, clock: bool = False):
+    """Times `steps` launches after `warmup` untimed ones; returns (launch statistics, inputs, outputs)."""
     import torch
 
     import exact_attention_head_amd as ffpa
@@ -46,23 +148,18 @@ def time_workload(w, steps: int, warmup: int):
     def step():
         return ffpa.attn(qd, kd, vd, attn_mask=md, is_causal=w.causal, enable_gqa=gqa, return_lse=True, out=o)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()  # ffpa.attn enqueues on torch's current stream
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        _, lse = step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    return ms, (q, k, v, mask), (o.cpu(), lse.cpu())
+    res = {}
+
+    def step_keep():
+        res["lse"] = step()[1]
+
+    st = timed(step_keep, steps, warmup, clock=clock)
+    return st, (q, k, v, mask), (o.cpu(), res["lse"].cpu())
 
 
 def time_dropout(w, p: float, steps: int, warmup: int):
     """Times the forward with attention dropout (ffpa_fwd_dropout, keep words drawn once beforehand) and,
-    separately, the keep-word generator (ffpa_dropout_keep); returns (forward ms, generator ms)."""
+    separately, the keep-word generator (ffpa_dropout_keep); returns the two launch statistics."""
     import torch
 
     import exact_attention_head_amd as ffpa
@@ -85,22 +182,10 @@ def time_dropout(w, p: float, steps: int, warmup: int):
         if st != ffpa.OK:
             raise RuntimeError(f"ffpa_dropout_keep returned {st}")
 
-    out = []
-    for fn in (fwd, gen):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        out.append(e0.elapsed_time(e1) / steps)
-    return out[0], out[1]
+    return timed(fwd, steps, warmup), timed(gen, steps, warmup)
 
 
-def time_varlen(w, steps: int, warmup: int):
+def time_varlen(w, steps: int, warmup: int, clock: bool = False):
     """As time_workload, for a packed variable-length batch (one ffpa_fwd_varlen launch per step)."""
     import torch
 
@@ -126,21 +211,12 @@ def time_varlen(w, steps: int, warmup: int):
         if st != ffpa.OK:
             raise RuntimeError(f"ffpa_fwd_varlen returned {st}")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    return timed(step, steps, warmup, clock=clock)
 
 
 def time_backward(w, steps: int, warmup: int):
-    """Times ffpa_bwd (dQ, dK, dV) of a dense workload after one forward for its O and LSE; returns ms
-    per backward launch sequence (the whole ffpa_bwd call)."""
+    """Times ffpa_bwd (dQ, dK, dV) of a dense workload after one forward for its O and LSE; returns the
+    statistics of the whole ffpa_bwd call."""
     import torch
 
     import exact_attention_head_amd as ffpa
@@ -168,17 +244,9 @@ def time_backward(w, steps: int, warmup: int):
         if st != ffpa.OK:
             raise RuntimeError(f"ffpa_bwd returned {st}")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+    st = timed(step, steps, warmup)
     del keep
-    return e0.elapsed_time(e1) / steps
+    return st
 
 
 def cpu_baseline(w, inputs, outputs, seconds: float):
@@ -318,11 +386,15 @@ def main() -> int:
     log(f"workload {w.name}: warmup {args.warmup}, steps {args.steps}")
     packed = isinstance(w, W.VarlenWorkload)
     if packed:
-        ms, inputs, outputs = time_varlen(w, args.steps, args.warmup), None, None
+        st, inputs, outputs = time_varlen(w, args.steps, args.warmup, clock=True), None, None
     else:
-        ms, inputs, outputs = time_workload(w, args.steps, args.warmup)
+        st, inputs, outputs = time_workload(w, args.steps, args.warmup, clock=True)
+    # the headline figure is the median launch; mean, min and max sit beside it
+    ms = st["median_ms"]
     tflops = w.flops / (ms * 1e-3) / 1e12
-    log(f"{w.name}: {ms:.4f} ms/launch, {tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak)")
+    log(f"{w.name}: median {ms:.4f} ms/launch (min {st['min_ms']:.4f}, mean {st['mean_ms']:.4f}), "
+        f"{tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak), sclk {st['sclk_mhz']} MHz "
+        f"({st['sclk_samples']} samples)")
 
     traffic = measured_traffic(args.traffic_json, w.name)
     import exact_attention_head_amd as ffpa
@@ -330,7 +402,8 @@ def main() -> int:
     kernel = ffpa.kernel_name(w.D)
     roofline = dict(bound="mfma", achieved=round(tflops, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(tflops / PEAK_TFLOPS, 4), traffic=traffic, traffic_unit="HBM bytes per launch",
-                    kernel=kernel, flops_per_launch=w.flops, avg_launch_ms=round(ms, 5))
+                    kernel=kernel, flops_per_launch=w.flops, avg_launch_ms=round(st["mean_ms"], 5),
+                    median_launch_ms=round(ms, 5))
 
     secondary = []
     if args.sweep:
@@ -345,24 +418,27 @@ def main() -> int:
             w2 = pick(name[5:] if dropout else (name[4:] if backward else name))
             if dropout:
                 # forward with attention dropout at p = 0.1: same FLOP count; the keep-word generator apart
-                ms2, gen_ms = time_dropout(w2, 0.1, max(5, args.steps // 5), 2)
+                st2, gst = time_dropout(w2, 0.1, max(5, args.steps // 2), 2)
+                gen_ms = gst["median_ms"]
                 flops2 = w2.flops
                 log(f"dropout keep words {w2.name}: {gen_ms:.4f} ms/launch")
             elif backward:
                 # the backward's five products: 10*B*Hq*Nq*Nkv*D FLOPs (2.5x the forward), halved for causal
-                ms2 = time_backward(w2, max(3, args.steps // 10), 1)
+                st2 = time_backward(w2, max(3, args.steps // 5), 1)
                 flops2 = 2.5 * w2.flops
             elif isinstance(w2, W.VarlenWorkload):
-                ms2, flops2 = time_varlen(w2, max(5, args.steps // 5), 2), w2.flops
+                st2, flops2 = time_varlen(w2, max(5, args.steps // 2), 2), w2.flops
             else:
-                (ms2, _, _), flops2 = time_workload(w2, max(5, args.steps // 5), 2), w2.flops
+                (st2, _, _), flops2 = time_workload(w2, max(5, args.steps // 2), 2), w2.flops
+            ms2 = st2["median_ms"]
             tf2 = flops2 / (ms2 * 1e-3) / 1e12
             tag = ("backward " if backward else ("dropout p=0.1 " if dropout else "")) + w2.name
             log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
             secondary.append(dict(workload=tag, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
                                   kernel="ffpa_bwd (library GEMMs + HIP kernels)" if backward else ffpa.kernel_name(w2.D),
                                   **({"keep_words_ms": round(gen_ms, 4)} if dropout else {}),
-                                  ms_per_step=round(ms2, 4), tflops=round(tf2, 2),
+                                  ms_per_step=round(ms2, 4), min_ms=round(st2["min_ms"], 4),
+                                  mean_ms=round(st2["mean_ms"], 4), tflops=round(tf2, 2),
                                   frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
 
     cpu, parity = None, None
@@ -377,6 +453,8 @@ def main() -> int:
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp16", "data": "synthetic",
+        "median_ms": round(ms, 5), "min_ms": round(st["min_ms"], 5), "mean_ms": round(st["mean_ms"], 5),
+        "max_ms": round(st["max_ms"], 5), "sclk_mhz": st["sclk_mhz"], "cpu_model": cpu_model(),
         "config": w.describe(), "frac_of_peak": round(tflops / PEAK_TFLOPS, 4), "roofline": roofline,
         "cpu_baseline": cpu, "parity_sample": parity, "secondary": secondary,
     }

@@ -31,7 +31,7 @@ def head_dims() -> list[int]:
     return [int(x) for x in re.findall(r"X\((\d+)\)", body)]
 
 
-def _compile(src: str, obj: str, defines: list[str], remarks: bool) -> tuple[str, str]:
+def _compile(src: str, obj: str, defines: list[str], remarks: bool = False) -> tuple[str, str]:
     """Compiles one object, keeping its gfx950 assembly next to it (obj with .s) for the hazard check."""
     work = obj + ".tmp.d"
     shutil.rmtree(work, ignore_errors=True)
@@ -49,16 +49,35 @@ def _compile(src: str, obj: str, defines: list[str], remarks: bool) -> tuple[str
     return obj, r.stderr
 
 
-def resource_summary(stderr: str) -> dict:
-    """Parses -Rpass-analysis=kernel-resource-usage remarks (VGPRs, AGPRs, spills, LDS)."""
+def kernel_resources(asm_path: str) -> dict:
+    """Per-kernel resources from the code-object metadata in a saved gfx950 assembly file:
+    {mangled name: {vgpr, agpr, sgpr, vgpr_spill, sgpr_spill, scratch, lds}}."""
+    with open(asm_path) as f:
+        txt = f.read()
+    i = txt.find("amdhsa.kernels:")
+    if i < 0:
+        return {}
+    j = txt.find("amdhsa.target", i)
     out = {}
-    for key, pat in [("vgpr", r"VGPRs: (\d+)"), ("agpr", r"AGPRs: (\d+)"), ("vgpr_spill", r"VGPRs Spill: (\d+)"),
-                     ("sgpr_spill", r"SGPRs Spill: (\d+)"), ("scratch", r"ScratchSize \[bytes/lane\]: (\d+)"),
-                     ("lds", r"LDS Size \[bytes/block\]: (\d+)"), ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)")]:
-        m = re.search(pat, stderr)
-        if m:
-            out[key] = int(m.group(1))
+    fields = [("vgpr", "vgpr_count"), ("agpr", "agpr_count"), ("sgpr", "sgpr_count"),
+              ("vgpr_spill", "vgpr_spill_count"), ("sgpr_spill", "sgpr_spill_count"),
+              ("scratch", "private_segment_fixed_size"), ("lds", "group_segment_fixed_size")]
+    for blk in re.split(r"\n  - ", txt[i:j if j > 0 else None])[1:]:
+        m = re.search(r"\.name:\s+(\S+)", blk)
+        if not m:
+            continue
+        res = {}
+        for key, field in fields:
+            v = re.search(r"\." + field + r":\s+(\d+)", blk)
+            res[key] = int(v.group(1)) if v else 0
+        out[m.group(1)] = res
     return out
+
+
+def spills(resources: dict) -> list[str]:
+    """Kernels that spill VGPRs or use scratch memory (SGPR spills go to VGPR lanes, not memory)."""
+    return [f"{name}: {r['vgpr_spill']} VGPRs spilled, {r['scratch']} B/lane scratch"
+            for name, r in resources.items() if r["vgpr_spill"] > 0 or r["scratch"] > 0]
 
 
 def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -> str:
@@ -80,14 +99,19 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     # largest kernels first
     kd = lambda path: re.search(r"_d(\d+)(_p\d)?\.o$", path)  # per-head-dim kernel objects
     tasks.sort(key=lambda t: -int(kd(t[1]).group(1)) if kd(t[1]) else 0)
-    resources = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_compile, s, o, d, report) for s, o, d in tasks]
+        futs = [ex.submit(_compile, s, o, d, False) for s, o, d in tasks]
         for f in cf.as_completed(futs):
-            obj, err = f.result()
-            if report and kd(obj):
-                resources[os.path.basename(obj)[:-2]] = resource_summary(err)
+            f.result()
     objs = [o for _, o, _ in tasks]
+    # resource gate: no kernel may spill VGPRs or use scratch memory
+    resources = {}
+    for o in objs:
+        if os.path.exists(o[:-2] + ".s"):
+            resources.update(kernel_resources(o[:-2] + ".s"))
+    bad = spills(resources)
+    if bad:
+        raise RuntimeError("kernels spill registers to scratch memory:\n" + "\n".join(bad))
     # the kernels' inline assembly relies on rules the compiler does not check: verify them
     sys.path.insert(0, PKG)
     try:
@@ -113,8 +137,11 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     if verbose:
         print(f"[build] {LIB} ({len(objs)} objects, {time.time() - t0:.0f}s, {jobs} jobs)", flush=True)
     if report:
-        for k in sorted(resources, key=lambda s: (s.split("_")[1], int(s.split("_d")[1]))):
-            print(f"[build] {k}: {resources[k]}", flush=True)
+        names = sorted(resources)
+        dem = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True).stdout.split("\n")
+        for name, pretty in zip(names, dem):
+            print(f"[build] {pretty or name}: {resources[name]}", flush=True)
+        print(f"[build] {len(resources)} kernels, none spills", flush=True)
     return LIB
 
 

@@ -1071,9 +1071,9 @@ hipError_t launch_fwd_drop(const FwdArgs& a, hipStream_t stream, long long block
     if (plain && !a.causal && a.Nkv % 64 == 0)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false, true>), dim3((unsigned)blocks), dim3(256), 0,
                          stream, a);
-    else if (plain)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false, true>), dim3((unsigned)blocks), dim3(256), 0,
-                         stream, a);
+    else if (plain && split_drop_fits<D>())
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, split_drop_fits<D>() ? kRowSplit : kRowGeneral, false, true>),
+                         dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false, true>), dim3((unsigned)blocks), dim3(256), 0,
                          stream, a);
@@ -1138,7 +1138,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     else if (plain && !a.causal && a.Nkv % 64 == 0)
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowRaw, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else if (plain)
-      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, false>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+      // the runtime-layout variant where the contiguous one does not fit its registers (the
+      // contiguous strides are set in the arguments either way)
+      hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowSplit, !dense_split_fits<D>()>), dim3((unsigned)blocks),
+                         dim3(256), 0, stream, a);
     else
       hipLaunchKernelGGL((ffpa_fwd_row_kernel<T, D, kRowGeneral, false>), dim3((unsigned)blocks), dim3(256), 0, stream,
                          a);

@@ -109,6 +109,19 @@ constexpr bool use_row_kernel() {
   return RowTiling<D>::OK;
 }
 
+// Variants that do not fit the register file without spilling (from the kernels' resource metadata;
+// the build refuses any spill): the contiguous split variant at D = 1024, whose runtime-layout twin
+// fits, and the split variant with dropout above D = 448, where the general variant with dropout
+// fits.  The launcher takes the variant that fits and never instantiates the others.
+template <int D>
+constexpr bool dense_split_fits() {
+  return D != 1024;
+}
+template <int D>
+constexpr bool split_drop_fits() {
+  return D <= 448;
+}
+
 // s_waitcnt lgkmcnt(N) before a product whose operand fragments were read by inline assembly.
 // It names no registers: volatile assembly statements keep their order, so the product (also
 // volatile assembly) stays behind it, and declaring the fragments as outputs would make the
