@@ -24,7 +24,7 @@ from typing import Optional
 __all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
            "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
-           "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_name", "FFPA_BF16", "FFPA_FP16",
+           "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_head_dim", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +37,8 @@ OK, ERR_TYPE, ERR_VALUE, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3, 4
 EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_error_detail", "ffpa_rows_per_block",
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
-            "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout")
+            "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout",
+            "ffpa_kernel_head_dim")
 
 
 class MaskDesc(ctypes.Structure):
@@ -78,6 +79,8 @@ def library() -> ctypes.CDLL:
     lib.ffpa_rows_per_block.restype = i32
     lib.ffpa_kernel_name.argtypes = [i64]
     lib.ffpa_kernel_name.restype = ctypes.c_char_p
+    lib.ffpa_kernel_head_dim.argtypes = [i64]
+    lib.ffpa_kernel_head_dim.restype = i64
     vargs = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32]
     lib.ffpa_fwd_varlen.argtypes = vargs + [p]
     lib.ffpa_fwd_varlen.restype = i32
@@ -199,6 +202,18 @@ def _strides3(t):
     return st
 
 
+def _strided_plan(ptrs, strides, B, Hq, Hkv, Nq, Nkv, D, dtype) -> Optional[LayoutDesc]:
+    """The layout descriptor for reading Q, K, V and writing O in place through ffpa_fwd_strided
+    (ptrs: their device addresses; strides: their {batch, head, row} element strides), or None when the
+    strided entry cannot address them (ffpa_check_strided_args: FFPA_ERR_UNSUPPORTED, e.g. row strides
+    or one head's rows beyond the kernels' 32-bit buffer offsets, or K and V row strides that differ):
+    the caller then works on contiguous copies, which the dense entry takes.  Host-only."""
+    lay = LayoutDesc(*((ctypes.c_int64 * 3)(*st) for st in strides))
+    st = ffpa_check_strided_args(ptrs[0], ptrs[1], ptrs[2], None, ptrs[3], None, B, Hq, Hkv, Nq, Nkv, D, lay,
+                                 math.nan, False, dtype)
+    return None if st == ERR_UNSUPPORTED else lay
+
+
 def ffpa_fwd_varlen(q, k, v, cu_q, cu_k, o, lse, B, Hq, Hkv, Tq, Tk, max_q, max_k, D, scale, is_causal, dtype,
                     stream) -> int:
     """The raw packed entry point: pointers are integers (device addresses), returns the status code."""
@@ -220,6 +235,12 @@ def ffpa_check_cu_seqlens(offsets, T: int, max_seqlen: int) -> int:
 
 def rows_per_block(D: int) -> int:
     return int(library().ffpa_rows_per_block(D))
+
+
+def kernel_head_dim(D: int) -> int:
+    """Head dim of the kernel serving tensors of head dim D (D itself, or the next compiled one up whose
+    columns past D are padding); 0 if unsupported."""
+    return int(library().ffpa_kernel_head_dim(D))
 
 
 def kernel_name(D: int):
@@ -312,6 +333,14 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     contiguous = all(t.is_contiguous() for t in (q, k, v, o))
     if not contiguous and None in (sq, sk, sv):
         raise ValueError("query, key and value must be 16-byte aligned")
+    lay, o_user = None, o
+    if not contiguous and not dropping:
+        lay = _strided_plan([t.data_ptr() for t in (q, k, v, o)], [sq, sk, sv, so], B, Hq, Hkv, Nq, Nkv, D, dtype)
+        if lay is None:  # a layout the kernels cannot address in place: contiguous copies instead
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            if not o.is_contiguous():
+                o = torch.empty((B, Hq, Nq, D), dtype=query.dtype, device=query.device)
+            contiguous = True
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=query.device) if return_lse else None
     desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(query.device), B, Hq, Nq, Nkv)
     sc = math.nan if scale is None else float(scale)
@@ -325,14 +354,14 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
             st = ffpa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(), lp, B, Hq, Hkv, Nq, Nkv, D,
                           sc, bool(is_causal), dtype, stream)
         else:
-            lay = LayoutDesc((ctypes.c_int64 * 3)(*sq), (ctypes.c_int64 * 3)(*sk), (ctypes.c_int64 * 3)(*sv),
-                             (ctypes.c_int64 * 3)(*so))
             st = ffpa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), desc, o.data_ptr(), lp, B, Hq, Hkv, Nq,
                                   Nkv, D, lay, sc, bool(is_causal), dtype, stream)
     del keep
     if st != OK:
         _raise(st)
-    return (o, lse) if return_lse else o
+    if o is not o_user:
+        o_user.copy_(o)
+    return (o_user, lse) if return_lse else o_user
 
 
 def _attn_dropout(q, k, v, o, out, lse, desc, mask_keep, B, Hq, Hkv, Nq, Nkv, D, sc, is_causal, dtype, p, seed,

@@ -56,6 +56,20 @@ int rows_for(int64_t D) {
   }
 }
 
+// Head dim of the kernel that serves tensors of head dim D: D itself when a kernel is compiled for
+// it; otherwise (D a multiple of 8) the smallest row-kernel head dim above D, whose columns past D
+// are padding.  0 if none.
+int64_t kernel_dim(int64_t D) {
+  if (rows_for(D) > 0) return D;
+  if (D < 8 || D % 8 != 0) return 0;
+  int64_t best = 0;
+#define FFPA_PAD_CASE(Dv) \
+  if (best == 0 && Dv >= D && ffpa::use_row_kernel<Dv>()) best = Dv;
+  FFPA_FOR_EACH_D(FFPA_PAD_CASE)
+#undef FFPA_PAD_CASE
+  return best;
+}
+
 // Elements from a tensor's first element to one past its last: (B-1)*sb + (H-1)*sh + (N-1)*sn + D.
 int64_t extent(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t D) {
   return (B - 1) * st[0] + (H - 1) * st[1] + (N - 1) * st[2] + D;
@@ -121,10 +135,10 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
     return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
   if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
-  if (D < 64 || D > 1024 || D % 64 != 0)
-    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
+  if (D > 1024 || kernel_dim(D) == 0)
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
   // grid size and 32-bit in-kernel indexing
-  const int br = rows_for(D);
+  const int br = rows_for(kernel_dim(D));
   const int64_t nqt = (Nq + br - 1) / br;
   if (B * Hq * nqt > 0x7fffffffLL) return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
   if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B * Hq > (1LL << 30) || B * Hkv > (1LL << 30))
@@ -197,9 +211,9 @@ int check_varlen(const void* q, const void* k, const void* v, const int32_t* cu_
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
     return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
   if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
-  if (D < 64 || D > 1024 || D % 64 != 0)
-    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
-  const int br = rows_for(D);
+  if (D > 1024 || kernel_dim(D) == 0)
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
+  const int br = rows_for(kernel_dim(D));
   if (B > (1LL << 30) || B * Hq * ((maxq + br - 1) / br) > 0x7fffffffLL)
     return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
   if (Tq >= (1LL << 31) || Tk >= (1LL << 31) || Tq * Hq >= (1LL << 31) || Tk * Hkv >= (1LL << 31))
@@ -221,7 +235,7 @@ int check_varlen(const void* q, const void* k, const void* v, const int32_t* cu_
 
 template <typename T>
 hipError_t dispatch(int64_t D, const ffpa::FwdArgs& a, hipStream_t s) {
-  switch (D) {
+  switch (kernel_dim(D)) {
 #define FFPA_DISPATCH_CASE(Dv) \
   case Dv: return ffpa::launch_fwd<T, Dv>(a, s);
     FFPA_FOR_EACH_D(FFPA_DISPATCH_CASE)
@@ -299,6 +313,7 @@ static int launch_dense(const void* q, const void* k, const void* v, const ffpa_
   a.Nq = (int)Nq;
   a.Nkv = (int)Nkv;
   a.group = (int)(Hq / Hkv);
+  a.dcols = (int)D;
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
@@ -322,6 +337,9 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
   const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
   if (st != FFPA_OK) return st;
   if (!(dropout_p >= 0.f && dropout_p < 1.f)) return fail(FFPA_ERR_VALUE, "dropout probability must lie in [0, 1)");
+  if (kernel_dim(D) != D)
+    return fail(FFPA_ERR_UNSUPPORTED, "dropout needs a head dim with a kernel of its own (D %% 64 == 0), not %lld",
+                (long long)D);
   if (keep == nullptr || ((uintptr_t)keep & 3)) return fail(FFPA_ERR_VALUE, "keep must be non-null and 4-byte aligned");
   if (B * Hq * Nq * ((Nkv + 31) / 32) >= (1LL << 40)) return fail(FFPA_ERR_UNSUPPORTED, "keep mask too large");
   const size_t kbytes = (size_t)(B * Hq * Nq * ((Nkv + 31) / 32)) * 4;
@@ -386,6 +404,7 @@ int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
   a.Nq = (int)max_seqlen_q;
   a.Nkv = (int)max_seqlen_k;
   a.group = (int)(Hq / Hkv);
+  a.dcols = (int)D;
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
@@ -431,10 +450,12 @@ const char* ffpa_status_string(int status) {
 
 const char* ffpa_last_error_detail(void) { return g_detail; }
 
-int ffpa_rows_per_block(int64_t D) { return rows_for(D); }
+int ffpa_rows_per_block(int64_t D) { return D > 1024 ? 0 : rows_for(kernel_dim(D)); }
+
+int64_t ffpa_kernel_head_dim(int64_t D) { return D > 1024 ? 0 : kernel_dim(D); }
 
 const char* ffpa_kernel_name(int64_t D) {
-  switch (D) {
+  switch (D > 1024 ? 0 : kernel_dim(D)) {
 #define FFPA_NAME_CASE(Dv) \
   case Dv: return ffpa::kernel_name<Dv>();
     FFPA_FOR_EACH_D(FFPA_NAME_CASE)

@@ -100,6 +100,10 @@ struct FwdArgs {
   int64_t q_sb, q_sh, k_sb, k_sh, v_sb, v_sh, o_sb, o_sh;
   int q_sr, kv_sr, o_sr;
   int strided;  // 1: the dense layout is not contiguous (the runtime-layout variants serve it)
+  // Head dim of the tensors.  Below the kernel's compile-time D (a multiple of 8 served by the next
+  // compiled head dim, runtime-layout variants only) the columns from dcols on are padding: Q reads
+  // zeros there, so K's padding columns add nothing to S, and O is stored up to dcols only.
+  int dcols;
   // Attention dropout (null keep: none; dense contiguous layout only).  keep is [B, Hq, Nq, keep_w]
   // 32-bit words: bit i of word w set keeps the weight of key 32 w + i for that query row; kept
   // weights are scaled by drop_scale = 1 / (1 - p) (applied to O with the 1/l normalisation).
@@ -1114,6 +1118,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = rows_per_block<D>();
   const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
+  if (!use_row_kernel<D>() && a.dcols != D) return hipErrorInvalidValue;  // padding runs the row kernel only
   if constexpr (use_row_kernel<D>()) {
     const bool plain = a.mask_kind == kMaskNone && a.scale_log2 > 0.f;
     // fp32 additive mask with 16-byte-aligned rows whose 32-key blocks start on 128-byte lines
@@ -1125,9 +1130,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     const bool staged_bool = a.mask_kind == kMaskBoolU8 && a.mask_vec && !a.causal && a.Nkv % 64 == 0 &&
                              a.msq % 32 == 0 &&
                              ((int64_t)a.Nq + RowTiling<D>::BR) * a.msq + (int64_t)a.Nkv < (1LL << 31);
-    // packed batches and strided layouts take the runtime-layout variants (for packed batches the
-    // lengths live on the device, so whole and partial tiles are told apart in the kernel)
-    const bool runtime_layout = packed || a.strided;
+    // packed batches, strided layouts and padded head dims take the runtime-layout variants (for
+    // packed batches the lengths live on the device, so whole and partial tiles are told apart in
+    // the kernel)
+    const bool padded = a.dcols != D;
+    if (padded && (drop || a.dcols > D || a.dcols < 8 || a.dcols % 8 != 0)) return hipErrorInvalidValue;
+    const bool runtime_layout = packed || a.strided || padded;
     if (drop) return launch_fwd_drop<T, D>(a, stream, blocks, plain);
     if (!runtime_layout && (staged_mask || staged_bool)) return launch_fwd_staged<T, D>(a, stream, blocks, staged_bool);
     if (runtime_layout && plain)

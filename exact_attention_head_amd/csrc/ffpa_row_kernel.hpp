@@ -381,7 +381,11 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     const int qrow = row < Nq ? row : Nq - 1;
     const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 8);
 #pragma unroll
-    for (int k = 0; k < DW / 16; ++k) qf[k] = src[k * 2];
+    for (int k = 0; k < DW / 16; ++k) {
+      // runtime layouts may carry a padded head dim: columns from dcols on are not read and hold zero
+      if constexpr (VL) qf[k] = col0 + hi * 8 + 16 * k < a.dcols ? src[k * 2] : i32x4{0, 0, 0, 0};
+      else qf[k] = src[k * 2];
+    }
     // complete here, and redefine through the assembler: the compiler then has no load of these
     // registers to wait for inside the key loop (where it would drain the prefetch ring)
     vm_wait<0>();
@@ -838,7 +842,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         i32x2 w;
         w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
         w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
-        *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
+        // four columns; with a padded head dim (a multiple of 8) either all or none lie below dcols
+        if (!VL || col0 + s * 32 + q4 * 8 + hi * 4 < a.dcols) *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
       }
       __builtin_amdgcn_sched_barrier(0);  // one column block at a time: few registers in flight
     });

@@ -66,7 +66,7 @@ enum {
   FFPA_OK = 0,
   FFPA_ERR_TYPE = 1,        /* dtype not bf16/fp16, or unknown mask kind */
   FFPA_ERR_VALUE = 2,       /* inconsistent shapes, causal with Nkv < Nq, bad scale, bad pointers */
-  FFPA_ERR_UNSUPPORTED = 3, /* a valid request outside what the kernels cover (e.g. D % 64 != 0) */
+  FFPA_ERR_UNSUPPORTED = 3, /* a valid request outside what the kernels cover (e.g. D % 8 != 0) */
   FFPA_ERR_HIP = 4          /* the HIP runtime refused the launch */
 };
 
@@ -80,7 +80,12 @@ enum {
  *        where both the mask and the causal rule admit it
  *   o    device, [B, Hq, Nq, D], contiguous, dtype elements; written
  *   lse  device, [B, Hq, Nq] float32, natural log; written; NULL skips it
- *   B, Hq, Hkv, Nq, Nkv >= 1; Hq % Hkv == 0; 64 <= D <= 1024 with D % 64 == 0
+ *   B, Hq, Hkv, Nq, Nkv >= 1; Hq % Hkv == 0; 8 <= D <= 1024 with D % 8 == 0
+ *        (head dims divisible by 8, as the README's "End-to-End Inference"
+ *        section allows; a D without a kernel of its own runs the next one up,
+ *        see ffpa_kernel_head_dim; K and V must then hold finite values, since
+ *        the padding columns of one key row read the next row's first ones,
+ *        multiplied by zero)
  *   scale   finite, or NaN for the default 1/sqrt(D)
  *   is_causal  0 or 1; 1 requires Nkv >= Nq
  *   dtype   ffpa_dtype
@@ -171,7 +176,8 @@ int ffpa_dropout_keep(uint32_t* keep, int64_t B, int64_t Hq, int64_t Nq, int64_t
  * the logits, as in ffpa_fwd: dropout does not change it.  Tensors are
  * contiguous as in ffpa_fwd; every other argument, rule and error is that of
  * ffpa_fwd, plus FFPA_ERR_VALUE for dropout_p outside [0, 1), a null or
- * misaligned keep, or o / lse overlapping keep.
+ * misaligned keep, or o / lse overlapping keep, and FFPA_ERR_UNSUPPORTED for
+ * a head dim without a kernel of its own (D % 64 != 0).
  */
 int ffpa_fwd_dropout(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
@@ -257,6 +263,12 @@ const char* ffpa_last_error_detail(void);
 /* Rows of Q handled by one workgroup for head dim D (the tiling the kernels
  * use), or 0 for an unsupported D.  Host-only; for schedulers and tests. */
 int ffpa_rows_per_block(int64_t D);
+
+/* Head dim of the kernel that serves tensors of head dim D: D itself when
+ * D % 64 == 0, else the smallest head dim above D among 64, 128, 192, 256,
+ * 320, 384, 448, 512, 640, 768, 896 and 1024 (its columns past D are padding:
+ * zeros in Q, never stored in O).  0 for an unsupported D.  Host-only. */
+int64_t ffpa_kernel_head_dim(int64_t D);
 
 /* Name of the GPU kernel that serves head dim D (as profilers list it, without
  * template arguments), or NULL for an unsupported D.  Which variant of that

@@ -44,7 +44,7 @@ def detail():
 def test_valid_arguments_pass():
     assert check() == ffpa.OK
     assert detail() == ""
-    for D in range(64, 1025, 64):
+    for D in range(8, 1025, 8):  # every multiple of 8 (those without a kernel of their own run padded)
         assert check(D=D) == ffpa.OK, D
     assert check(causal=True) == ffpa.OK
     assert check(lse=None) == ffpa.OK
@@ -70,8 +70,10 @@ def test_valid_arguments_pass():
     (dict(o=Q), ffpa.ERR_VALUE),
     (dict(o=Q + 1024), ffpa.ERR_VALUE),
     (dict(lse=V + 64), ffpa.ERR_VALUE),
-    (dict(D=96), ffpa.ERR_UNSUPPORTED),
-    (dict(D=32), ffpa.ERR_UNSUPPORTED),
+    (dict(D=100), ffpa.ERR_UNSUPPORTED),
+    (dict(D=4), ffpa.ERR_UNSUPPORTED),
+    (dict(D=1020), ffpa.ERR_UNSUPPORTED),
+    (dict(D=1032), ffpa.ERR_UNSUPPORTED),
     (dict(D=1088), ffpa.ERR_UNSUPPORTED),
     (dict(D=2048), ffpa.ERR_UNSUPPORTED),
 ])
@@ -116,9 +118,21 @@ def test_status_maps_to_the_pages_error_classes(status, exc):
 
 
 def test_rows_per_block():
-    rows = {D: ffpa.rows_per_block(D) for D in range(64, 1025, 64)}
+    rows = {D: ffpa.rows_per_block(D) for D in range(8, 1025, 8)}
     assert all(r in (64, 128, 256) for r in rows.values()), rows
-    assert ffpa.rows_per_block(96) == 0
+    assert ffpa.rows_per_block(100) == 0 and ffpa.rows_per_block(1032) == 0
+    assert ffpa.rows_per_block(80) == ffpa.rows_per_block(128)
+
+
+def test_kernel_head_dim():
+    row_dims = [64, 128, 192, 256, 320, 384, 448, 512, 640, 768, 896, 1024]
+    for D in range(8, 1025, 8):
+        want = D if D % 64 == 0 else min(d for d in row_dims if d >= D)
+        assert ffpa.kernel_head_dim(D) == want, D
+    assert ffpa.kernel_head_dim(8) == 64 and ffpa.kernel_head_dim(520) == 640 and ffpa.kernel_head_dim(1016) == 1024
+    assert ffpa.kernel_head_dim(576) == 576  # a compiled head dim serves itself
+    for bad in (0, 4, 100, 1020, 1032, 2048):
+        assert ffpa.kernel_head_dim(bad) == 0, bad
 
 
 def test_kernel_name():
@@ -126,7 +140,9 @@ def test_kernel_name():
     assert set(names.values()) <= {"ffpa_fwd_row_kernel", "ffpa_fwd_split_kernel", "ffpa_fwd_kernel"}, names
     # the head dims of the benchmark run the row kernel
     assert names[512] == "ffpa_fwd_row_kernel" and names[1024] == "ffpa_fwd_row_kernel"
-    assert ffpa.kernel_name(96) is None and ffpa.kernel_name(2048) is None
+    # padded head dims run the row kernel of the next head dim up
+    assert ffpa.kernel_name(96) == "ffpa_fwd_row_kernel" and ffpa.kernel_name(552) == "ffpa_fwd_row_kernel"
+    assert ffpa.kernel_name(100) is None and ffpa.kernel_name(2048) is None
 
 
 def test_python_layer_rejects_before_the_library():
@@ -144,6 +160,22 @@ def test_python_layer_rejects_before_the_library():
         ffpa.attn(qb, kb, kb, enable_gqa=True)
 
 
+def test_strided_views_the_kernels_cannot_address_are_copied():
+    """attn reads a strided view in place only when ffpa_check_strided_args accepts its layout; a view
+    whose row stride or span exceeds the kernels' 32-bit buffer offsets goes through contiguous copies
+    (the dense entry takes those) instead of failing."""
+    B, H, N, D = 1, 64, 131072, 128
+    ptrs = [Q, K, V, O]
+    bnhd = [0, D, H * D]  # [B, N, H, D] storage seen as [B, H, N, D]: row stride H * D
+    assert ffpa._strided_plan(ptrs, [bnhd] * 4, B, H, H, N, N, D, ffpa.FFPA_BF16) is None
+    small = [0, D, 8 * D]
+    lay = ffpa._strided_plan(ptrs, [small] * 4, B, 8, 8, 300, 300, D, ffpa.FFPA_BF16)
+    assert lay is not None and list(lay.q) == small and list(lay.o) == small
+    # K and V with different row strides: also copied
+    assert ffpa._strided_plan(ptrs, [small, small, [0, D, 16 * D], small], B, 8, 8, 300, 300, D,
+                              ffpa.FFPA_BF16) is None
+
+
 # ---- packed variable-length entry (ffpa_fwd_varlen)
 CQ, CK = 0x70_0000_0000, 0x80_0000_0000
 
@@ -155,7 +187,7 @@ def vcheck(B=3, Hq=4, Hkv=2, Tq=300, Tk=500, mq=200, mk=300, D=512, scale=math.n
 
 def test_varlen_valid_arguments_pass():
     assert vcheck() == ffpa.OK and detail() == ""
-    for D in range(64, 1025, 64):
+    for D in range(8, 1025, 8):
         assert vcheck(D=D) == ffpa.OK, D
     assert vcheck(causal=True, mq=500, mk=10) == ffpa.OK   # fewer keys than queries is allowed
     assert vcheck(Tq=0, Tk=0, mq=0, mk=0, q=None, k=None, v=None, o=None) == ffpa.OK
@@ -177,7 +209,7 @@ def test_varlen_valid_arguments_pass():
     (dict(o=O + 8), ffpa.ERR_VALUE),
     (dict(o=Q + 64), ffpa.ERR_VALUE),          # o overlaps q
     (dict(o=CQ - 64), ffpa.ERR_VALUE),         # o overlaps the offsets
-    (dict(D=96), ffpa.ERR_UNSUPPORTED),
+    (dict(D=100), ffpa.ERR_UNSUPPORTED),
     (dict(mk=1 << 20, Hkv=4, Hq=4, D=1024), ffpa.ERR_UNSUPPORTED),  # one sequence's K rows beyond 2 GiB
 ])
 def test_varlen_argument_errors(kw, status):
