@@ -20,6 +20,9 @@ query row r of batch b and query head h, with kv head ``h // (Hq // Hkv)``,
 ``scale=None`` means 1/sqrt(D).  A boolean mask excludes keys whose entry is
 false.  A row with every key excluded gets O = 0 and LSE = -inf.
 
+``attention_rows_fp8`` takes fp8 e4m3 inputs with per-head dequantisation factors and computes the
+same attention over the values they stand for.
+
 ``attention_varlen`` is the packed variable-length form (same page,
 ``ffpa_attn_varlen_func``): sequence b of a batch packed as [T, H, D] holds
 query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens cu_k[b] .. cu_k[b+1]-1 and
@@ -79,6 +82,12 @@ def _load():
     lib.oracle_attn_rows.argtypes = [p, p, p, p, ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                      ctypes.c_double, ctypes.c_int, ctypes.c_int, p, i64, p, p, p, ctypes.c_int,
                                      ctypes.c_int]
+    lib.oracle_attn_rows_e4m3.restype = ctypes.c_int
+    lib.oracle_attn_rows_e4m3.argtypes = [p, p, p, p, p, p, p, ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, i64,
+                                          i64, i64, ctypes.c_double, ctypes.c_int, p, i64, p, p, p, ctypes.c_int,
+                                          ctypes.c_int]
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
     lib.oracle_causal_visible.restype = i64
     lib.oracle_causal_visible.argtypes = [i64, i64, i64]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -179,6 +188,75 @@ def attention_rows(q, k, v, rows: Sequence[int], mask=None, scale: Optional[floa
                               ptr(P), int(threads), int(fault))
     if rc != 0:
         raise RuntimeError(f"oracle_attn_rows failed with code {rc}")
+    return (O, L, P) if want_probs else (O, L)
+
+
+# Planted-mistake switches of the fp8 dequantisation (tests of its pins only).
+Q8_FAULT_KSCALE_QHEAD = 101  # K's factor taken at the query head's index
+Q8_FAULT_NO_VSCALE = 102     # V's factor left out
+Q8_FAULT_DIVIDE = 103        # the factors divide instead of multiply
+
+
+def e4m3_value(code: int) -> float:
+    """The value of one fp8 e4m3 (OCP "e4m3fn") code, as the oracle widens it."""
+    return float(_load().oracle_e4m3_value(code))
+
+
+def _bytes8(t) -> np.ndarray:
+    """Raw bytes of an fp8 e4m3 torch tensor (or a uint8 numpy array)."""
+    if isinstance(t, np.ndarray):
+        if t.dtype != np.uint8:
+            raise TypeError("numpy fp8 inputs must hold raw uint8 codes")
+        return np.ascontiguousarray(t)
+    import torch
+
+    if t.dtype != torch.float8_e4m3fn:
+        raise TypeError(f"fp8 oracle inputs must be float8_e4m3fn, got {t.dtype}")
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy()
+
+
+def _factors(f, n: int):
+    if f is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(f.detach().cpu().numpy() if hasattr(f, "detach") else f, dtype=np.float32))
+    if a.size != n:
+        raise ValueError(f"descale factors must hold {n} values")
+    return a.reshape(-1)
+
+
+def attention_rows_fp8(q, k, v, rows: Sequence[int], q_descale=None, k_descale=None, v_descale=None, mask=None,
+                       scale: Optional[float] = None, is_causal: bool = False, want_probs: bool = False,
+                       threads: int = 0, fault: int = FAULT_NONE):
+    """Selected rows of exact attention over fp8 e4m3 inputs in fp64.
+
+    q [B, Hq, Nq, D], k and v [B, Hkv, Nkv, D] are float8_e4m3fn tensors (or uint8 code arrays);
+    q_descale [B, Hq], k_descale and v_descale [B, Hkv] (fp32; None = 1) are per-head factors: the
+    tensor taking part in the attention holds descale[b, head] times each element's e4m3 value.
+    Everything else is as in ``attention_rows`` (``scale=None`` means 1/sqrt(D)).
+    """
+    lib = _load()
+    B, Hq, Nq, D = (int(x) for x in q.shape)
+    Bk, Hkv, Nkv, Dk = (int(x) for x in k.shape)
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or Dk != D:
+        raise ValueError("q/k/v shapes are inconsistent")
+    qb, kb, vb = _bytes8(q), _bytes8(k), _bytes8(v)
+    fq, fk, fv = _factors(q_descale, B * Hq), _factors(k_descale, B * Hkv), _factors(v_descale, B * Hkv)
+    if scale is None or (isinstance(scale, float) and math.isnan(scale)):
+        scale = 1.0 / math.sqrt(D)
+    marr, mkind, ms = _mask_args(mask, B, Hq, Nq, Nkv)
+    rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    n = rows_arr.size
+    if n and (rows_arr.min() < 0 or rows_arr.max() >= B * Hq * Nq):
+        raise ValueError("row index out of range")
+    O = np.zeros((n, D), dtype=np.float64)
+    L = np.zeros((n,), dtype=np.float64)
+    P = np.zeros((n, Nkv), dtype=np.float64) if want_probs else None
+    ptr = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    rc = lib.oracle_attn_rows_e4m3(ptr(qb), ptr(kb), ptr(vb), ptr(fq), ptr(fk), ptr(fv), ptr(marr), mkind, ms[0], ms[1],
+                                   ms[2], ms[3], B, Hq, Hkv, Nq, Nkv, D, float(scale), int(bool(is_causal)),
+                                   ptr(rows_arr), n, ptr(O), ptr(L), ptr(P), int(threads), int(fault))
+    if rc != 0:
+        raise RuntimeError(f"oracle_attn_rows_e4m3 failed with code {rc}")
     return (O, L, P) if want_probs else (O, L)
 
 

@@ -32,8 +32,14 @@
  * by the convention documented with the build its output row is 0 and its
  * LSE is -inf.
  *
- * Inputs are the raw 16-bit patterns of bf16 or fp16 values; both widen to
- * double exactly.  Built without fast-math so IEEE infinities behave.
+ * Inputs are the raw 16-bit patterns of bf16 or fp16 values, or the bytes of
+ * fp8 e4m3 values (the FP8 attention of the ffpa-attn README, "Latest News"
+ * and "End-to-End Inference"), all of which widen to double exactly.  fp8
+ * inputs come with per-head dequantisation factors (the "scale folding" the
+ * skill descriptions on the skillsmp page name): the value a byte stands
+ * for is descale[b, head] times its e4m3 value, and the attention above is
+ * taken over those values.  Built without fast-math so IEEE infinities
+ * behave.
  */
 #include <math.h>
 #include <stdint.h>
@@ -43,7 +49,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_BF16 = 0, OR_FP16 = 1 };
+enum { OR_BF16 = 0, OR_FP16 = 1, OR_E4M3 = 2 };
 enum { OR_MASK_NONE = 0, OR_MASK_BOOL_U8 = 1, OR_MASK_ADD_F32 = 2, OR_MASK_ADD_BF16 = 3, OR_MASK_ADD_FP16 = 4 };
 
 /* Planted-mistake switches, used only by the tests that show the oracle's
@@ -81,7 +87,32 @@ static double widen_fp16(uint16_t h) {
   return sign ? -mag : mag;
 }
 
-static double widen(uint16_t h, int dtype) { return dtype == OR_FP16 ? widen_fp16(h) : widen_bf16(h); }
+/* OCP 8-bit floating point E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+ * no infinities; exponent 15 with fraction 7 is NaN; exponent 0 holds the subnormals f * 2^-9. */
+static double widen_e4m3(uint8_t x) {
+  int sign = (x >> 7) & 1;
+  int e = (x >> 3) & 0xf;
+  int f = x & 0x7;
+  double mag;
+  if (e == 0)
+    mag = ldexp((double)f, -9); /* f/8 * 2^(1-7) */
+  else if (e == 15 && f == 7)
+    mag = NAN;
+  else
+    mag = ldexp((double)(f | 0x8), e - 10); /* (1 + f/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+double oracle_e4m3_value(uint8_t x) { return widen_e4m3(x); }
+
+/* Element i of a tensor of the given format, widened exactly. */
+static double elem(const void* base, int64_t i, int dtype) {
+  switch (dtype) {
+    case OR_FP16: return widen_fp16(((const uint16_t*)base)[i]);
+    case OR_E4M3: return widen_e4m3(((const uint8_t*)base)[i]);
+    default: return widen_bf16(((const uint16_t*)base)[i]);
+  }
+}
 
 /* The bias mu(b,h,r,k) of the mask, or 0 / -inf for a boolean mask. */
 static double mask_term(const void* mask, int kind, int64_t off) {
@@ -93,6 +124,26 @@ static double mask_term(const void* mask, int kind, int64_t off) {
     default: return 0.0;
   }
 }
+
+/* Planted mistakes of the fp8 dequantisation (tests of its pins only). */
+enum {
+  OR_FAULT_Q8_KSCALE_QHEAD = 101, /* K's factor taken at the query head's index, not its KV head's */
+  OR_FAULT_Q8_NO_VSCALE = 102,    /* V's factor left out */
+  OR_FAULT_Q8_DIVIDE = 103        /* the factors divide instead of multiply */
+};
+
+/* The per-head factor of tensor t for (b, head); NULL means 1. */
+static double factor(const float* f, int64_t b, int64_t heads, int64_t head, int fault) {
+  if (f == NULL) return 1.0;
+  const double x = (double)f[b * heads + head];
+  return fault == OR_FAULT_Q8_DIVIDE ? 1.0 / x : x;
+}
+
+static int attn_rows(const void* q, const void* k, const void* v, const float* q_f, const float* k_f,
+                     const float* v_f, const void* mask, int mask_kind, int64_t msb, int64_t msh, int64_t msq,
+                     int64_t msk, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     double scale, int is_causal, int dtype, const int64_t* rows, int64_t nrows, double* O_out,
+                     double* LSE_out, double* P_out, int nthreads, int fault);
 
 /*
  * Computes the rows listed in `rows` (flat indices (b*Hq + h)*Nq + r).
@@ -106,8 +157,28 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
                      int64_t Nq, int64_t Nkv, int64_t D, double scale, int is_causal, int dtype,
                      const int64_t* rows, int64_t nrows, double* O_out, double* LSE_out, double* P_out,
                      int nthreads, int fault) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1 || Hq % Hkv != 0) return -1;
   if (dtype != OR_BF16 && dtype != OR_FP16) return -1;
+  return attn_rows(q, k, v, NULL, NULL, NULL, mask, mask_kind, msb, msh, msq, msk, B, Hq, Hkv, Nq, Nkv, D, scale,
+                   is_causal, dtype, rows, nrows, O_out, LSE_out, P_out, nthreads, fault);
+}
+
+/* The same rows for fp8 e4m3 inputs (bytes) with per-head factors q_f [B, Hq], k_f and v_f [B, Hkv]
+ * (NULL: 1): the attention of the tensors whose elements are factor * e4m3 value. */
+int oracle_attn_rows_e4m3(const uint8_t* q, const uint8_t* k, const uint8_t* v, const float* q_f,
+                          const float* k_f, const float* v_f, const void* mask, int mask_kind, int64_t msb,
+                          int64_t msh, int64_t msq, int64_t msk, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                          int64_t Nkv, int64_t D, double scale, int is_causal, const int64_t* rows, int64_t nrows,
+                          double* O_out, double* LSE_out, double* P_out, int nthreads, int fault) {
+  return attn_rows(q, k, v, q_f, k_f, v_f, mask, mask_kind, msb, msh, msq, msk, B, Hq, Hkv, Nq, Nkv, D, scale,
+                   is_causal, OR_E4M3, rows, nrows, O_out, LSE_out, P_out, nthreads, fault);
+}
+
+static int attn_rows(const void* q, const void* k, const void* v, const float* q_f, const float* k_f,
+                     const float* v_f, const void* mask, int mask_kind, int64_t msb, int64_t msh, int64_t msq,
+                     int64_t msk, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D,
+                     double scale, int is_causal, int dtype, const int64_t* rows, int64_t nrows, double* O_out,
+                     double* LSE_out, double* P_out, int nthreads, int fault) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1 || Hq % Hkv != 0) return -1;
   if (mask_kind != OR_MASK_NONE && mask == NULL) return -1;
   const int64_t group = Hq / Hkv;
   const int64_t shift = Nkv - Nq; /* tail alignment of the causal mask */
@@ -130,10 +201,14 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
       const int64_t h = (idx / Nq) % Hq;
       const int64_t b = idx / (Nq * Hq);
       const int64_t hk = fault == OR_FAULT_HEAD_MODULO ? h % Hkv : h / group;
-      const uint16_t* qp = q + ((b * Hq + h) * Nq + r) * D;
-      const uint16_t* kp = k + (b * Hkv + hk) * Nkv * D;
-      const uint16_t* vp = v + (b * Hkv + hk) * Nkv * D;
-      for (int64_t d = 0; d < D; ++d) qrow[d] = widen(qp[d], dtype);
+      const int64_t qp = ((b * Hq + h) * Nq + r) * D; /* element offsets of the row and of the KV head */
+      const int64_t kp = (b * Hkv + hk) * Nkv * D;
+      const int64_t vp = kp;
+      /* per-head dequantisation factors (1 for 16-bit inputs, whose elements are used as they are) */
+      const double fq = factor(q_f, b, Hq, h, fault);
+      const double fk = fault == OR_FAULT_Q8_KSCALE_QHEAD ? factor(k_f, b, Hq, h, fault) : factor(k_f, b, Hkv, hk, fault);
+      const double fv = fault == OR_FAULT_Q8_NO_VSCALE ? 1.0 : factor(v_f, b, Hkv, hk, fault);
+      for (int64_t d = 0; d < D; ++d) qrow[d] = elem(q, qp + d, dtype) * fq;
       int64_t nk = fault == OR_FAULT_DROP_LAST_KEY && Nkv > 1 ? Nkv - 1 : Nkv;
       const int64_t last_visible = fault == OR_FAULT_TOPLEFT_CAUSAL ? r : r + shift;
 
@@ -145,8 +220,8 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
           logit = -INFINITY;
         } else {
           double dot = 0.0;
-          const uint16_t* krow = kp + kk * D;
-          for (int64_t d = 0; d < D; ++d) dot += qrow[d] * widen(krow[d], dtype);
+          const int64_t krow = kp + kk * D;
+          for (int64_t d = 0; d < D; ++d) dot += qrow[d] * (elem(k, krow + d, dtype) * fk);
           double mu = mask_kind ? mask_term(mask, mask_kind, b * msb + h * msh + r * msq + kk * msk) : 0.0;
           logit = fault == OR_FAULT_MASK_BEFORE_SCALE ? scale * (dot + mu) : scale * dot + mu;
         }
@@ -174,10 +249,10 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, co
         if (p == 0.0) continue;
         if (fault == OR_FAULT_V_TRANSPOSED) {
           /* reads V as if it were stored [D][Nkv] (only meaningful when D == Nkv) */
-          for (int64_t d = 0; d < D; ++d) orow[d] += p * widen(vp[(d % Nkv) * D + (kk % D)], dtype);
+          for (int64_t d = 0; d < D; ++d) orow[d] += p * (elem(v, vp + (d % Nkv) * D + (kk % D), dtype) * fv);
         } else {
-          const uint16_t* vrow = vp + kk * D;
-          for (int64_t d = 0; d < D; ++d) orow[d] += p * widen(vrow[d], dtype);
+          const int64_t vrow = vp + kk * D;
+          for (int64_t d = 0; d < D; ++d) orow[d] += p * (elem(v, vrow + d, dtype) * fv);
         }
       }
     }
