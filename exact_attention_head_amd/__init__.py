@@ -7,7 +7,8 @@ with the semantics of ffpa_attn_func on the ffpa-attn "API Reference" page: SDPA
 additive floating masks, scale = 1/sqrt(D) by default, and SDPA-style attention dropout
 (dropout_p: keep decisions drawn on the GPU by Philox4x32-10, or given).  ``attn_varlen`` is the packed
 variable-length form of ffpa_attn_varlen_func on the same page: THD tensors [T, H, D], cumulative
-sequence offsets, the longest lengths, and an [Hq, Tq] LSE.
+sequence offsets, the longest lengths, and an [Hq, Tq] LSE.  ``attn_fp8`` is the FP8 attention of
+the README: e4m3 tensors with per-head dequantisation factors, both products on the fp8 matrix core.
 
 Everything here is argument marshalling around the C ABI of ``libffpa.so`` (include/ffpa.h):
 tensors are passed by device pointer, outputs are allocated with torch, and the work is enqueued
@@ -21,7 +22,7 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn", "attn_varlen", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
+__all__ = ["attn", "attn_varlen", "attn_fp8", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
            "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
            "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_head_dim", "kernel_name", "FFPA_BF16", "FFPA_FP16",
@@ -38,7 +39,7 @@ EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_erro
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
             "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout",
-            "ffpa_kernel_head_dim")
+            "ffpa_kernel_head_dim", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fp8_kernel_head_dim")
 
 
 class MaskDesc(ctypes.Structure):
@@ -81,6 +82,13 @@ def library() -> ctypes.CDLL:
     lib.ffpa_kernel_name.restype = ctypes.c_char_p
     lib.ffpa_kernel_head_dim.argtypes = [i64]
     lib.ffpa_kernel_head_dim.restype = i64
+    fargs = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, i64, i64, i64, i64, i64, i64, f32, i32, i32]
+    lib.ffpa_fwd_fp8.argtypes = fargs + [p]
+    lib.ffpa_fwd_fp8.restype = i32
+    lib.ffpa_check_fp8_args.argtypes = fargs
+    lib.ffpa_check_fp8_args.restype = i32
+    lib.ffpa_fp8_kernel_head_dim.argtypes = [i64]
+    lib.ffpa_fp8_kernel_head_dim.restype = i64
     vargs = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32]
     lib.ffpa_fwd_varlen.argtypes = vargs + [p]
     lib.ffpa_fwd_varlen.restype = i32
@@ -127,6 +135,21 @@ def ffpa_fwd(q, k, v, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv, D, 
     m = ctypes.byref(mask) if mask is not None else None
     return library().ffpa_fwd(q, k, v, m, o, lse, B, Hq, Hkv, Nq, Nkv, D, ctypes.c_float(scale), int(is_causal),
                               dtype, stream)
+
+
+def ffpa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq, Nkv,
+                 D, scale, is_causal, out_dtype, stream) -> int:
+    """The raw fp8 entry point: pointers are integers (device addresses, None for absent factors)."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, m, o, lse, B, Hq, Hkv, Nq, Nkv, D,
+                                  ctypes.c_float(scale), int(is_causal), out_dtype, stream)
+
+
+def ffpa_check_fp8_args(q, k, v, q_descale, k_descale, v_descale, mask: Optional[MaskDesc], o, lse, B, Hq, Hkv, Nq,
+                        Nkv, D, scale, is_causal, out_dtype) -> int:
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_check_fp8_args(q, k, v, q_descale, k_descale, v_descale, m, o, lse, B, Hq, Hkv, Nq, Nkv, D,
+                                         ctypes.c_float(scale), int(is_causal), out_dtype)
 
 
 def ffpa_dropout_keep(keep, B, Hq, Nq, Nkv, p, seed, offset, stream) -> int:
@@ -362,6 +385,63 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     if o is not o_user:
         o_user.copy_(o)
     return (o_user, lse) if return_lse else o_user
+
+
+def attn_fp8(query, key, value, q_descale=None, k_descale=None, v_descale=None, attn_mask=None,
+             is_causal: bool = False, scale: Optional[float] = None, enable_gqa: bool = False,
+             return_lse: bool = False, out_dtype=None, out=None):
+    """FP8 attention forward (ffpa_fwd_fp8).  query [B, Hq, Nq, D], key/value [B, Hkv, Nkv, D] are
+    torch.float8_e4m3fn tensors on the GPU; q_descale [B, Hq], k_descale and v_descale [B, Hkv] are
+    positive float32 per-head dequantisation factors (None = 1), so that the attention runs over
+    descale * tensor.  O is returned in out_dtype (torch.bfloat16 by default, or torch.float16), and
+    with return_lse also the fp32 [B, Hq, Nq] LSE.  Other arguments as for ``attn``; 16 <= D <= 512
+    with D % 16 == 0.  Non-contiguous inputs are copied to contiguous ones first."""
+    import torch
+
+    for name, t in (("query", query), ("key", key), ("value", value)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, H, N, D]")
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{name} dtype {t.dtype} is not float8_e4m3fn")
+    if not (query.is_cuda and key.device == query.device and value.device == query.device):
+        raise ValueError("query, key and value must live on the same GPU")
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"out_dtype {out_dtype} is neither bfloat16 nor float16")
+    B, Hq, Nq, D = query.shape
+    Bk, Hkv, Nkv, Dk = key.shape
+    if tuple(value.shape) != tuple(key.shape) or Bk != B or Dk != D:
+        raise ValueError("query, key and value disagree on [B, H, N, D]")
+    if Hq != Hkv and not enable_gqa:
+        raise ValueError("Hq != Hkv needs enable_gqa=True")
+    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+    facs = []
+    for name, f, heads in (("q_descale", q_descale, Hq), ("k_descale", k_descale, Hkv), ("v_descale", v_descale, Hkv)):
+        if f is None:
+            facs.append(None)
+            continue
+        if not isinstance(f, torch.Tensor) or f.numel() != B * heads:
+            raise ValueError(f"{name} must hold B * heads = {B * heads} factors")
+        facs.append(f.to(device=query.device, dtype=torch.float32).contiguous())
+    if out is None:
+        o = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=query.device)
+    else:
+        if tuple(out.shape) != (B, Hq, Nq, D) or out.dtype != out_dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous [B, Hq, Nq, D] tensor of out_dtype")
+        o = out
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=query.device) if return_lse else None
+    desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(query.device), B, Hq, Nq, Nkv)
+    sc = math.nan if scale is None else float(scale)
+    with torch.cuda.device(query.device):
+        stream = torch.cuda.current_stream(query.device).cuda_stream
+        st = ffpa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), *[f.data_ptr() if f is not None else None
+                                                                     for f in facs],
+                          desc, o.data_ptr(), lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Nq, Nkv, D, sc,
+                          bool(is_causal), FFPA_BF16 if out_dtype == torch.bfloat16 else FFPA_FP16, stream)
+    del keep, facs
+    if st != OK:
+        _raise(st)
+    return (o, lse) if return_lse else o
 
 
 def _attn_dropout(q, k, v, o, out, lse, desc, mask_keep, B, Hq, Hkv, Nq, Nkv, D, sc, is_causal, dtype, p, seed,

@@ -23,12 +23,22 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-result", "-I", os.path.join(PKG, "..", "include")]
 
 
-def head_dims() -> list[int]:
+def _dims(macro: str) -> list[int]:
     with open(os.path.join(CSRC, "ffpa_launch.hpp")) as f:
         txt = f.read()
-    body = txt[txt.index("#define FFPA_FOR_EACH_D(X)"):]
-    body = body[:body.index("\n\n")]
+    body = txt[txt.index(f"#define {macro}(X)"):]
+    body = body[:body.index("\n")] if macro == "FFPA_FP8_FOR_EACH_D" else body[:body.index("\n\n")]
     return [int(x) for x in re.findall(r"X\((\d+)\)", body)]
+
+
+def head_dims() -> list[int]:
+    """Head dims with compiled 16-bit kernels."""
+    return _dims("FFPA_FOR_EACH_D")
+
+
+def fp8_head_dims() -> list[int]:
+    """Head dims with compiled fp8 kernels."""
+    return _dims("FFPA_FP8_FOR_EACH_D")
 
 
 def _compile(src: str, obj: str, defines: list[str], remarks: bool = False) -> tuple[str, str]:
@@ -96,6 +106,10 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
                 tasks.append((os.path.join(CSRC, "ffpa_inst.hip"),
                               os.path.join(BUILD, f"ffpa_{tag.lower()}_d{d}" + (f"_p{part}" if part else "") + ".o"),
                               [f"-DFFPA_INST_T={tag}", f"-DFFPA_INST_D={d}", f"-DFFPA_INST_PART={part}"]))
+    # the fp8 forward: one object per head dim
+    for d in fp8_head_dims():
+        tasks.append((os.path.join(CSRC, "ffpa_fp8.hip"), os.path.join(BUILD, f"ffpa_fp8_d{d}.o"),
+                      [f"-DFFPA_FP8_D={d}"]))
     # largest kernels first
     kd = lambda path: re.search(r"_d(\d+)(_p\d)?\.o$", path)  # per-head-dim kernel objects
     tasks.sort(key=lambda t: -int(kd(t[1]).group(1)) if kd(t[1]) else 0)

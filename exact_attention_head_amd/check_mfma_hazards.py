@@ -5,8 +5,8 @@ which the compiler's hazard recognizer and wait-count pass do not see into.  The
 checked here over the generated assembly of every kernel:
 
 1. After a v_mfma writes its destination registers, no other instruction may read or write them for
-   12 wait states (one per issued instruction, N+1 per s_nop N) - except another v_mfma accumulating
-   into exactly the same registers.
+   12 wait states (one per issued instruction, N+1 per s_nop N), 20 after the 16-pass fp8 product
+   v_mfma_f32_32x32x64_f8f6f4 - except another v_mfma accumulating into exactly the same registers.
 2. A VALU write of a register needs 2 wait states before a v_mfma reads it as an operand.
 3. The destination of an LDS read (ds_read*, also when issued from inline assembly) is valid only
    after an s_waitcnt lgkmcnt(N) that covers it: LDS returns in order, so lgkmcnt(N) completes a
@@ -25,8 +25,13 @@ import re
 import sys
 
 MFMA_RESULT_WAIT = 12
+MFMA_RESULT_WAIT_16PASS = 20  # 64-cycle products (the fp8 32x32x64 form)
 VALU_TO_MFMA_WAIT = 2
 REG = re.compile(r"\b([va])\[(\d+):(\d+)\]|\b([va])(\d+)\b")
+
+
+def mfma_result_wait(op: str) -> int:
+    return MFMA_RESULT_WAIT_16PASS if "32x32x64" in op or "16x16x128" in op else MFMA_RESULT_WAIT
 
 
 def regs(text: str) -> frozenset:
@@ -144,7 +149,7 @@ def check_function(path: str, name: str, body) -> list:
                 hit = wr & touched
                 if hit and not (is_mfma and ops and ops[0] == dst and len(ops) > 3 and ops[3] == dst):
                     problems.add(f"{path}:{lineno}: {name}: '{line}' touches {sorted(hit)[:2]} written by "
-                                 f"'{text}' {MFMA_RESULT_WAIT - rem} wait states earlier")
+                                 f"'{text}' {mfma_result_wait(text.split()[0]) - rem} wait states earlier")
             # rule 2
             if is_mfma and len(ops) > 1:
                 srcs = frozenset().union(*[regs(o) for o in ops[1:]])
@@ -165,7 +170,7 @@ def check_function(path: str, name: str, body) -> list:
             if op.startswith("ds_"):
                 state.tr = {k: v + 1 for k, v in state.tr.items()}
             if is_mfma and ops:
-                state.mfma[(regs(ops[0]), ops[0], line)] = MFMA_RESULT_WAIT
+                state.mfma[(regs(ops[0]), ops[0], line)] = mfma_result_wait(op)
             elif op.startswith("v_") and ops:
                 state.valu[(regs(ops[0]), line)] = VALU_TO_MFMA_WAIT
             if op.startswith("ds_read") and ops:

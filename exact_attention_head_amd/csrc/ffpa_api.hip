@@ -116,11 +116,19 @@ int check_layout(const ffpa_layout_t* lay, int64_t Hq, int64_t Nq, int64_t Nkv, 
   return FFPA_OK;
 }
 
+// Head dim of the fp8 kernel that serves D (the next multiple of 128 from 128 to 512), 0 if none.
+int64_t fp8_kernel_dim(int64_t D) {
+  if (D < 16 || D > 512 || D % 16 != 0) return 0;
+  return (D + 127) / 128 * 128;
+}
+
+// fp8: q, k and v hold e4m3 bytes (one byte per element) and dtype is the output's element type.
 int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, const void* o, const float* lse,
           int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
-          int dtype, const ffpa_layout_t* lay = nullptr) {
+          int dtype, const ffpa_layout_t* lay = nullptr, bool fp8 = false) {
   g_detail[0] = '\0';
-  if (dtype != FFPA_BF16 && dtype != FFPA_FP16) return fail(FFPA_ERR_TYPE, "dtype %d is neither bf16 nor fp16", dtype);
+  if (dtype != FFPA_BF16 && dtype != FFPA_FP16)
+    return fail(FFPA_ERR_TYPE, "%s %d is neither bf16 nor fp16", fp8 ? "out_dtype" : "dtype", dtype);
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1)
     return fail(FFPA_ERR_VALUE, "every size must be >= 1 (B=%lld Hq=%lld Hkv=%lld Nq=%lld Nkv=%lld D=%lld)",
                 (long long)B, (long long)Hq, (long long)Hkv, (long long)Nq, (long long)Nkv, (long long)D);
@@ -135,10 +143,13 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15)
     return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
   if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
-  if (D > 1024 || kernel_dim(D) == 0)
+  if (fp8 && fp8_kernel_dim(D) == 0)
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: the fp8 kernels cover 16 <= D <= 512 with D %% 16 == 0",
+                (long long)D);
+  if (!fp8 && (D > 1024 || kernel_dim(D) == 0))
     return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
   // grid size and 32-bit in-kernel indexing
-  const int br = rows_for(kernel_dim(D));
+  const int br = fp8 ? 128 : rows_for(kernel_dim(D));
   const int64_t nqt = (Nq + br - 1) / br;
   if (B * Hq * nqt > 0x7fffffffLL) return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
   if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B * Hq > (1LL << 30) || B * Hkv > (1LL << 30))
@@ -149,10 +160,10 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
     const int st = check_layout(lay, Hq, Nq, Nkv, D, B);
     if (st != FFPA_OK) return st;
   }
-  const size_t esz = 2;
+  const size_t esz = fp8 ? 1 : 2;
   // byte extents of the tensors (for a strided layout: from the first to one past the last element)
   size_t qbytes = (size_t)(B * Hq * Nq * D) * esz, kbytes = (size_t)(B * Hkv * Nkv * D) * esz;
-  size_t vbytes = kbytes, obytes = qbytes;
+  size_t vbytes = kbytes, obytes = (size_t)(B * Hq * Nq * D) * 2;
   if (lay != nullptr) {
     qbytes = (size_t)extent(lay->q, B, Hq, Nq, D) * esz;
     kbytes = (size_t)extent(lay->k, B, Hkv, Nkv, D) * esz;
@@ -436,6 +447,81 @@ int ffpa_check_cu_seqlens(const int32_t* cu_host, int64_t B, int64_t T, int64_t 
     return fail(FFPA_ERR_VALUE, "cu_seqlens[B] is %d, not the token count %lld", (int)cu_host[B], (long long)T);
   return FFPA_OK;
 }
+
+int ffpa_check_fp8_args(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                        const float* v_descale, const ffpa_mask_t* mask, const void* o, const float* lse, int64_t B,
+                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
+                        int out_dtype) {
+  const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, out_dtype, nullptr, true);
+  if (st != FFPA_OK) return st;
+  const float* f[3] = {q_descale, k_descale, v_descale};
+  const int64_t heads[3] = {Hq, Hkv, Hkv};
+  const size_t obytes = (size_t)(B * Hq * Nq * D) * 2, lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
+  for (int t = 0; t < 3; ++t) {
+    if (f[t] == nullptr) continue;
+    if ((uintptr_t)f[t] & 3) return fail(FFPA_ERR_VALUE, "descale factors must be 4-byte aligned");
+    const size_t fb = (size_t)(B * heads[t]) * 4;
+    if (ranges_overlap(o, obytes, f[t], fb) || ranges_overlap(lse, lbytes, f[t], fb))
+      return fail(FFPA_ERR_VALUE, "o and lse must not overlap the descale factors");
+  }
+  return FFPA_OK;
+}
+
+int ffpa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                 const float* v_descale, const ffpa_mask_t* mask, void* o, float* lse, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int out_dtype,
+                 void* stream) {
+  const int st = ffpa_check_fp8_args(q, k, v, q_descale, k_descale, v_descale, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D,
+                                     scale, is_causal, out_dtype);
+  if (st != FFPA_OK) return st;
+  ffpa::FwdArgs a{};
+  a.q = (const uint16_t*)q;  // e4m3 bytes: the kernels read them as such
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.q_desc = q_descale;
+  a.k_desc = k_descale;
+  a.v_desc = v_descale;
+  a.mask_kind = ffpa::kMaskNone;
+  if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
+    const size_t msz = mask_elem_size(mask->kind);
+    a.mask = mask->data;
+    a.mask_kind = mask->kind;
+    a.msb = mask->stride_b;
+    a.msh = mask->stride_h;
+    a.msq = mask->stride_q;
+    const bool aligned = ((uintptr_t)mask->data % (4 * msz)) == 0;
+    a.mask_vec = aligned && (a.msb % 4 == 0) && (a.msh % 4 == 0) && (a.msq % 4 == 0);
+  }
+  a.B = (int)B;
+  a.Hq = (int)Hq;
+  a.Hkv = (int)Hkv;
+  a.Nq = (int)Nq;
+  a.Nkv = (int)Nkv;
+  a.group = (int)(Hq / Hkv);
+  a.dcols = (int)D;
+  a.q_sr = a.kv_sr = (int)D;  // bytes per Q/K/V row
+  a.o_sr = (int)D;            // elements per O row
+  const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.causal = is_causal;
+  const hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipErrorInvalidValue;
+  switch (fp8_kernel_dim(D)) {
+#define FFPA_FP8_CASE(Dv)                                                                                         \
+  case Dv:                                                                                                        \
+    e = out_dtype == FFPA_BF16 ? ffpa::launch_fwd_fp8<ffpa::Bf16, Dv>(a, s) : ffpa::launch_fwd_fp8<ffpa::Fp16, Dv>(a, s); \
+    break;
+    FFPA_FP8_FOR_EACH_D(FFPA_FP8_CASE)
+#undef FFPA_FP8_CASE
+    default: break;
+  }
+  if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FFPA_OK;
+}
+
+int64_t ffpa_fp8_kernel_head_dim(int64_t D) { return fp8_kernel_dim(D); }
 
 const char* ffpa_status_string(int status) {
   switch (status) {

@@ -104,6 +104,11 @@ struct FwdArgs {
   // compiled head dim, runtime-layout variants only) the columns from dcols on are padding: Q reads
   // zeros there, so K's padding columns add nothing to S, and O is stored up to dcols only.
   int dcols;
+  // fp8 forward (ffpa_fwd_fp8): per-head dequantisation factors [B, Hq] and [B, Hkv] (null: 1); q, k, v
+  // then point at e4m3 bytes, and the row strides count bytes
+  const float* q_desc;
+  const float* k_desc;
+  const float* v_desc;
   // Attention dropout (null keep: none; dense contiguous layout only).  keep is [B, Hq, Nq, keep_w]
   // 32-bit words: bit i of word w set keeps the weight of key 32 w + i for that query row; kept
   // weights are scaled by drop_scale = 1 / (1 - p) (applied to O with the 1/l normalisation).
@@ -307,6 +312,15 @@ __device__ inline i32x2 lds_read_tr_async(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
   i32x2 d;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF) : "memory");
+  return d;
+}
+// The byte form: 16 lanes read 8 rows x 16 bytes (two 8-byte halves per row); lane i of the group
+// receives column i of the 8 rows, row j in byte j (lane x addresses row x / 2, half x % 2).
+template <int OFF>
+__device__ inline i32x2 lds_read_tr8_async(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  i32x2 d;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "n"(OFF) : "memory");
   return d;
 }
 __device__ inline uint32_t lds_addr(const char* p) { return (uint32_t)(uintptr_t)(FFPA_LDS const char*)p; }

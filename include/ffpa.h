@@ -277,6 +277,58 @@ int64_t ffpa_kernel_head_dim(int64_t D);
 const char* ffpa_kernel_name(int64_t D);
 
 /*
+ * ffpa_fwd_fp8 -- enqueue the FP8 attention forward (the ffpa-attn README,
+ * "Latest News": FP8 attention for head dims 64..1024, and "End-to-End
+ * Inference": masks, causal, GQA/MQA) on the gfx950 fp8 matrix core, for
+ * head dims up to 512 (larger ones return FFPA_ERR_UNSUPPORTED).  q, k and v hold OCP e4m3 ("e4m3fn") codes, one byte per
+ * element, laid out as the 16-bit tensors of ffpa_fwd; the per-head
+ * dequantisation factors make the tensors that take part
+ *
+ *   Q' = q_descale[b, hq] * Q,  K' = k_descale[b, hk] * K,  V' = v_descale[b, hk] * V,
+ *
+ * and the result is ffpa_fwd's over them: O = softmax(scale Q' K'^T + mask) V'
+ * in out_dtype (bf16 or fp16) and the natural-log LSE in fp32.  The factors
+ * are folded into the kernels' arithmetic (the "scale folding" named on the
+ * skills page), never applied to the tensors.
+ *
+ *   q            device, [B, Hq, Nq, D] e4m3 bytes, contiguous
+ *   k, v         device, [B, Hkv, Nkv, D] e4m3 bytes, contiguous
+ *   q_descale    device, [B, Hq] float32, positive and finite; NULL = all 1
+ *   k_descale, v_descale  device, [B, Hkv] float32, positive and finite;
+ *                NULL = all 1 (other values give unspecified results: the
+ *                kernels cannot check device memory)
+ *   mask, o, lse, B, Hq, Hkv, Nq, Nkv, scale, is_causal, stream: as for ffpa_fwd
+ *   D            16 <= D <= 512, D % 16 == 0 (FFPA_ERR_UNSUPPORTED otherwise);
+ *                D not a multiple of 128 runs the next one up with padding
+ *                columns (zeros in Q, never stored in O; K and V must then
+ *                hold finite codes)
+ *   out_dtype    ffpa_dtype of o (FFPA_ERR_TYPE otherwise)
+ *
+ * Both products run on e4m3 operands with fp32 accumulation: the
+ * probabilities are rounded to e4m3 (round to nearest even) for the P V
+ * product, so O carries a relative error of about 2^-4 / sqrt(3) per weight
+ * (the tolerance the tests derive); the LSE is exact up to fp32 rounding.
+ * q, k, v and o must be 16-byte aligned, the factors 4-byte aligned; o must
+ * not overlap q, k, v, lse, the mask or the factors.  Errors as ffpa_fwd.
+ * Allocates nothing.
+ */
+int ffpa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                 const float* v_descale, const ffpa_mask_t* mask, void* o, float* lse, int64_t B, int64_t Hq,
+                 int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int out_dtype,
+                 void* stream);
+
+/* The host-side argument check ffpa_fwd_fp8 performs, without enqueuing
+ * anything. */
+int ffpa_check_fp8_args(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                        const float* v_descale, const ffpa_mask_t* mask, const void* o, const float* lse, int64_t B,
+                        int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
+                        int out_dtype);
+
+/* Head dim of the fp8 kernel serving D (128, 256, 384 or 512: the next
+ * multiple of 128), 0 for an unsupported D.  Host-only. */
+int64_t ffpa_fp8_kernel_head_dim(int64_t D);
+
+/*
  * ffpa_fwd_varlen -- enqueue the attention forward over a packed batch of
  * sequences of different lengths (ffpa-attn "API Reference" page,
  * ffpa_attn_varlen_func: packed THD layout, cumulative sequence offsets,

@@ -329,3 +329,40 @@ def test_dropout_keep_rejects_before_launching():
         assert ffpa.ffpa_dropout_keep(*args, 0, 0, None) == ffpa.ERR_VALUE
     ffpa.ffpa_dropout_keep(KEEP, 1, 1, 1, 1, 1.0, 0, 0, None)
     assert b"[0, 1)" in lib.ffpa_last_error_detail()
+
+
+# ---- fp8 entry (ffpa_fwd_fp8): host checks only
+DQ, DK, DV = 0x90_0000_0000, 0xA0_0000_0000, 0xB0_0000_0000
+
+
+def fcheck(B=1, Hq=2, Hkv=1, Nq=100, Nkv=130, D=512, scale=math.nan, causal=False, out=ffpa.FFPA_BF16, q=Q, k=K,
+           v=V, o=O, lse=L, dq=DQ, dk=DK, dv=DV, mask=None):
+    return ffpa.ffpa_check_fp8_args(q, k, v, dq, dk, dv, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, causal, out)
+
+
+def test_fp8_valid_arguments_pass():
+    assert fcheck() == ffpa.OK and detail() == ""
+    for D in range(16, 513, 16):
+        assert fcheck(D=D) == ffpa.OK, D
+    assert fcheck(dq=None, dk=None, dv=None) == ffpa.OK
+    assert fcheck(out=ffpa.FFPA_FP16, causal=True, Nq=100, Nkv=130) == ffpa.OK
+    assert fcheck(mask=mdesc(kind=ffpa.MASK_BOOL_U8)) == ffpa.OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=2), ffpa.ERR_TYPE), (dict(D=8), ffpa.ERR_UNSUPPORTED), (dict(D=520), ffpa.ERR_UNSUPPORTED),
+    (dict(D=100), ffpa.ERR_UNSUPPORTED), (dict(D=1024), ffpa.ERR_UNSUPPORTED), (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE),
+    (dict(causal=True, Nq=131, Nkv=130), ffpa.ERR_VALUE), (dict(dq=DQ + 2), ffpa.ERR_VALUE),
+    (dict(dv=O), ffpa.ERR_VALUE), (dict(q=Q + 8), ffpa.ERR_VALUE), (dict(o=Q), ffpa.ERR_VALUE),
+])
+def test_fp8_argument_errors(kw, status):
+    assert fcheck(**kw) == status, kw
+    assert detail() != ""
+
+
+def test_fp8_kernel_head_dim():
+    lib = ffpa.library()
+    for D in range(16, 513, 16):
+        assert lib.ffpa_fp8_kernel_head_dim(D) == (D + 127) // 128 * 128, D
+    for bad in (0, 8, 100, 528, 1024):
+        assert lib.ffpa_fp8_kernel_head_dim(bad) == 0

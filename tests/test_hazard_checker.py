@@ -25,6 +25,12 @@ def test_mfma_result_read_too_early(tmp_path):
     assert not _check(tmp_path, [MFMA, "s_nop 7", "s_nop 3", "v_accvgpr_read_b32 v10, a3"])  # 12
 
 
+def test_fp8_product_needs_twenty_wait_states(tmp_path):
+    f8 = "v_mfma_f32_32x32x64_f8f6f4 v[0:15], v[16:23], v[24:31], v[0:15]"
+    assert _check(tmp_path, [f8, "s_nop 7", "s_nop 3", "v_mov_b32 v40, v3"])  # 12 < 20
+    assert not _check(tmp_path, [f8, "s_nop 7", "s_nop 7", "s_nop 3", "v_mov_b32 v40, v3"])  # 20
+
+
 def test_same_destination_accumulation_is_allowed(tmp_path):
     assert not _check(tmp_path, [MFMA, MFMA])
     # a different accumulator overlapping the first destination is not
