@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5033.2  # MI355X dense fp8 MFMA (twice the 16-bit rate)
 METRIC = "forward TFLOPS + % of MI355X bf16 MFMA peak at D=512 and D=1024"
 
 
@@ -183,6 +184,35 @@ def time_dropout(w, p: float, steps: int, warmup: int):
             raise RuntimeError(f"ffpa_dropout_keep returned {st}")
 
     return timed(fwd, steps, warmup), timed(gen, steps, warmup)
+
+
+def fp8_quantize(x):
+    """Per-head e4m3 codes of a host float tensor [B, H, N, D] and the factors that undo the scaling
+    (head max |x| / 448): input preparation, outside the timed region."""
+    import torch
+
+    s = (x.float().abs().amax(dim=(2, 3)) / 448.0).clamp_min(1e-12)
+    return (x.float() / s[:, :, None, None]).to(torch.float8_e4m3fn), s.float()
+
+
+def time_fp8(w, steps: int, warmup: int):
+    """Times ffpa_fwd_fp8 on the workload's q, k, v quantised per head to e4m3 (bf16 output)."""
+    import torch
+
+    import exact_attention_head_amd as ffpa
+    import workloads as W
+
+    q, k, v, mask = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    (q8, dq), (k8, dk), (v8, dv) = (fp8_quantize(t) for t in (q, k, v))
+    qd, kd, vd, dqd, dkd, dvd = (t.to(dev) for t in (q8, k8, v8, dq, dk, dv))
+    md = mask.to(dev) if mask is not None else None
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ffpa.attn_fp8(qd, kd, vd, dqd, dkd, dvd, attn_mask=md, is_causal=w.causal, enable_gqa=w.Hq != w.Hkv, out=o)
+
+    return timed(step, steps, warmup)
 
 
 def time_varlen(w, steps: int, warmup: int, clock: bool = False):
@@ -349,7 +379,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_d_self",
-                    help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16] | varlen_causal")
+                    help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16] | varlen_causal | "
+                         "fp8:<one of those> (the fp8 forward on the workload quantised per head)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -382,9 +413,24 @@ def main() -> int:
             return W.sweep(int(parts[1]), torch.float16 if len(parts) > 2 and parts[2] == "fp16" else torch.bfloat16)
         return getattr(W, name)()
 
-    w = pick(args.workload)
-    log(f"workload {w.name}: warmup {args.warmup}, steps {args.steps}")
+    fp8_main = args.workload.startswith("fp8:")
+    w = pick(args.workload[4:] if fp8_main else args.workload)
+    log(f"workload {'fp8 ' if fp8_main else ''}{w.name}: warmup {args.warmup}, steps {args.steps}")
     packed = isinstance(w, W.VarlenWorkload)
+    if fp8_main:
+        # the fp8 forward alone (profiling runs): one JSON line against the fp8 peak, no CPU leg
+        st = time_fp8(w, args.steps, args.warmup)
+        tf = w.flops / (st["median_ms"] * 1e-3) / 1e12
+        log(f"fp8 {w.name}: median {st['median_ms']:.4f} ms/launch, {tf:.1f} TFLOPS "
+            f"({100 * tf / PEAK_FP8_TFLOPS:.1f}% of the fp8 peak)")
+        print(json.dumps({"metric": "fp8 forward TFLOPS", "value": round(tf, 2), "unit": "TFLOPS", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(st["median_ms"], 5),
+                          "higher_is_better": True, "dtype": "e4m3", "data": "synthetic",
+                          "config": dict(w.describe(), inputs="e4m3 per-head factors"),
+                          "roofline": dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS,
+                                           unit="TFLOP/s", frac=round(tf / PEAK_FP8_TFLOPS, 4),
+                                           kernel="ffpa_fwd_fp8_kernel")}), flush=True)
+        return 0
     if packed:
         st, inputs, outputs = time_varlen(w, args.steps, args.warmup, clock=True), None, None
     else:
@@ -409,14 +455,19 @@ def main() -> int:
     if args.sweep:
         names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
     else:
-        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "drop:large_d_self",
-                 "drop:sweep:1024", "bwd:large_d_self", "bwd:sweep:1024"]
+        names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "fp8:large_d_self",
+                 "fp8:sweep:512", "drop:large_d_self", "drop:sweep:1024", "bwd:large_d_self", "bwd:sweep:1024"]
     if not args.no_secondary and args.workload == "large_d_self":
         for name in names:
             backward = name.startswith("bwd:")
             dropout = name.startswith("drop:")
-            w2 = pick(name[5:] if dropout else (name[4:] if backward else name))
-            if dropout:
+            fp8 = name.startswith("fp8:")
+            w2 = pick(name[5:] if dropout else (name[4:] if backward or fp8 else name))
+            peak = PEAK_FP8_TFLOPS if fp8 else PEAK_TFLOPS
+            if fp8:
+                # e4m3 inputs with per-head factors, both products on the fp8 matrix core: against its peak
+                st2, flops2 = time_fp8(w2, max(5, args.steps // 2), 2), w2.flops
+            elif dropout:
                 # forward with attention dropout at p = 0.1: same FLOP count; the keep-word generator apart
                 st2, gst = time_dropout(w2, 0.1, max(5, args.steps // 2), 2)
                 gen_ms = gst["median_ms"]
@@ -432,14 +483,18 @@ def main() -> int:
                 (st2, _, _), flops2 = time_workload(w2, max(5, args.steps // 2), 2), w2.flops
             ms2 = st2["median_ms"]
             tf2 = flops2 / (ms2 * 1e-3) / 1e12
-            tag = ("backward " if backward else ("dropout p=0.1 " if dropout else "")) + w2.name
-            log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / PEAK_TFLOPS:.1f}% of peak)")
-            secondary.append(dict(workload=tag, D=w2.D, dtype="bf16" if w2.dtype == torch.bfloat16 else "fp16",
-                                  kernel="ffpa_bwd (library GEMMs + HIP kernels)" if backward else ffpa.kernel_name(w2.D),
+            tag = ("backward " if backward else ("dropout p=0.1 " if dropout else ("fp8 " if fp8 else ""))) + w2.name
+            log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / peak:.1f}% of the "
+                f"{'fp8' if fp8 else 'bf16'} peak)")
+            kname = ("ffpa_bwd (library GEMMs + HIP kernels)" if backward else
+                     ("ffpa_fwd_fp8_kernel" if fp8 else ffpa.kernel_name(w2.D)))
+            secondary.append(dict(workload=tag, D=w2.D,
+                                  dtype="e4m3" if fp8 else ("bf16" if w2.dtype == torch.bfloat16 else "fp16"),
+                                  kernel=kname, peak_tflops=peak,
                                   **({"keep_words_ms": round(gen_ms, 4)} if dropout else {}),
                                   ms_per_step=round(ms2, 4), min_ms=round(st2["min_ms"], 4),
                                   mean_ms=round(st2["mean_ms"], 4), tflops=round(tf2, 2),
-                                  frac_of_peak=round(tf2 / PEAK_TFLOPS, 4)))
+                                  frac_of_peak=round(tf2 / peak, 4)))
 
     cpu, parity = None, None
     if packed and not args.no_cpu_baseline:
