@@ -30,93 +30,46 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-class ClockSampler:
-    """Samples the GPU's shader (gfx) clock through the AMD SMI library in a background thread while a
-    timed region runs; reports the median of the samples in MHz (None when the library is absent or
-    refuses, e.g. without a driver)."""
-
-    def __init__(self, period_s: float = 0.002):
-        self.period, self.samples, self._h, self._thread, self._stop = period_s, [], None, None, False
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            self._smi, self._h = amdsmi, (handles[0] if handles else None)
-        except Exception:
-            self._h = None
-
-    def _read(self):
-        m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        if clks:
-            return sum(clks) / len(clks)
-        return float(self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.SYS)["clk"])
-
-    def _run(self):
-        import time as _t
-
-        while not self._stop:
-            try:
-                self.samples.append(self._read())
-            except Exception:
-                return
-            _t.sleep(self.period)
-
-    def __enter__(self):
-        if self._h is not None:
-            import threading
-
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop = True
-        if self._thread is not None:
-            self._thread.join()
-
-    def median(self):
-        if not self.samples:
-            return None
-        xs = sorted(self.samples)
-        return round(xs[len(xs) // 2], 1)
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
 def timed(fn, steps: int, warmup: int, clock: bool = False):
     """Runs fn `warmup` times untimed, then `steps` times, each launch between its own pair of HIP
     events on torch's current stream (the stream the library's calls enqueue on), with a device
     synchronisation on both sides of the timed region.  Returns per-launch statistics in ms and, with
-    clock=True, the median shader clock sampled during the timed region."""
+    clock=True, the shader clock of the timed launches: each launch's first wave of workgroup 0
+    stamps the shader-clock and 100 MHz counters at its start and end (ffpa_clock_stamps), and the
+    median over the launches of cycles / time is reported in MHz."""
     import torch
+
+    import exact_attention_head_amd as ffpa
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    sampler = ClockSampler() if clock else None
-    ctx = sampler if sampler is not None else _Null()
-    with ctx:
-        for e0, e1 in ev:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
+    stamps = torch.zeros((steps, 4), dtype=torch.int64, device="cuda") if clock else None
+    for i, (e0, e1) in enumerate(ev):
+        if clock:
+            ffpa.library().ffpa_clock_stamps(stamps[i].data_ptr())
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    if clock:
+        ffpa.library().ffpa_clock_stamps(None)
+    torch.cuda.synchronize()
     per = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     total = ev[0][0].elapsed_time(ev[-1][1])
-    return dict(median_ms=per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2]),
-                min_ms=per[0], max_ms=per[-1], mean_ms=total / steps,
-                sclk_mhz=sampler.median() if sampler is not None else None,
-                sclk_samples=len(sampler.samples) if sampler is not None else 0)
-
-
-class _Null:
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *exc):
-        return False
+    sclk = None
+    if clock:
+        st = stamps.cpu().tolist()
+        mhz = [(c1 - c0) * 100.0 / (r1 - r0) for c0, r0, c1, r1 in st if r1 > r0 and c1 > c0]
+        sclk = round(_median(mhz), 1) if mhz else None
+    return dict(median_ms=_median(per), min_ms=per[0], max_ms=per[-1], mean_ms=total / steps, sclk_mhz=sclk)
 
 
 def cpu_model() -> str:
@@ -195,7 +148,7 @@ def fp8_quantize(x):
     return (x.float() / s[:, :, None, None]).to(torch.float8_e4m3fn), s.float()
 
 
-def time_fp8(w, steps: int, warmup: int):
+def time_fp8(w, steps: int, warmup: int, clock: bool = False):
     """Times ffpa_fwd_fp8 on the workload's q, k, v quantised per head to e4m3 (bf16 output)."""
     import torch
 
@@ -212,7 +165,7 @@ def time_fp8(w, steps: int, warmup: int):
     def step():
         ffpa.attn_fp8(qd, kd, vd, dqd, dkd, dvd, attn_mask=md, is_causal=w.causal, enable_gqa=w.Hq != w.Hkv, out=o)
 
-    return timed(step, steps, warmup)
+    return timed(step, steps, warmup, clock=clock)
 
 
 def time_varlen(w, steps: int, warmup: int, clock: bool = False):
@@ -332,7 +285,8 @@ def cpu_baseline(w, inputs, outputs, seconds: float):
 
 # the forward kernels and their launcher (the C-ABI checks and the backward do not change what a
 # forward launch moves)
-KERNEL_SOURCES = ("ffpa_kernel.hpp", "ffpa_row_kernel.hpp", "ffpa_launch.hpp", "ffpa_inst.hip")
+KERNEL_SOURCES = ("ffpa_kernel.hpp", "ffpa_row_kernel.hpp", "ffpa_launch.hpp", "ffpa_inst.hip", "ffpa_fp8_kernel.hpp",
+                  "ffpa_fp8.hip")
 
 
 def kernel_fingerprint() -> str:
@@ -419,13 +373,13 @@ def main() -> int:
     packed = isinstance(w, W.VarlenWorkload)
     if fp8_main:
         # the fp8 forward alone (profiling runs): one JSON line against the fp8 peak, no CPU leg
-        st = time_fp8(w, args.steps, args.warmup)
+        st = time_fp8(w, args.steps, args.warmup, clock=True)
         tf = w.flops / (st["median_ms"] * 1e-3) / 1e12
         log(f"fp8 {w.name}: median {st['median_ms']:.4f} ms/launch, {tf:.1f} TFLOPS "
-            f"({100 * tf / PEAK_FP8_TFLOPS:.1f}% of the fp8 peak)")
+            f"({100 * tf / PEAK_FP8_TFLOPS:.1f}% of the fp8 peak), shader clock {st['sclk_mhz']} MHz")
         print(json.dumps({"metric": "fp8 forward TFLOPS", "value": round(tf, 2), "unit": "TFLOPS", "n_gpus": 1,
                           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(st["median_ms"], 5),
-                          "higher_is_better": True, "dtype": "e4m3", "data": "synthetic",
+                          "higher_is_better": True, "dtype": "e4m3", "data": "synthetic", "sclk_mhz": st["sclk_mhz"],
                           "config": dict(w.describe(), inputs="e4m3 per-head factors"),
                           "roofline": dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS,
                                            unit="TFLOP/s", frac=round(tf / PEAK_FP8_TFLOPS, 4),
@@ -439,8 +393,7 @@ def main() -> int:
     ms = st["median_ms"]
     tflops = w.flops / (ms * 1e-3) / 1e12
     log(f"{w.name}: median {ms:.4f} ms/launch (min {st['min_ms']:.4f}, mean {st['mean_ms']:.4f}), "
-        f"{tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak), sclk {st['sclk_mhz']} MHz "
-        f"({st['sclk_samples']} samples)")
+        f"{tflops:.1f} TFLOPS ({100 * tflops / PEAK_TFLOPS:.1f}% of peak), shader clock {st['sclk_mhz']} MHz")
 
     traffic = measured_traffic(args.traffic_json, w.name)
     import exact_attention_head_amd as ffpa

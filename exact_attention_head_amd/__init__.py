@@ -39,7 +39,8 @@ EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_erro
             "ffpa_kernel_name", "ffpa_fwd_varlen", "ffpa_check_varlen_args", "ffpa_check_cu_seqlens",
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
             "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout",
-            "ffpa_kernel_head_dim", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fp8_kernel_head_dim")
+            "ffpa_kernel_head_dim", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fp8_kernel_head_dim",
+            "ffpa_clock_stamps")
 
 
 class MaskDesc(ctypes.Structure):
@@ -89,6 +90,8 @@ def library() -> ctypes.CDLL:
     lib.ffpa_check_fp8_args.restype = i32
     lib.ffpa_fp8_kernel_head_dim.argtypes = [i64]
     lib.ffpa_fp8_kernel_head_dim.restype = i64
+    lib.ffpa_clock_stamps.argtypes = [p]
+    lib.ffpa_clock_stamps.restype = i32
     vargs = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, i64, i64, f32, i32, i32]
     lib.ffpa_fwd_varlen.argtypes = vargs + [p]
     lib.ffpa_fwd_varlen.restype = i32

@@ -19,6 +19,8 @@
 namespace {
 
 thread_local char g_detail[256];
+// measurement aid: clock-stamp buffer of the calling thread's forward launches (null: off)
+thread_local unsigned long long* g_stamps = nullptr;
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -325,6 +327,7 @@ static int launch_dense(const void* q, const void* k, const void* v, const ffpa_
   a.Nkv = (int)Nkv;
   a.group = (int)(Hq / Hkv);
   a.dcols = (int)D;
+  a.stamps = g_stamps;
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
@@ -416,6 +419,7 @@ int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
   a.Nkv = (int)max_seqlen_k;
   a.group = (int)(Hq / Hkv);
   a.dcols = (int)D;
+  a.stamps = g_stamps;
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
@@ -503,6 +507,7 @@ int ffpa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_des
   a.dcols = (int)D;
   a.q_sr = a.kv_sr = (int)D;  // bytes per Q/K/V row
   a.o_sr = (int)D;            // elements per O row
+  a.stamps = g_stamps;
   const double sc = std::isnan(scale) ? 1.0 / std::sqrt((double)D) : (double)scale;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
@@ -522,6 +527,13 @@ int ffpa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_des
 }
 
 int64_t ffpa_fp8_kernel_head_dim(int64_t D) { return fp8_kernel_dim(D); }
+
+int ffpa_clock_stamps(unsigned long long* stamps) {
+  g_detail[0] = '\0';
+  if (stamps != nullptr && ((uintptr_t)stamps & 7)) return fail(FFPA_ERR_VALUE, "stamps must be 8-byte aligned");
+  g_stamps = stamps;
+  return FFPA_OK;
+}
 
 const char* ffpa_status_string(int status) {
   switch (status) {

@@ -79,7 +79,9 @@ struct Fp8Tiling {
   static constexpr int NE = NG / BI;           // epochs held by the ring
   static constexpr int LA = NE - 2;            // epochs of load lookahead
   static constexpr int BR = 128;               // query rows per workgroup
-  static constexpr int LDS_BYTES = NG * 4096;
+  static constexpr int LDS_RING = NG * 4096;
+  // the epilogue stages each wave's O block (32 rows x D 16-bit columns) through LDS
+  static constexpr int LDS_BYTES = LDS_RING > 4 * o_stage_bytes<D>() ? LDS_RING : 4 * o_stage_bytes<D>();
   static constexpr bool OK = D % 128 == 0 && D >= 128 && D <= 512;
 };
 
@@ -132,6 +134,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  clock_stamp(a.stamps, 0);
 
   // ---- work item (b, hq, q tile), XCD-contiguous, heaviest causal tiles first
   const int nqt = (a.Nq + BR - 1) / BR;
@@ -488,32 +491,25 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
     });
   }
   vm_wait<0>();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // the last stage read the next stage's first fragments (never used): their registers stay reserved
+  // until those reads have landed
+  static_assert(NFR == 4, "fragment registers tied below");
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fr[0]), "+v"(fr[1]), "+v"(fr[2]), "+v"(fr[3]) : : "memory");
 
   // ================= epilogue =================
   mma_guard_all<NPV>(o_acc);
   mma_guard_all<NPV>(o_acc);
   const float l = sum_halves(l_lane);
-  if (row < Nq) {
-    const float inv = l > 0.f ? fv / l : 0.f;
-    uint16_t* orow = a.o + (int64_t)(b * a.Hq + hq) * Nq * o_rs + (int64_t)row * o_rs;
-    static_for<NPV>([&](auto c_c) {
-      constexpr int c = decltype(c_c)::value;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& acc = o_acc[c];
-        i32x2 w;
-        w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
-        w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
-        if (c * 32 + q4 * 8 + hi * 4 < a.dcols) *(i32x2*)(orow + c * 32 + q4 * 8 + hi * 4) = w;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if (a.lse != nullptr && hi == 0) {
-      const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
-      a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
-    }
+  const float inv = l > 0.f ? fv / l : 0.f;
+  __builtin_amdgcn_s_barrier();  // every wave is done with the ring before the staged O overwrites it
+  store_o_staged<T, D, NPV>(o_acc, inv, smem + wave * o_stage_bytes<D>(),
+                            a.o + (int64_t)(b * a.Hq + hq) * Nq * o_rs + (int64_t)rw0 * o_rs, o_rs, Nq - rw0, a.dcols,
+                            lane);
+  if (row < Nq && a.lse != nullptr && hi == 0) {
+    const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
+    a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
   }
+  clock_stamp(a.stamps, 1);
 }
 
 // Rows per workgroup of the fp8 forward.

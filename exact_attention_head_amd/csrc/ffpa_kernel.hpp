@@ -1,8 +1,8 @@
 // Exact large-head-dim attention forward for gfx950 (MI355X, CDNA4): shared definitions (argument
-// block, matrix-core wrappers, logit and mask helpers), the launcher, and the shared-staging
-// kernel that serves the head dims the row-owner kernel (ffpa_row_kernel.hpp, every other head
-// dim from 256 to 1024) does not: 64, 128, 192 and the multiples of 64 above 512 whose half is
-// an odd number of 32-column steps (576, 704, 832, 960).
+// block, matrix-core wrappers, logit and mask helpers, the staged O store), the launcher, and the
+// shared-staging kernel that serves the head dims the row-owner kernel (ffpa_row_kernel.hpp: 64,
+// 128, 192, ..., 512, 640, 768, 896, 1024) does not: the multiples of 64 above 512 whose half is an
+// odd number of 32-column steps (576, 704, 832, 960).
 //
 // Shared-staging kernel.  One workgroup = 4 wave64s = one (batch, query head, tile of BR query rows).
 // It loops over the keys in tiles of BC = 64 and keeps an online softmax, as
@@ -109,6 +109,9 @@ struct FwdArgs {
   const float* q_desc;
   const float* k_desc;
   const float* v_desc;
+  // Measurement aid (null: off): the first wave of workgroup 0 records the shader-clock counter and the
+  // 100 MHz real-time counter at its start (stamps[0], stamps[1]) and end (stamps[2], stamps[3]).
+  unsigned long long* stamps;
   // Attention dropout (null keep: none; dense contiguous layout only).  keep is [B, Hq, Nq, keep_w]
   // 32-bit words: bit i of word w set keeps the weight of key 32 w + i for that query row; kept
   // weights are scaled by drop_scale = 1 / (1 - p) (applied to O with the 1/l normalisation).
@@ -277,6 +280,64 @@ __device__ inline void mma_guard_all<16>(f32x16* o) {
 // ---------------------------------------------------------------------------------------------
 // Small device helpers
 // ---------------------------------------------------------------------------------------------
+
+// Clock stamps of the measurement aid (FwdArgs::stamps): first wave of workgroup 0 only.
+__device__ inline void clock_stamp(unsigned long long* stamps, int at) {
+  if (stamps != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    const unsigned long long c = __builtin_amdgcn_s_memtime();
+    const unsigned long long r = __builtin_amdgcn_s_memrealtime();
+    stamps[2 * at] = c;
+    stamps[2 * at + 1] = r;
+  }
+}
+
+// Bytes of one wave's O staging area: 32 rows of DW 16-bit columns, rows padded by 16 bytes.
+template <int DW>
+constexpr int o_stage_bytes() {
+  return 32 * (2 * DW + 16);
+}
+
+// Epilogue store of a wave's O block (the "collective stores" of the sourcepulse page, "How It
+// Works"): the NB accumulators (32 rows x 32 columns each; lane l holds row l % 32, element i column
+// 8 (i / 4) + 4 (l / 32) + i % 4 of its block) are scaled by this lane's inv, rounded, written to the
+// wave's LDS area `stage` and read back so that each store instruction writes whole rows, 16
+// contiguous bytes per lane.  Rows from nrows on and columns from ncols on are not stored.  The caller
+// has made the LDS area free (no wave reads it any more) and waited for the accumulators.
+template <typename T, int DW, int NB, bool OPAQUE_LANE = true>
+__device__ inline void store_o_staged(const f32x16* o_acc, float inv, char* stage, uint16_t* orow0, int64_t o_rs,
+                                      int nrows, int ncols, int lane) {
+  static_assert(NB * 32 == DW, "one accumulator per 32 columns");
+  constexpr int PITCH = 2 * DW + 16;
+  // opaque: keeps the lane's staging addresses from being formed before the key loop (where they
+  // would hold registers throughout); which variants need it is read from the build's register figures
+  if constexpr (OPAQUE_LANE) asm volatile("" : "+v"(lane));
+  const int l32 = lane & 31, hi = lane >> 5;
+  FFPA_LDS char* st = (FFPA_LDS char*)stage;
+#pragma unroll
+  for (int s = 0; s < NB; ++s) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      i32x2 w;
+      w[0] = (int)pack2<T>(o_acc[s][q4 * 4 + 0] * inv, o_acc[s][q4 * 4 + 1] * inv);
+      w[1] = (int)pack2<T>(o_acc[s][q4 * 4 + 2] * inv, o_acc[s][q4 * 4 + 3] * inv);
+      *(FFPA_LDS i32x2*)(st + l32 * PITCH + (s * 32 + q4 * 8 + hi * 4) * 2) = w;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one column block at a time: few registers in flight
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int ROWB = 2 * DW;          // bytes of one row
+  constexpr int NI = 32 * ROWB / 1024;  // store instructions (1 KiB each)
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int off = i * 1024 + 16 * lane;
+    const int r = off / ROWB, cb = off % ROWB;
+    const i32x4 x = *(FFPA_LDS const i32x4*)(st + r * PITCH + cb);
+    if (r < nrows && cb / 2 < ncols) *(i32x4*)(orow0 + (int64_t)r * o_rs + cb / 2) = x;
+    if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // four rows of reads in flight at a time
+  }
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding.  Loads retire in
 // order, so this also completes every load issued before the last N.

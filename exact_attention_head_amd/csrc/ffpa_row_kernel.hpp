@@ -288,7 +288,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   constexpr int MESZ = MASK_U8 ? 1 : 4;  // bytes per staged mask element
   constexpr int MROWB = 32 * MESZ;       // bytes of one row's 32-key block
   static_assert(!DROP || (!VL && !MASK_LDS), "dropout runs on the contiguous dense layout");
-  constexpr int LDS_BYTES = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
+  constexpr int LDS_MAIN = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
+  // the epilogue stages each wave's O block through LDS once the ring is no longer read
+  constexpr int LDS_BYTES = LDS_MAIN > 4 * o_stage_bytes<DW>() ? LDS_MAIN : 4 * o_stage_bytes<DW>();
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   // the partner's partial of block 0 is read (after a barrier, complete PF products later) before
   // block 1's partial overwrites the single exchange buffer: a barrier must separate the two
@@ -309,6 +311,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if constexpr (!VL) clock_stamp(a.stamps, 0);  // (the runtime-layout variants have no register to spare)
   const int dg = DG == 1 ? 0 : (wave & 1);
   const int rg = DG == 1 ? wave : (wave >> 1);
   const int l32 = lane & 31;
@@ -825,14 +828,31 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
     for (int j = nraw; j < ntiles; ++j) tile_body(j, std::false_type{});
   }
   vm_wait<0>();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // the last tile read the next tile's first fragments (never used): their registers stay reserved until
+  // those reads have landed, or the epilogue could reuse one that an in-flight read still writes
+  static_assert(NFR == 4, "fragment registers tied below");
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(kfr[0]), "+v"(kfr[1]), "+v"(kfr[2]), "+v"(kfr[3]), "+v"(vlo[0]), "+v"(vlo[1]), "+v"(vlo[2]),
+                 "+v"(vlo[3]), "+v"(vhi[0]), "+v"(vhi[1]), "+v"(vhi[2]), "+v"(vhi[3])
+               :
+               : "memory");
 
   // ================= epilogue =================
   mma_guard_all<NSUB>(o_acc);
   const float l = sum_halves(l_lane);
-  if (row < Nq) {
-    float inv = l > 0.f ? 1.f / l : 0.f;
-    if constexpr (DROP) inv *= a.drop_scale;
+  float inv = l > 0.f ? 1.f / l : 0.f;
+  if constexpr (DROP) inv *= a.drop_scale;
+  // O leaves through LDS in row-contiguous 16-byte stores; the runtime-layout variants at D = 1024 have
+  // no registers to spare for the staging addresses and store straight from the accumulators
+  constexpr bool STAGED_O = !(VL && D == 1024);
+  if constexpr (STAGED_O) {
+    // every wave is done with the ring before any wave's staged O overwrites it
+    __builtin_amdgcn_s_barrier();
+    // (with a padded head dim, a multiple of 8, the columns from dcols on are not stored)
+    store_o_staged<T, DW, NSUB, !VL>(o_acc, inv, smem + wave * o_stage_bytes<DW>(),
+                                     a.o + o_base + (int64_t)rw0 * o_rs + col0, o_rs, Nq - rw0,
+                                     VL ? a.dcols - col0 : DW, lane);
+  } else if (row < Nq) {
     uint16_t* orow = a.o + o_base + (int64_t)row * o_rs + col0;
     static_for<NSUB>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
@@ -843,15 +863,16 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         w[0] = (int)pack2<T>(acc[q4 * 4 + 0] * inv, acc[q4 * 4 + 1] * inv);
         w[1] = (int)pack2<T>(acc[q4 * 4 + 2] * inv, acc[q4 * 4 + 3] * inv);
         // four columns; with a padded head dim (a multiple of 8) either all or none lie below dcols
-        if (!VL || col0 + s * 32 + q4 * 8 + hi * 4 < a.dcols) *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
+        if (col0 + s * 32 + q4 * 8 + hi * 4 < a.dcols) *(i32x2*)(orow + s * 32 + q4 * 8 + hi * 4) = w;
       }
       __builtin_amdgcn_sched_barrier(0);  // one column block at a time: few registers in flight
     });
-    if (a.lse != nullptr && dg == 0 && hi == 0) {
-      const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
-      a.lse[lse_base + row] = lse;
-    }
   }
+  if (row < Nq && a.lse != nullptr && dg == 0 && hi == 0) {
+    const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
+    a.lse[lse_base + row] = lse;
+  }
+  if constexpr (!VL) clock_stamp(a.stamps, 1);
 }
 
 }  // namespace ffpa

@@ -329,6 +329,20 @@ int ffpa_check_fp8_args(const void* q, const void* k, const void* v, const float
 int64_t ffpa_fp8_kernel_head_dim(int64_t D);
 
 /*
+ * ffpa_clock_stamps -- measurement aid.  While `stamps` is non-NULL, every
+ * forward launch (ffpa_fwd, ffpa_fwd_strided, ffpa_fwd_dropout,
+ * ffpa_fwd_varlen, ffpa_fwd_fp8) enqueued by the calling thread makes the
+ * first wave of its workgroup 0 write the GPU's shader-clock counter and its
+ * 100 MHz real-time counter at that wave's start (stamps[0], stamps[1]) and
+ * end (stamps[2], stamps[3]); the shader clock over that span is
+ * (stamps[2] - stamps[0]) * 100 / (stamps[3] - stamps[1]) MHz.  `stamps` is
+ * a device pointer to 4 uint64 owned by the caller (8-byte aligned, else
+ * FFPA_ERR_VALUE); NULL turns the aid off.  The setting is the calling
+ * thread's own; nothing is allocated.  Host-only.
+ */
+int ffpa_clock_stamps(unsigned long long* stamps);
+
+/*
  * ffpa_fwd_varlen -- enqueue the attention forward over a packed batch of
  * sequences of different lengths (ffpa-attn "API Reference" page,
  * ffpa_attn_varlen_func: packed THD layout, cumulative sequence offsets,
