@@ -409,7 +409,7 @@ def main() -> int:
         names = [f"sweep:{d}" for d in W.SWEEP_D] + [f"sweep:{d}:fp16" for d in W.SWEEP_D]
     else:
         names = ["cross_mask", "sweep:1024", "gqa_causal", "sweep:512", "varlen_causal", "fp8:large_d_self",
-                 "fp8:sweep:512", "drop:large_d_self", "drop:sweep:1024", "bwd:large_d_self", "bwd:sweep:1024"]
+                 "fp8:sweep:512", "fp8:sweep:1024", "drop:large_d_self", "drop:sweep:1024", "bwd:large_d_self", "bwd:sweep:1024"]
     if not args.no_secondary and args.workload == "large_d_self":
         for name in names:
             backward = name.startswith("bwd:")

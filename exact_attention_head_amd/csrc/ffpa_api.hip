@@ -118,10 +118,11 @@ int check_layout(const ffpa_layout_t* lay, int64_t Hq, int64_t Nq, int64_t Nkv, 
   return FFPA_OK;
 }
 
-// Head dim of the fp8 kernel that serves D (the next multiple of 128 from 128 to 512), 0 if none.
+// Head dim of the fp8 kernel that serves D (the next of 128, 256, 384, 512, 768, 1024), 0 if none.
 int64_t fp8_kernel_dim(int64_t D) {
-  if (D < 16 || D > 512 || D % 16 != 0) return 0;
-  return (D + 127) / 128 * 128;
+  if (D < 16 || D > 1024 || D % 16 != 0) return 0;
+  if (D <= 512) return (D + 127) / 128 * 128;
+  return D <= 768 ? 768 : 1024;
 }
 
 // fp8: q, k and v hold e4m3 bytes (one byte per element) and dtype is the output's element type.
@@ -146,12 +147,12 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
     return fail(FFPA_ERR_VALUE, "q, k, v and o must be 16-byte aligned");
   if (lse != nullptr && ((uintptr_t)lse & 3)) return fail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
   if (fp8 && fp8_kernel_dim(D) == 0)
-    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: the fp8 kernels cover 16 <= D <= 512 with D %% 16 == 0",
+    return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: the fp8 kernels cover 16 <= D <= 1024 with D %% 16 == 0",
                 (long long)D);
   if (!fp8 && (D > 1024 || kernel_dim(D) == 0))
     return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
   // grid size and 32-bit in-kernel indexing
-  const int br = fp8 ? 128 : rows_for(kernel_dim(D));
+  const int br = fp8 ? (D <= 512 ? 128 : 64) : rows_for(kernel_dim(D));
   const int64_t nqt = (Nq + br - 1) / br;
   if (B * Hq * nqt > 0x7fffffffLL) return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
   if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B * Hq > (1LL << 30) || B * Hkv > (1LL << 30))

@@ -16,11 +16,13 @@
 // ds_read_b64_tr_b8 in the matching key order, which the sum over keys does not care about (the
 // README's reduction-axis permutation invariance).
 //
-// One workgroup = 4 waves = 128 query rows; each wave owns 32 rows and the whole O row block
-// (32 x D fp32 = D / 2 AGPRs, D <= 512) and keeps its Q rows in VGPRs (D / 8 registers).  K and V
+// One workgroup = 4 waves.  Up to D = 512 each wave owns 32 rows and the whole O row block (32 x D
+// fp32 = D / 2 AGPRs) and keeps its Q rows in VGPRs (D / 8 registers): 128 rows per workgroup.  Above,
+// two waves share 32 rows and split the columns (DW = D / 2 each: the output-D split of the README's
+// "Split-D and TiledMMA"), summing their partial S tiles through LDS: 64 rows per workgroup.  K and V
 // stream through an LDS ring of 4 KiB groups ([32 keys][128 columns], 128-byte rows, 16-byte chunks
-// swizzled as in the 16-bit kernels) filled by direct-to-LDS buffer loads, one barrier per epoch of
-// eight products.
+// swizzled as in the 16-bit kernels; one ring per column group) filled by direct-to-LDS buffer loads,
+// one barrier per epoch of eight products (four with two column groups).
 //
 // Software pipeline.  Stage T issues S(T) (the 2 D / 64 products of tile T) and then P V of tile st - 2
 // (D / 32 products).  Tile T - 1's exponentials run as small pieces between all the products of stage
@@ -65,24 +67,31 @@ __device__ inline int pack_fp8x2(float a, float b, int w) {
 
 template <int D>
 struct Fp8Tiling {
-  static constexpr int NS = D / 64;           // 64-column steps: S products per 32-key block
+  static constexpr int DG = D > 512 ? 2 : 1;   // column groups: waves sharing 32 rows (O is D/2 AGPRs per wave)
+  static constexpr int DW = D / DG;            // output columns per wave
+  static constexpr int NS = DW / 64;           // 64-column steps: S products per 32-key block
   static constexpr int PS = 2 * NS;            // S products per stage
-  static constexpr int NPV = D / 32;           // P V products per stage (one per 32 output columns)
+  static constexpr int NPV = DW / 32;          // P V products per stage (one per 32 output columns)
   static constexpr int MPT = PS + NPV;         // products per stage
-  static constexpr int NCG = D / 128;          // 128-column groups
-  static constexpr int GT = 4 * NCG;           // 4 KiB groups per stage: K (2 key blocks x NCG), V (same)
-  static constexpr int EM = 8;                 // products per epoch
-  static constexpr int BI = 4;                 // groups per epoch
+  static constexpr int NCGW = DW / 128;        // 128-column groups of one column group
+  static constexpr int GTW = 4 * NCGW;         // 4 KiB groups per stage of one column group: K, then V
+  static constexpr int GT = DG * GTW;          // groups per stage
+  static constexpr int EM = DG == 1 ? 8 : 4;   // products per epoch
+  static constexpr int BIW = EM / 2;           // groups per epoch of one column group
+  static constexpr int BI = DG * BIW;          // groups per epoch
   static constexpr int EPT = MPT / EM;         // epochs per stage
-  static constexpr int RS = GT <= 4 ? 8 : (GT <= 8 ? 4 : 2);  // stages per turn of the ring (even)
+  static constexpr int RS = DG == 2 ? 1 : (GT <= 4 ? 8 : (GT <= 8 ? 4 : 2));  // stages per turn of the ring
+  static constexpr int UNR = RS % 2 ? 2 * RS : RS;  // stages per loop iteration (even: the stage parity)
+  static constexpr int CGB = RS * GTW * 4096;  // ring bytes of one column group ([column group][slot][4 KiB])
   static constexpr int NG = RS * GT;           // ring groups
   static constexpr int NE = NG / BI;           // epochs held by the ring
   static constexpr int LA = NE - 2;            // epochs of load lookahead
-  static constexpr int BR = 128;               // query rows per workgroup
-  static constexpr int LDS_RING = NG * 4096;
-  // the epilogue stages each wave's O block (32 rows x D 16-bit columns) through LDS
-  static constexpr int LDS_BYTES = LDS_RING > 4 * o_stage_bytes<D>() ? LDS_RING : 4 * o_stage_bytes<D>();
-  static constexpr bool OK = D % 128 == 0 && D >= 128 && D <= 512;
+  static constexpr int BR = 128 / DG;          // query rows per workgroup
+  static constexpr int EXCH = DG == 2 ? 4 * 8192 : 0;  // partial S exchange: [wave][32-key block][4 KiB]
+  static constexpr int LDS_RING = NG * 4096 + EXCH;
+  // the epilogue stages each wave's O block (32 rows x DW 16-bit columns) through LDS
+  static constexpr int LDS_BYTES = LDS_RING > 4 * o_stage_bytes<DW>() ? LDS_RING : 4 * o_stage_bytes<DW>();
+  static constexpr bool OK = D % 128 == 0 && D >= 128 && D <= 1024 && DW % 128 == 0;
 };
 
 // Operand fragments are read this many products ahead of their use.
@@ -99,33 +108,51 @@ enum Fp8Mode { kFp8Mask = 0, kFp8Raw = 1, kFp8Edge = 2 };
 
 // Slot of exponential piece k (0..31) of the previous tile within a stage.
 constexpr int fp8_exp_slot(int k, int MPT) { return 1 + (k * (MPT - 3)) / 32; }
+// First slot at which block kb's logits can be formed.  One column group: the slot after its last S
+// product.  Two: the partial S is published in that slot, becomes visible at the next epoch barrier,
+// and the partner's partial read right after it is complete PF products later.
+constexpr int fp8_block_first(int kb, int DG, int NS, int EM, int PF) {
+  const int w = (kb + 1) * NS;
+  if (DG == 1) return w + 1;
+  int bs = w;
+  while ((bs + PF) % EM != 0) ++bs;
+  return bs + PF;
+}
+constexpr int fp8_block_barrier(int kb, int NS, int EM, int PF) {
+  int bs = (kb + 1) * NS;
+  while ((bs + PF) % EM != 0) ++bs;
+  return bs;
+}
 // Logit pieces of one 32-key block of the current tile (4 raw maxima of 4 products, or 8 explicit
-// pieces of 2 logits).  Block 0's run once its S products are complete (slots NS+1 .. PS-1), block 1's
-// and then the cross-half maximum and the decision after S (slots PS+1 .. MPT-2).
+// pieces of 2 logits).  Block 0's run from its first slot up to block 1's; block 1's, then the
+// cross-half maximum and the decision, from its first slot to MPT - 2.
 constexpr int fp8_block_pieces(bool raw) { return raw ? 4 : 8; }
-constexpr int fp8_logit_slot(int kb, int k, int NS, int PS, int MPT, bool raw) {
-  return kb == 0 ? NS + 1 + (k * (PS - 1 - NS)) / fp8_block_pieces(raw)
-                 : PS + 1 + (k * (MPT - 2 - PS)) / (fp8_block_pieces(raw) + 2);
+constexpr int fp8_logit_slot(int kb, int k, int DG, int NS, int MPT, int EM, int PF, bool raw) {
+  const int f0 = fp8_block_first(0, DG, NS, EM, PF), f1 = fp8_block_first(1, DG, NS, EM, PF);
+  return kb == 0 ? f0 + (k * (f1 - f0)) / fp8_block_pieces(raw)
+                 : f1 + (k * (MPT - 1 - f1)) / (fp8_block_pieces(raw) + 2);
 }
 
 template <typename T, int D, int MODE, int MK = kMaskNone>
 __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   using FT = Fp8Tiling<D>;
-  static_assert(FT::OK, "fp8 head dims: 128, 256, 384, 512");
-  constexpr int NS = FT::NS, PS = FT::PS, NPV = FT::NPV, MPT = FT::MPT, NCG = FT::NCG, GT = FT::GT;
-  constexpr int EM = FT::EM, BI = FT::BI, EPT = FT::EPT, RS = FT::RS, NG = FT::NG, LA = FT::LA, BR = FT::BR;
+  static_assert(FT::OK, "fp8 head dims: 128, 256, 384, 512, 768, 1024");
+  constexpr int DG = FT::DG, DW = FT::DW, NS = FT::NS, PS = FT::PS, NPV = FT::NPV, MPT = FT::MPT;
+  constexpr int NCGW = FT::NCGW, GTW = FT::GTW, CGB = FT::CGB, UNR = FT::UNR;
+  constexpr int EM = FT::EM, BIW = FT::BIW, BI = FT::BI, EPT = FT::EPT, RS = FT::RS, LA = FT::LA, BR = FT::BR;
   constexpr int PF = kFp8PF, NFR = 4, BC = 64;
   constexpr bool RAW = MODE == kFp8Raw;
   constexpr bool MASK = MODE == kFp8Mask;  // mask kind MK (a template parameter: one load path per kernel)
   static_assert(!MASK || MK != kMaskNone, "masked variant needs a mask kind");
   static_assert(MPT % EM == 0 && MPT % NFR == 0 && PF < EM && LA >= 2, "stage plan");
   constexpr int NLB = fp8_block_pieces(RAW);
-  static_assert(NS >= 2 && fp8_logit_slot(0, NLB - 1, NS, PS, MPT, RAW) <= PS - 1 &&
-                    fp8_logit_slot(1, NLB + 1, NS, PS, MPT, RAW) <= MPT - 2,
+  constexpr int F0 = fp8_block_first(0, DG, NS, EM, PF), F1 = fp8_block_first(1, DG, NS, EM, PF);
+  static_assert(NS >= 2 && F0 < F1 && fp8_logit_slot(1, NLB + 1, DG, NS, MPT, EM, PF, RAW) <= MPT - 2,
                 "logit pieces fit their windows");
-  constexpr int NL = BI;                                  // loads per wave per epoch (one per group)
-  constexpr int LSTEP = EM / NL;
-  static_assert(1 + (NL - 1) * LSTEP < EM, "the loads after a barrier end before the next one");
+  static_assert(DG == 1 || (CGB <= 65536 && FT::NG * 4096 + FT::EXCH <= 160 * 1024), "LDS windows");
+  static_assert(DG == 1 || fp8_block_barrier(1, NS, EM, PF) + PF < MPT, "publishing barriers inside the stage");
+  constexpr int NL = BI;  // loads per wave per epoch (one per group): slot bs + 1 + (q (EM - 1)) / NL
+  static_assert(1 + ((NL - 1) * (EM - 1)) / NL < EM, "the loads after a barrier end before the next one");
 
   __shared__ __attribute__((aligned(1024))) char smem[FT::LDS_BYTES];
 
@@ -134,6 +161,9 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int hi = lane >> 5;
+  const int dg = DG == 1 ? 0 : (wave & 1);  // column group
+  const int rg = DG == 1 ? wave : (wave >> 1);  // row group
+  const int col0 = dg * DW;
   clock_stamp(a.stamps, 0);
 
   // ---- work item (b, hq, q tile), XCD-contiguous, heaviest causal tiles first
@@ -150,7 +180,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const int r0 = qt * BR;
   const int Nq = a.Nq, Nkv = a.Nkv;
   const int q_rs = a.q_sr, kv_rs = a.kv_sr, o_rs = a.o_sr;  // row strides: bytes of Q/K/V rows, O elements
-  const int rw0 = r0 + wave * 32;
+  const int rw0 = r0 + rg * 32;
   const int row = rw0 + l32;
   const int off = Nkv - Nq;
   int kv_end = Nkv;
@@ -172,14 +202,14 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const uint8_t* kg = (const uint8_t*)a.k + (int64_t)(b * a.Hkv + hk) * Nkv * kv_rs;
   const uint8_t* vg = (const uint8_t*)a.v + (int64_t)(b * a.Hkv + hk) * Nkv * kv_rs;
 
-  // ---- Q rows in VGPRs: step s holds bytes 64 s + 32 hi .. +31 of row l32 (zero past dcols)
+  // ---- Q rows in VGPRs: step s holds bytes col0 + 64 s + 32 hi .. +31 of row l32 (zero past dcols)
   i32x8 qf[NS];
   {
     const int qrow = row < Nq ? row : Nq - 1;
-    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + hi * 32);
+    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 32);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int c = 64 * s + 32 * hi;
+      const int c = col0 + 64 * s + 32 * hi;
       const i32x4 lo = c < a.dcols ? src[4 * s] : i32x4{0, 0, 0, 0};
       const i32x4 up = c + 16 < a.dcols ? src[4 * s + 1] : i32x4{0, 0, 0, 0};
       qf[s] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
@@ -198,28 +228,30 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc((void*)kg, (short)0, head_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc((void*)vg, (short)0, head_bytes, 0x00020000);
   char* const ring_w = smem + wave * 1024;
-  // group gi of stage st into ring slot (u * GT + gi): K groups (gi < 2 NCG) hold key block gi / NCG of
-  // tile min(st, n - 1), columns 128 (gi % NCG); V groups hold key block gi % 2 of tile
-  // clamp(st - 2, 0, n - 1), columns 128 ((gi - 2 NCG) / 2)
-  auto issue_group = [&](int st, auto u_c, auto gi_c) {
-    constexpr int U = decltype(u_c)::value, GI = decltype(gi_c)::value;
-    constexpr bool ISK = GI < 2 * NCG;
-    constexpr int KB = ISK ? GI / NCG : (GI - 2 * NCG) % 2;
-    constexpr int CG = ISK ? GI % NCG : (GI - 2 * NCG) / 2;
+  // group gi of column group cg of stage st into that column group's ring slot (u * GTW + gi): K groups
+  // (gi < 2 NCGW) hold key block gi / NCGW of tile min(st, n - 1), columns 128 (cg NCGW + gi % NCGW);
+  // V groups hold key block gi % 2 of tile clamp(st - 2, 0, n - 1), columns 128 (cg NCGW + (gi - 2 NCGW) / 2)
+  auto issue_group = [&](int st, auto u_c, auto cg_c, auto gi_c) {
+    constexpr int U = decltype(u_c)::value, CGR = decltype(cg_c)::value, GI = decltype(gi_c)::value;
+    constexpr bool ISK = GI < 2 * NCGW;
+    constexpr int KB = ISK ? GI / NCGW : (GI - 2 * NCGW) % 2;
+    constexpr int CG = CGR * NCGW + (ISK ? GI % NCGW : (GI - 2 * NCGW) / 2);
     int tile = ISK ? st : st - 2;
     tile = tile < ntiles - 1 ? tile : ntiles - 1;
     tile = tile > 0 ? tile : 0;
     const uint32_t so = (uint32_t)(tile * BC + KB * 32) * (uint32_t)kv_rs + (uint32_t)(CG * 128);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ISK ? rsrc_k : rsrc_v,
-                                             (FFPA_LDS void*)(ring_w + ((U * GT + GI) % NG) * 4096), 16, voff_lane,
-                                             so, 0, 0);
+                                             (FFPA_LDS void*)(ring_w + CGR * CGB + ((U * GTW + GI) % (RS * GTW)) * 4096),
+                                             16, voff_lane, so, 0, 0);
   };
-  // load q of local epoch E (E >= EPT: of a later stage) of stage T, whose ring position is U
+  // load q of local epoch E (E >= EPT: of a later stage) of stage st, whose ring position is U: group
+  // E * BIW + q % BIW of column group q / BIW
   auto issue_epoch_load = [&](int st, auto u_c, auto e_c, auto q_c) {
     constexpr int U = decltype(u_c)::value, E = decltype(e_c)::value, Q = decltype(q_c)::value;
     constexpr int SD = E / EPT, EL = E % EPT;
     if (st + SD >= nstages) return;
-    issue_group(st + SD, std::integral_constant<int, (U + SD) % RS>{}, std::integral_constant<int, EL * BI + Q>{});
+    issue_group(st + SD, std::integral_constant<int, (U + SD) % RS>{}, std::integral_constant<int, Q / BIW>{},
+                std::integral_constant<int, EL * BIW + Q % BIW>{});
   };
   auto wait_epoch = [&](int eg) {
     if (eg + LA - 1 < total_epochs) vm_wait<(LA - 1) * NL>();
@@ -231,11 +263,12 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   // 2 NCG + 2 (c / 4) + r / 2, with m' = m (m < 4) or m + 4 for m = (lane % 16) / 2, logical chunk
   // 2 (c % 4) + (lane / 16) % 2, half (lane % 2).
   const uint32_t ring_addr = lds_addr(smem);
+  const uint32_t cgb = ring_addr + dg * CGB;  // this wave's column group's ring
   uint32_t ka[2][2];
 #pragma unroll
   for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) ka[s2][j] = ring_addr + l32 * 128 + ((4 * s2 + 2 * hi + j) ^ pi7((l32 >> 1) & 7)) * 16;
+    for (int j = 0; j < 2; ++j) ka[s2][j] = cgb + l32 * 128 + ((4 * s2 + 2 * hi + j) ^ pi7((l32 >> 1) & 7)) * 16;
   uint32_t vaddr[2][4];
   {
     const int g16 = lane >> 4, i16 = lane & 15, m = i16 >> 1;
@@ -244,7 +277,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
       const int vrow = 16 * r2 + 4 * (g16 >> 1) + (m < 4 ? m : m + 4);
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
-        vaddr[r2][c4] = ring_addr + vrow * 128 + ((2 * c4 + (g16 & 1)) ^ pi7((vrow >> 1) & 7)) * 16 + 8 * (i16 & 1);
+        vaddr[r2][c4] = cgb + vrow * 128 + ((2 * c4 + (g16 & 1)) ^ pi7((vrow >> 1) & 7)) * 16 + 8 * (i16 & 1);
     }
   }
   i32x8 fr[NFR];
@@ -256,7 +289,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
     constexpr int r = M % NFR;
     if constexpr (mm < PS) {
       constexpr int kb = mm / NS, s = mm % NS;
-      constexpr int ofs = ((U * GT + kb * NCG + s / 2) % NG) * 4096;
+      constexpr int ofs = ((U * GTW + kb * NCGW + s / 2) % (RS * GTW)) * 4096;
       constexpr uint32_t win = ofs >= 65536 ? 65536u : 0u;
       const i32x4 x0 = lds_read_b128_async<(ofs & 65535)>(ka[s % 2][0] + win);
       const i32x4 x1 = lds_read_b128_async<(ofs & 65535)>(ka[s % 2][1] + win);
@@ -266,7 +299,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
       i32x2 y[4];
       static_for<4>([&](auto rr_c) {
         constexpr int rr = decltype(rr_c)::value;
-        constexpr int ofs = ((U * GT + 2 * NCG + 2 * (c / 4) + rr / 2) % NG) * 4096;
+        constexpr int ofs = ((U * GTW + 2 * NCGW + 2 * (c / 4) + rr / 2) % (RS * GTW)) * 4096;
         constexpr uint32_t win = ofs >= 65536 ? 65536u : 0u;
         y[rr] = lds_read_tr8_async<(ofs & 65535)>(vaddr[rr % 2][c % 4] + win);
       });
@@ -275,6 +308,11 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   };
 
   const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
+
+  // partial S exchange (two column groups): [wave][block][4 x 1 KiB], 16 bytes per lane
+  const uint32_t ex_mine = ring_addr + FT::NG * 4096 + wave * 8192 + lane * 16;
+  const uint32_t ex_partner = ring_addr + FT::NG * 4096 + (wave ^ 1) * 8192 + lane * 16;
+  f32x4 part[4];  // the partner's partial of the block being published
 
   // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
   static_for<LA>([&](auto e_c) {
@@ -313,12 +351,13 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   float alpha[2] = {1.f, 1.f};      // rescale of O and l that tile brings
   bool need[2] = {false, false};
   float lmax = kNegInf, mt = kNegInf, m_old = kNegInf, psum = 0.f, pv3[3] = {0.f, 0.f, 0.f};
+  (void)part;
   int pw = 0;
   f32x4 bias[4];  // mask biases of one 32-key block (keys 8 g + 4 hi + e)
 
   auto stage = [&](const int st, auto u_c) {
-    constexpr int U = decltype(u_c)::value;
-    constexpr int PAR = U & 1;      // parity of st (RS is even)
+    constexpr int U = decltype(u_c)::value % RS;  // ring position
+    constexpr int PAR = decltype(u_c)::value & 1;  // parity of st (UNR is even)
     // this stage's tile for S and logits (tiles past the last are masked out), the tile of the P V phase
     const bool live = st < ntiles;
     const int key0 = st * BC;
@@ -423,9 +462,18 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // a block of S(st) finished one product ago: 20 wait states before its logits are formed
+      // a block of S(st) finished one product ago: 20 wait states before its logits are formed (two
+      // column groups: before its partial is published to the partner)
       if constexpr (m == NS) mma8_guard1(sacc[PAR][0]);
       if constexpr (m == PS) mma8_guard1(sacc[PAR][1]);
+      if constexpr (DG == 2 && (m == NS || m == PS)) {
+        constexpr int kb = m / NS - 1;
+        const f32x16& x = sacc[PAR][kb];
+        lds_write_b128_async<kb * 4096 + 0>(ex_mine, f32x4{x[0], x[1], x[2], x[3]});
+        lds_write_b128_async<kb * 4096 + 1024>(ex_mine, f32x4{x[4], x[5], x[6], x[7]});
+        lds_write_b128_async<kb * 4096 + 2048>(ex_mine, f32x4{x[8], x[9], x[10], x[11]});
+        lds_write_b128_async<kb * 4096 + 3072>(ex_mine, f32x4{x[12], x[13], x[14], x[15]});
+      }
       // mask biases of tile st's block 0, requested at the start of the stage
       if constexpr (MASK && m == 0) load_block_bias(key0);
 
@@ -433,9 +481,21 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
       // last are refilled LA epochs ahead
       if constexpr ((m + PF) % EM == 0) {
         const int eg = st * EPT + (m + PF) / EM;
+        // the barrier that publishes a partial: the partial's writes have landed before it
+        constexpr int pub = DG == 2 ? (m == fp8_block_barrier(0, NS, EM, PF) ? 0
+                                       : (m == fp8_block_barrier(1, NS, EM, PF) ? 1 : -1))
+                                    : -1;
+        if constexpr (pub >= 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (eg < total_epochs) {
           wait_epoch(eg);
           __builtin_amdgcn_s_barrier();
+        }
+        // the partner's partial of that block (complete once a fragment read issued after it is)
+        if constexpr (pub >= 0) {
+          part[0] = lds_read_f4_async<pub * 4096 + 0>(ex_partner);
+          part[1] = lds_read_f4_async<pub * 4096 + 1024>(ex_partner);
+          part[2] = lds_read_f4_async<pub * 4096 + 2048>(ex_partner);
+          part[3] = lds_read_f4_async<pub * 4096 + 3072>(ex_partner);
         }
       }
       static_for<EPT + 1>([&](auto eb_c) {
@@ -444,7 +504,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
         if constexpr (bs >= 0 && bs < MPT) {
           static_for<NL>([&](auto q_c) {
             constexpr int Q = decltype(q_c)::value;
-            constexpr int slot = bs + 1 + Q * LSTEP < MPT ? bs + 1 + Q * LSTEP : MPT - 1;
+            constexpr int ls = bs + 1 + (Q * (EM - 1)) / NL;
+            constexpr int slot = ls < MPT ? ls : MPT - 1;
             if constexpr (slot == m)
               issue_epoch_load(st, std::integral_constant<int, U>{}, std::integral_constant<int, eb + LA>{}, q_c);
           });
@@ -458,14 +519,24 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
       for (int k = 0; k < 32; ++k)
         if (fp8_exp_slot(k, MPT) == m) exp_piece(k);
+      // (two column groups) the partner's partial joins this wave's before the block's logits
+      if constexpr (DG == 2 && (m == F0 || m == F1)) {
+        constexpr int kb = m == F0 ? 0 : 1;
+        asm volatile("" : "+v"(part[0]), "+v"(part[1]), "+v"(part[2]), "+v"(part[3]));
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[PAR][kb][4 * g + e] += part[g][e];
+        asm volatile("" : "+v"(sacc[PAR][kb]));
+      }
 #pragma unroll
       for (int k = 0; k < NLB; ++k)
-        if (fp8_logit_slot(0, k, NS, PS, MPT, RAW) == m) logit_piece(0, k);
+        if (fp8_logit_slot(0, k, DG, NS, MPT, EM, PF, RAW) == m) logit_piece(0, k);
       // block 1's biases replace block 0's once its last logit piece has read them
-      if constexpr (MASK && m == fp8_logit_slot(0, NLB - 1, NS, PS, MPT, false)) load_block_bias(key0 + 32);
+      if constexpr (MASK && m == fp8_logit_slot(0, NLB - 1, DG, NS, MPT, EM, PF, false)) load_block_bias(key0 + 32);
 #pragma unroll
       for (int k = 0; k < NLB + 2; ++k)
-        if (fp8_logit_slot(1, k, NS, PS, MPT, RAW) == m) logit_piece(1, k);
+        if (fp8_logit_slot(1, k, DG, NS, MPT, EM, PF, RAW) == m) logit_piece(1, k);
 
       // ---- close the stage: l and O take tile st - 1's rescale (O holds exactly the tiles before it)
       if constexpr (m == MPT - 1) {
@@ -484,8 +555,8 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
     });
   };
 
-  for (int T0 = 0; T0 < nstages; T0 += RS) {
-    static_for<RS>([&](auto u_c) {
+  for (int T0 = 0; T0 < nstages; T0 += UNR) {
+    static_for<UNR>([&](auto u_c) {
       constexpr int U = decltype(u_c)::value;
       if (T0 + U < nstages) stage(T0 + U, u_c);
     });
@@ -502,25 +573,23 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const float l = sum_halves(l_lane);
   const float inv = l > 0.f ? fv / l : 0.f;
   __builtin_amdgcn_s_barrier();  // every wave is done with the ring before the staged O overwrites it
-  store_o_staged<T, D, NPV>(o_acc, inv, smem + wave * o_stage_bytes<D>(),
-                            a.o + (int64_t)(b * a.Hq + hq) * Nq * o_rs + (int64_t)rw0 * o_rs, o_rs, Nq - rw0, a.dcols,
-                            lane);
-  if (row < Nq && a.lse != nullptr && hi == 0) {
+  store_o_staged<T, DW, NPV>(o_acc, inv, smem + wave * o_stage_bytes<DW>(),
+                             a.o + (int64_t)(b * a.Hq + hq) * Nq * o_rs + (int64_t)rw0 * o_rs + col0, o_rs, Nq - rw0,
+                             a.dcols - col0, lane);
+  if (row < Nq && a.lse != nullptr && dg == 0 && hi == 0) {
     const float lse = l > 0.f ? (m_run + __builtin_log2f(l)) * kLn2 : kNegInf;
     a.lse[(int64_t)(b * a.Hq + hq) * Nq + row] = lse;
   }
   clock_stamp(a.stamps, 1);
 }
 
-// Rows per workgroup of the fp8 forward.
-constexpr int fp8_rows_per_block() { return 128; }
-
 template <typename T, int D>
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
   if (a.group < 1 || a.Hkv < 1 || a.Hq != a.group * a.Hkv || a.B < 1 || a.Nq < 1 || a.Nkv < 1 || a.dcols > D ||
       a.dcols < 16 || a.dcols % 16 != 0)
     return hipErrorInvalidValue;
-  const int nqt = (a.Nq + 127) / 128;
+  constexpr int BR = Fp8Tiling<D>::BR;
+  const int nqt = (a.Nq + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.Hq * nqt;
   const bool masked = a.mask_kind != kMaskNone;
   const bool raw = !masked && !a.causal && a.Nkv % 64 == 0 && a.scale_log2 > 0.f;

@@ -21,11 +21,11 @@ hipError_t launch_fwd_staged(const FwdArgs& a, hipStream_t stream, long long blo
 #define FFPA_FOR_EACH_D(X) \
   X(64) X(128) X(192) X(256) X(320) X(384) X(448) X(512) X(576) X(640) X(704) X(768) X(832) X(896) X(960) X(1024)
 
-// fp8 forward: launchers per output element type and head dim (128, 256, 384, 512; smaller multiples
-// of 16 run the next one up with padding columns).
+// fp8 forward: launchers per output element type and head dim (128, 256, 384, 512, 768, 1024; other
+// multiples of 16 run the next one up with padding columns).
 template <typename T, int D>
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
-#define FFPA_FP8_FOR_EACH_D(X) X(128) X(256) X(384) X(512)
+#define FFPA_FP8_FOR_EACH_D(X) X(128) X(256) X(384) X(512) X(768) X(1024)
 #define FFPA_FP8_DECLARE(Dv)                                                          \
   extern template hipError_t launch_fwd_fp8<Bf16, Dv>(const FwdArgs&, hipStream_t); \
   extern template hipError_t launch_fwd_fp8<Fp16, Dv>(const FwdArgs&, hipStream_t);

@@ -279,8 +279,7 @@ const char* ffpa_kernel_name(int64_t D);
 /*
  * ffpa_fwd_fp8 -- enqueue the FP8 attention forward (the ffpa-attn README,
  * "Latest News": FP8 attention for head dims 64..1024, and "End-to-End
- * Inference": masks, causal, GQA/MQA) on the gfx950 fp8 matrix core, for
- * head dims up to 512 (larger ones return FFPA_ERR_UNSUPPORTED).  q, k and v hold OCP e4m3 ("e4m3fn") codes, one byte per
+ * Inference": masks, causal, GQA/MQA) on the gfx950 fp8 matrix core.  q, k and v hold OCP e4m3 ("e4m3fn") codes, one byte per
  * element, laid out as the 16-bit tensors of ffpa_fwd; the per-head
  * dequantisation factors make the tensors that take part
  *
@@ -298,10 +297,10 @@ const char* ffpa_kernel_name(int64_t D);
  *                NULL = all 1 (other values give unspecified results: the
  *                kernels cannot check device memory)
  *   mask, o, lse, B, Hq, Hkv, Nq, Nkv, scale, is_causal, stream: as for ffpa_fwd
- *   D            16 <= D <= 512, D % 16 == 0 (FFPA_ERR_UNSUPPORTED otherwise);
- *                D not a multiple of 128 runs the next one up with padding
- *                columns (zeros in Q, never stored in O; K and V must then
- *                hold finite codes)
+ *   D            16 <= D <= 1024, D % 16 == 0 (FFPA_ERR_UNSUPPORTED otherwise);
+ *                a D other than 128, 256, 384, 512, 768 or 1024 runs the next
+ *                of those up with padding columns (zeros in Q, never stored
+ *                in O; K and V must then hold finite codes)
  *   out_dtype    ffpa_dtype of o (FFPA_ERR_TYPE otherwise)
  *
  * Both products run on e4m3 operands with fp32 accumulation: the
@@ -324,8 +323,8 @@ int ffpa_check_fp8_args(const void* q, const void* k, const void* v, const float
                         int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal,
                         int out_dtype);
 
-/* Head dim of the fp8 kernel serving D (128, 256, 384 or 512: the next
- * multiple of 128), 0 for an unsupported D.  Host-only. */
+/* Head dim of the fp8 kernel serving D (the next of 128, 256, 384, 512, 768
+ * and 1024), 0 for an unsupported D.  Host-only. */
 int64_t ffpa_fp8_kernel_head_dim(int64_t D);
 
 /*

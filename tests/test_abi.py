@@ -342,7 +342,7 @@ def fcheck(B=1, Hq=2, Hkv=1, Nq=100, Nkv=130, D=512, scale=math.nan, causal=Fals
 
 def test_fp8_valid_arguments_pass():
     assert fcheck() == ffpa.OK and detail() == ""
-    for D in range(16, 513, 16):
+    for D in range(16, 1025, 16):
         assert fcheck(D=D) == ffpa.OK, D
     assert fcheck(dq=None, dk=None, dv=None) == ffpa.OK
     assert fcheck(out=ffpa.FFPA_FP16, causal=True, Nq=100, Nkv=130) == ffpa.OK
@@ -351,7 +351,7 @@ def test_fp8_valid_arguments_pass():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(out=2), ffpa.ERR_TYPE), (dict(D=8), ffpa.ERR_UNSUPPORTED), (dict(D=520), ffpa.ERR_UNSUPPORTED),
-    (dict(D=100), ffpa.ERR_UNSUPPORTED), (dict(D=1024), ffpa.ERR_UNSUPPORTED), (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE),
+    (dict(D=100), ffpa.ERR_UNSUPPORTED), (dict(D=1040), ffpa.ERR_UNSUPPORTED), (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE),
     (dict(causal=True, Nq=131, Nkv=130), ffpa.ERR_VALUE), (dict(dq=DQ + 2), ffpa.ERR_VALUE),
     (dict(dv=O), ffpa.ERR_VALUE), (dict(q=Q + 8), ffpa.ERR_VALUE), (dict(o=Q), ffpa.ERR_VALUE),
 ])
@@ -362,7 +362,8 @@ def test_fp8_argument_errors(kw, status):
 
 def test_fp8_kernel_head_dim():
     lib = ffpa.library()
-    for D in range(16, 513, 16):
-        assert lib.ffpa_fp8_kernel_head_dim(D) == (D + 127) // 128 * 128, D
-    for bad in (0, 8, 100, 528, 1024):
+    for D in range(16, 1025, 16):
+        want = (D + 127) // 128 * 128 if D <= 512 else (768 if D <= 768 else 1024)
+        assert lib.ffpa_fp8_kernel_head_dim(D) == want, D
+    for bad in (0, 8, 100, 520, 1040, 2048):
         assert lib.ffpa_fp8_kernel_head_dim(bad) == 0

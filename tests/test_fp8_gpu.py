@@ -83,14 +83,14 @@ def run_fp8(q8, k8, v8, dq, dk, dv, mask=None, is_causal=False, scale=None, out_
 
 
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16], ids=["bf16", "fp16"])
-@pytest.mark.parametrize("D", [128, 256, 384, 512])
+@pytest.mark.parametrize("D", [128, 256, 384, 512, 768, 1024])
 def test_fp8_every_head_dim(D, out_dtype):
     q8, k8, v8, dq, dk, dv = fp8_inputs(1, 2, 2, 133, 197, D, seed=D)
     o, l = run_fp8(q8, k8, v8, dq, dk, dv, out_dtype=out_dtype)
     _log(f"D={D} {out_dtype}", compare_fp8(o, l, q8, k8, v8, dq, dk, dv))
 
 
-@pytest.mark.parametrize("D", [16, 64, 80, 112, 208, 320, 448, 496])
+@pytest.mark.parametrize("D", [16, 64, 80, 112, 208, 320, 448, 496, 528, 640, 784, 1008])
 def test_fp8_padded_head_dims(D):
     q8, k8, v8, dq, dk, dv = fp8_inputs(1, 2, 1, 150, 170, D, seed=D + 1)
     o, l = run_fp8(q8, k8, v8, dq, dk, dv)
@@ -98,7 +98,7 @@ def test_fp8_padded_head_dims(D):
 
 
 @pytest.mark.parametrize("Nq,Nkv", [(1, 1), (7, 7), (64, 64), (65, 63), (128, 256), (129, 333), (333, 1), (1, 333)])
-@pytest.mark.parametrize("D", [128, 512])
+@pytest.mark.parametrize("D", [128, 512, 1024])
 def test_fp8_sequence_shapes(Nq, Nkv, D):
     q8, k8, v8, dq, dk, dv = fp8_inputs(1, 2, 1, Nq, Nkv, D, seed=Nq * 7 + Nkv)
     o, l = run_fp8(q8, k8, v8, dq, dk, dv)
@@ -106,7 +106,7 @@ def test_fp8_sequence_shapes(Nq, Nkv, D):
 
 
 @pytest.mark.parametrize("Nq,Nkv", [(1, 1), (64, 64), (200, 200), (100, 333), (257, 260)])
-@pytest.mark.parametrize("D", [128, 384, 512])
+@pytest.mark.parametrize("D", [128, 384, 512, 768, 1024])
 def test_fp8_causal_gqa(Nq, Nkv, D):
     q8, k8, v8, dq, dk, dv = fp8_inputs(2, 4, 2, Nq, Nkv, D, seed=Nq + Nkv + D)
     o, l = run_fp8(q8, k8, v8, dq, dk, dv, is_causal=True)
@@ -114,7 +114,7 @@ def test_fp8_causal_gqa(Nq, Nkv, D):
 
 
 @pytest.mark.parametrize("kind", ["bool", "f32", "bf16", "fp16"])
-@pytest.mark.parametrize("D", [128, 512])
+@pytest.mark.parametrize("D", [128, 512, 1024])
 @pytest.mark.parametrize("Nkv", [256, 333])
 def test_fp8_masks(kind, D, Nkv):
     B, H, Nq = 2, 3, 130
@@ -151,17 +151,19 @@ def test_fp8_codes_without_factors_and_explicit_scales():
         _log(f"no factors scale={scale}", compare_fp8(o, l, q8, k8, v8, None, None, None, scale=scale))
 
 
-def test_fp8_full_size_sampled():
-    """The fp8 benchmark workload (B1 H8 N4096 D512, per-head factors) on sampled rows of every head."""
-    q8, k8, v8, dq, dk, dv = fp8_inputs(1, 8, 8, 4096, 4096, 512, seed=2)
+@pytest.mark.parametrize("H,N,D", [(8, 4096, 512), (16, 4096, 1024)])
+def test_fp8_full_size_sampled(H, N, D):
+    """The fp8 benchmark shapes (per-head factors) on sampled rows of every head."""
+    q8, k8, v8, dq, dk, dv = fp8_inputs(1, H, H, N, N, D, seed=2)
     o, l = run_fp8(q8, k8, v8, dq, dk, dv)
-    rows = W.sample_rows(1, 8, 4096, seed=2)
-    _log("B1 H8 N4096 D512 sampled", compare_fp8(o, l, q8, k8, v8, dq, dk, dv, rows=rows))
+    rows = W.sample_rows(1, H, N, seed=2)
+    _log(f"B1 H{H} N{N} D{D} sampled", compare_fp8(o, l, q8, k8, v8, dq, dk, dv, rows=rows))
 
 
-def test_fp8_in_bounds_and_deterministic():
+@pytest.mark.parametrize("D", [208, 784])
+def test_fp8_in_bounds_and_deterministic(D):
     dev = torch.device("cuda:0")
-    q8, k8, v8, dq, dk, dv = fp8_inputs(1, 4, 2, 300, 333, 208, seed=11)
+    q8, k8, v8, dq, dk, dv = fp8_inputs(1, 4, 2, 300, 333, D, seed=11)
     B, Hq, Nq, D = q8.shape
     n, pad = B * Hq * Nq * D, 4096
     big = torch.full((n + 2 * pad,), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -181,4 +183,4 @@ def test_fp8_in_bounds_and_deterministic():
     assert torch.isfinite(o.float()).all(), "some output element was not written"
     assert torch.isnan(big[:pad].float()).all() and torch.isnan(big[pad + n:].float()).all(), "O guard band written"
     assert (lbig[:pad] == 12345.0).all() and (lbig[pad + B * Hq * Nq:] == 12345.0).all(), "LSE guard band written"
-    _log("guard D=208", compare_fp8(o.cpu(), lse.cpu(), q8, k8, v8, dq, dk, dv))
+    _log(f"guard D={D}", compare_fp8(o.cpu(), lse.cpu(), q8, k8, v8, dq, dk, dv))
