@@ -329,10 +329,12 @@ BWD_FAULT_DK_UNSCALED = 2     # dK without the scale factor
 BWD_FAULT_GQA_LAST_HEAD = 3   # a KV head's gradient from the last head of its group only
 BWD_FAULT_KEEP_BIT_REVERSED = 4  # dropout keep words decoded with key 32 w + i at bit 31 - i
 BWD_FAULT_KEEP_WORD_SHIFTED = 5  # dropout keep words decoded one word late
+BWD_FAULT_DMASK_SCALED = 6       # the mask's gradient taken as scale * dS (the scores' gradient)
+BWD_FAULT_DMASK_ONE_HEAD = 7     # the mask's gradient from the first head of a broadcast only
 
 
 def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is_causal: bool = False,
-                       fault: int = BWD_FAULT_NONE, keep_bits=None, dropout_p: float = 0.0):
+                       fault: int = BWD_FAULT_NONE, keep_bits=None, dropout_p: float = 0.0, want_dmask: bool = False):
     """Gradients of the attention output with respect to Q, K and V in fp64 (the mask is a constant).
 
     q [B, Hq, Nq, D]; k, v [B, Hkv, Nkv, D]; do (the output's gradient) like q; torch bf16/fp16 or
@@ -348,6 +350,11 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
     With dropout (keep_bits [B, Hq, Nq, ceil(Nkv / 32)] uint32 words, ``oracle.philox`` layout, and
     dropout_p), the output is O = (P * M) V with M = keep / (1 - p) a constant; then
     dV = sum of (P * M)^T dO and the softmax's Jacobian is applied to dP = (dO V^T) * M.
+
+    With want_dmask (an additive floating mask), also the gradient with respect to the mask: the
+    logits are scale q.k + bias, so it is dS = P * (dP - rowsum(P * dP)) itself, summed over the
+    dimensions the mask broadcasts (size 1 in its shape).  Returns (dQ, dK, dV, dMask) then, dMask in
+    the mask's own shape.
     """
     import torch
 
@@ -369,6 +376,7 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
+    dS_all = np.zeros((B, Hq, Nq, Nkv)) if want_dmask else None
     Mdrop = None
     if keep_bits is not None:
         from .philox import KEEP_FAULT_BIT_REVERSED, KEEP_FAULT_NONE, KEEP_FAULT_WORD_SHIFTED, keep_matrix
@@ -391,10 +399,24 @@ def attention_backward(q, k, v, do, mask=None, scale: Optional[float] = None, is
             Md = 1.0 if Mdrop is None else Mdrop[b, h]
             dP = (dO[b, h] @ V[b, hk].T) * Md
             dS = P * dP if fault == BWD_FAULT_NO_DELTA else P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            if want_dmask:
+                dS_all[b, h] = scale * dS if fault == BWD_FAULT_DMASK_SCALED else dS
             dQ[b, h] = scale * (dS @ K[b, hk])
             dK[b, hk] += (1.0 if fault == BWD_FAULT_DK_UNSCALED else scale) * (dS.T @ Q[b, h])
             dV[b, hk] += (P * Md).T @ dO[b, h]
-    return dQ, dK, dV
+    if not want_dmask:
+        return dQ, dK, dV
+    if mask is None or mask.dtype == torch.bool:
+        raise ValueError("the mask's gradient needs an additive floating mask")
+    mshape = tuple(mask.shape)
+    full = (1,) * (4 - len(mshape)) + mshape
+    # sum over the broadcast dimensions (size 1 in the mask's shape)
+    axes = tuple(i for i in range(4) if full[i] == 1 and (B, Hq, Nq, Nkv)[i] != 1)
+    if fault == BWD_FAULT_DMASK_ONE_HEAD and full[1] == 1 and Hq > 1:
+        dS_all = dS_all[:, :1] * 1.0
+        axes = tuple(a for a in axes if a != 1)
+    dM = dS_all.sum(axis=axes, keepdims=True) if axes else dS_all
+    return dQ, dK, dV, dM.reshape(mshape)
 
 
 # Planted-mistake switches of the dropout form (tests of the pins only).

@@ -149,3 +149,56 @@ def test_fully_masked_rows_give_no_gradient():
     do2[0, 0, 1] = 0
     _, dK2, dV2 = oracle.attention_backward(q, k, v, do2, mask=mask)
     assert np.array_equal(dK, dK2) and np.array_equal(dV, dV2)
+
+
+def _torch_grads_with_mask(q, k, v, do, mask, scale, is_causal=False):
+    """float64 autograd through softmax(scale q.k + mask) V with the mask a leaf: its gradient."""
+    G = q.shape[1] // k.shape[1]
+    qd, kd, vd = (t.double() for t in (q, k, v))
+    md = mask.double().requires_grad_(True)
+    kr, vr = kd.repeat_interleave(G, dim=1), vd.repeat_interleave(G, dim=1)
+    s = (qd @ kr.transpose(-1, -2)) * scale + md
+    if is_causal:
+        Nq, Nkv = q.shape[2], k.shape[2]
+        vis = torch.arange(Nkv).view(1, Nkv) <= torch.arange(Nq).view(Nq, 1) + (Nkv - Nq)
+        s = s.masked_fill(~vis, -math.inf)
+    o = torch.softmax(s, dim=-1) @ vr
+    (g,) = torch.autograd.grad(o, (md,), do.double())
+    return g.numpy()
+
+
+def pin_dmask(fault=oracle.BWD_FAULT_NONE):
+    ok = True
+    g = torch.Generator().manual_seed(71)
+    for (B, Hq, Hkv, Nq, Nkv, D, causal, shape) in [(2, 4, 2, 5, 9, 8, False, (2, 1, 5, 9)),
+                                                     (1, 3, 3, 6, 6, 4, True, (1, 3, 6, 6)),
+                                                     (2, 2, 1, 4, 7, 8, False, (4, 7)),
+                                                     (2, 2, 2, 3, 5, 8, False, (1, 2, 1, 5))]:
+        q, k, v = random_qkv(B, Hq, Hkv, Nq, Nkv, D, seed=B + Nq)
+        do = torch.randn(B, Hq, Nq, D, generator=g).to(torch.bfloat16)
+        mask = torch.randn(*shape, generator=g)
+        scale = 1.0 / math.sqrt(D)
+        want = _torch_grads_with_mask(q, k, v, do, mask, scale, is_causal=causal)
+        *_, dm = oracle.attention_backward(q, k, v, do, mask=mask, is_causal=causal, fault=fault, want_dmask=True)
+        ok &= dm.shape == tuple(shape)
+        ok &= bool(np.all(np.abs(dm - want) <= 1e-10 * max(1.0, np.abs(want).max())))
+    return ok
+
+
+def test_mask_gradient_against_autograd():
+    assert pin_dmask()
+
+
+def test_mask_gradient_rows_sum_to_zero():
+    """Softmax is invariant to adding a constant to a row of logits, so each row of the logits'
+    gradient, and of a full mask's gradient, sums to zero."""
+    q, k, v = random_qkv(1, 2, 2, 4, 9, 8, seed=3)
+    do = torch.randn(1, 2, 4, 8, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    mask = torch.randn(1, 2, 4, 9, generator=torch.Generator().manual_seed(4))
+    *_, dm = oracle.attention_backward(q, k, v, do, mask=mask, want_dmask=True)
+    assert np.all(np.abs(dm.sum(axis=-1)) <= 1e-12)
+
+
+def test_mask_gradient_planted_mistakes_are_caught():
+    for fault in (oracle.BWD_FAULT_DMASK_SCALED, oracle.BWD_FAULT_DMASK_ONE_HEAD, oracle.BWD_FAULT_NO_DELTA):
+        assert not pin_dmask(fault), fault
