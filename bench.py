@@ -383,6 +383,8 @@ def main() -> int:
                           "config": dict(w.describe(), inputs="e4m3 per-head factors"),
                           "roofline": dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_FP8_TFLOPS,
                                            unit="TFLOP/s", frac=round(tf / PEAK_FP8_TFLOPS, 4),
+                                           traffic=measured_traffic(args.traffic_json, "fp8:" + w.name),
+                                           traffic_unit="HBM bytes per launch",
                                            kernel="ffpa_fwd_fp8_kernel")}), flush=True)
         return 0
     if packed:

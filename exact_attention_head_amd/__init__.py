@@ -24,7 +24,7 @@ from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "attn_fp8", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
-           "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
+           "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_bwd_mask_grad", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
            "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_head_dim", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
@@ -40,7 +40,7 @@ EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_erro
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
             "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout",
             "ffpa_kernel_head_dim", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fp8_kernel_head_dim",
-            "ffpa_clock_stamps")
+            "ffpa_clock_stamps", "ffpa_bwd_mask_grad")
 
 
 class MaskDesc(ctypes.Structure):
@@ -111,6 +111,9 @@ def library() -> ctypes.CDLL:
     lib.ffpa_bwd_dropout.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, i64, i64, i64, i64, i64, i64,
                                      f32, i32, i32, p, f32, p, ctypes.c_size_t, p]
     lib.ffpa_bwd_dropout.restype = i32
+    lib.ffpa_bwd_mask_grad.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, p, i64, i64, i64, i64, i64,
+                                       i64, f32, i32, i32, p, f32, p, ctypes.c_size_t, p]
+    lib.ffpa_bwd_mask_grad.restype = i32
     lib.ffpa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.ffpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffpa_dropout_keep.argtypes = [p, i64, i64, i64, i64, f32, ctypes.c_uint64, ctypes.c_uint32, p]
@@ -572,15 +575,25 @@ def ffpa_bwd_dropout(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv
                                       workspace, workspace_bytes, stream)
 
 
+def ffpa_bwd_mask_grad(q, k, v, o, dout, lse, mask: MaskDesc, dq, dk, dv, dmask, B, Hq, Hkv, Nq, Nkv, D, scale,
+                       is_causal, dtype, keep, dropout_p, workspace, workspace_bytes, stream) -> int:
+    """The raw backward entry point that also writes the additive mask's gradient; returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_bwd_mask_grad(q, k, v, o, dout, lse, m, dq, dk, dv, dmask, B, Hq, Hkv, Nq, Nkv, D,
+                                        ctypes.c_float(scale), int(is_causal), dtype, keep, ctypes.c_float(dropout_p),
+                                        workspace, workspace_bytes, stream)
+
+
 def ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D) -> int:
     return int(library().ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D))
 
 
 def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_causal: bool = False,
-                  scale: Optional[float] = None, dropout_p: float = 0.0, dropout_keep=None):
+                  scale: Optional[float] = None, dropout_p: float = 0.0, dropout_keep=None, mask_grad: bool = False):
     """Gradients (dQ, dK, dV) of ``attn`` at (query, key, value), given its output ``out``, its LSE and
-    the output's gradient.  Tensors [B, H, N, D] as for ``attn``; the mask gets no gradient.  After a
-    forward with dropout, pass its dropout_p and keep words (``return_dropout_keep``)."""
+    the output's gradient.  Tensors [B, H, N, D] as for ``attn``.  After a forward with dropout, pass its
+    dropout_p and keep words (``return_dropout_keep``).  With mask_grad (a floating attn_mask), returns
+    (dQ, dK, dV, dMask) with dMask the gradient of the additive mask: float32, in the mask's shape."""
     import torch
 
     q, k, v, o, do = (t.contiguous() for t in (query, key, value, out, grad_out))
@@ -596,9 +609,19 @@ def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_caus
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if mask_grad and (attn_mask is None or not attn_mask.is_floating_point()):
+        raise ValueError("mask_grad needs a floating (additive) attn_mask")
+    if mask_grad:
+        # a dimension the mask has at full size gets a gradient at full size, also if it is a
+        # stride-0 view: lay such masks out densely so that only size-1 dimensions broadcast
+        attn_mask = attn_mask.contiguous()
     desc, keep = (None, None) if attn_mask is None else _mask_desc(attn_mask.to(q.device), B, Hq, Nq, Nkv)
     dtype = FFPA_BF16 if q.dtype == torch.bfloat16 else FFPA_FP16
     sc = math.nan if scale is None else float(scale)
+    dm = None
+    if mask_grad:
+        m4 = keep  # the 4-D mask the descriptor points into: size 1 exactly where the stride is 0
+        dm = torch.empty((m4.shape[0], m4.shape[1], m4.shape[2], Nkv), dtype=torch.float32, device=q.device)
     if dropout_keep is not None:
         W = (Nkv + 31) // 32
         if dropout_keep.dtype != torch.int32 or tuple(dropout_keep.shape) != (B, Hq, Nq, W):
@@ -608,7 +631,14 @@ def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_caus
         raise ValueError("a backward with dropout needs the forward's keep words (dropout_keep)")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if dropout_keep is None:
+        if mask_grad:
+            kp = dropout_keep.data_ptr() if dropout_keep is not None else None
+            st = ffpa_bwd_mask_grad(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), desc, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dm.data_ptr(),
+                                    B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal), dtype, kp,
+                                    float(dropout_p) if dropout_keep is not None else 0.0, ws.data_ptr(), nbytes,
+                                    stream)
+        elif dropout_keep is None:
             st = ffpa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), desc,
                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nkv, D, sc, bool(is_causal),
                           dtype, ws.data_ptr(), nbytes, stream)
@@ -620,7 +650,13 @@ def attn_backward(query, key, value, out, grad_out, lse, attn_mask=None, is_caus
     del keep
     if st != OK:
         _raise(st)
-    return dq, dk, dv
+    if not mask_grad:
+        return dq, dk, dv
+    if attn_mask.shape[-1] == 1 and Nkv != 1:
+        # a mask constant along the keys adds the same value to a whole row of logits, which the
+        # softmax cancels: its gradient is exactly zero
+        dm = torch.zeros(attn_mask.shape, dtype=torch.float32, device=q.device)
+    return dq, dk, dv, dm.reshape(attn_mask.shape)
 
 
 def _autograd_function():
@@ -628,7 +664,8 @@ def _autograd_function():
 
     class AttnFunction(torch.autograd.Function):
         """Forward through ffpa_fwd or ffpa_fwd_dropout (keeping O, the LSE and the keep words),
-        backward through ffpa_bwd or ffpa_bwd_dropout."""
+        backward through ffpa_bwd or ffpa_bwd_dropout, or ffpa_bwd_mask_grad when a floating attn_mask
+        needs its gradient."""
 
         @staticmethod
         def forward(ctx, query, key, value, attn_mask, is_causal, scale, enable_gqa, dropout_p=0.0, dropout_seed=None):
@@ -649,10 +686,13 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, grad_o, grad_lse):
             query, key, value, o, lse = ctx.saved_tensors
-            dq, dk, dv = attn_backward(query, key, value, o, grad_o, lse, attn_mask=ctx.attn_mask,
-                                       is_causal=ctx.is_causal, scale=ctx.scale, dropout_p=ctx.dropout_p,
-                                       dropout_keep=ctx.keep)
-            return dq, dk, dv, None, None, None, None, None, None
+            want_dm = bool(ctx.needs_input_grad[3]) and ctx.attn_mask is not None
+            grads = attn_backward(query, key, value, o, grad_o, lse, attn_mask=ctx.attn_mask,
+                                  is_causal=ctx.is_causal, scale=ctx.scale, dropout_p=ctx.dropout_p,
+                                  dropout_keep=ctx.keep, mask_grad=want_dm)
+            dq, dk, dv = grads[:3]
+            dm = grads[3] if want_dm else None
+            return dq, dk, dv, dm, None, None, None, None, None
 
     return AttnFunction
 
@@ -670,7 +710,8 @@ def AttnFunction():
 
 def attn_with_grad(query, key, value, attn_mask=None, is_causal: bool = False, scale: Optional[float] = None,
                    enable_gqa: bool = False, dropout_p: float = 0.0, dropout_seed: Optional[int] = None):
-    """``attn`` recorded for autograd: O is differentiable in query, key and value (with dropout, the
-    keep words drawn by the forward are reused by the backward)."""
+    """``attn`` recorded for autograd: O is differentiable in query, key and value, and in a floating
+    attn_mask that requires grad (with dropout, the keep words drawn by the forward are reused by the
+    backward)."""
     o, _ = AttnFunction().apply(query, key, value, attn_mask, is_causal, scale, enable_gqa, dropout_p, dropout_seed)
     return o

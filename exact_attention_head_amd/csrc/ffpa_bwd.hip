@@ -16,6 +16,10 @@
 // With attention dropout (ffpa_bwd_dropout: O = (P * M) V with M = keep / (1 - p) a constant), the
 // 16-bit copy of P that forms dV holds P * M, and the row term is applied to dP * M:
 // dS = scale P (dP M - Delta), with Delta = rowsum(dO * O) of the dropped-out O.
+// With the additive mask's gradient (ffpa_bwd_mask_grad): the logits are scale S + bias, so the
+// bias's gradient is the logits' gradient P (dP - Delta) itself, summed over the dimensions the mask
+// broadcasts; the row-term kernel also keeps it in f32 (over dP, no longer needed), and one more
+// kernel adds each chunk's share into the dense f32 result, every element owned by one thread.
 // The matrix products are plain dense GEMMs (rocBLAS strided-batched, bf16/fp16 in, fp32
 // accumulate); the softmax recompute, the row term and the group sums are the kernels below.
 #include <hip/hip_fp16.h>
@@ -99,6 +103,7 @@ struct GroupArgs {
   const uint32_t* keep;  // dropout keep words [B, Hq, Nq, keep_w] (null: no dropout)
   int keep_w;
   float drop_scale;      // 1 / (1 - p)
+  int keep_ds;           // also keep the logits' gradient P (dP - Delta) in f32, over dP
 };
 
 // The dropout factor M of (row r of query head h, key k): keep bit / (1 - p).
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(256) void bwd_probs_kernel(float* __restrict__ s, u
   p16[i] = store16(g.keep != nullptr ? p * drop_factor(g, fh, r, k) : p, g.is_fp16);
 }
 
-// dS = scale P (dP - Delta) as 16-bit, over [nh, Nq, Nkv].
-__global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ p, const float* __restrict__ dp,
+// dS = scale P (dP - Delta) as 16-bit, over [nh, Nq, Nkv]; with keep_ds, dP[i] becomes P (dP - Delta).
+__global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ p, float* __restrict__ dp,
                                                      uint16_t* __restrict__ ds16, GroupArgs g) {
   const int64_t total = (int64_t)g.nh * g.Nq * g.Nkv;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -140,7 +145,76 @@ __global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ p
   const int fh = g.fh0 + (int)(gr / g.Nq);  // flat query head
   const float dl = g.delta[(int64_t)fh * g.Nq + r];
   const float dpm = g.keep != nullptr ? dp[i] * drop_factor(g, fh, r, (int)(i % g.Nkv)) : dp[i];
-  ds16[i] = store16(g.scale * p[i] * (dpm - dl), g.is_fp16);
+  const float dsu = p[i] * (dpm - dl);
+  ds16[i] = store16(g.scale * dsu, g.is_fp16);
+  if (g.keep_ds) dp[i] = dsu;
+}
+
+// The additive mask's gradient, dense f32 [Bm, Hm, Nqm, Nkv] with Bm = 1 where the mask broadcasts
+// over the batch (else B), Hm likewise over the heads, Nqm over the query rows.
+struct MaskGradArgs {
+  float* dmask;
+  int bcast_b, bcast_h, bcast_q;
+  int Hm, Nqm;
+  int npairs;  // mask heads (b', h') that the chunk's query heads reach
+  int b0;      // first batch of the chunk (batch broadcast kept, head broadcast)
+};
+
+// Mask head j of the chunk [fh0, fh0 + nh): its flat index in the mask's [Bm, Hm] and the query heads
+// fh = first, first + step, ... < end that map to it.
+__device__ inline void mask_pair(const GroupArgs& g, const MaskGradArgs& a, int j, int64_t& mh, int& first,
+                                 int& end, int& step) {
+  const int e = g.fh0 + g.nh;
+  step = 1;
+  if (!a.bcast_b && !a.bcast_h) {  // one query head each
+    first = g.fh0 + j;
+    end = first + 1;
+    mh = first;
+  } else if (!a.bcast_b) {  // a batch's heads
+    const int b = a.b0 + j;
+    first = max(g.fh0, b * g.Hq);
+    end = min(e, (b + 1) * g.Hq);
+    mh = b;
+  } else if (!a.bcast_h) {  // one head index across the chunk's batches
+    first = g.fh0 + j;
+    end = e;
+    step = g.Hq;
+    mh = first % g.Hq;
+  } else {  // every head of the chunk
+    first = g.fh0;
+    end = e;
+    mh = 0;
+  }
+}
+
+// dmask[mh, r', k] += sum over the chunk's query heads mapping to mh (and over the rows if the mask
+// broadcasts over them) of the logits' gradient kept by bwd_ds_kernel in dsu [nh, Nq, Nkv].
+__global__ __launch_bounds__(256) void bwd_mask_grad_kernel(const float* __restrict__ dsu, GroupArgs g, MaskGradArgs a) {
+  const int64_t per_pair = (int64_t)a.Nqm * g.Nkv;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.npairs * per_pair) return;
+  const int j = (int)(i / per_pair);
+  const int rq = (int)((i % per_pair) / g.Nkv);
+  const int k = (int)(i % g.Nkv);
+  int64_t mh;
+  int first, end, step;
+  mask_pair(g, a, j, mh, first, end, step);
+  const int r0 = a.bcast_q ? 0 : rq, r1 = a.bcast_q ? g.Nq : rq + 1;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int fh = first; fh < end; fh += step) {
+    const float* src = dsu + ((int64_t)(fh - g.fh0) * g.Nq) * g.Nkv + k;
+    int r = r0;
+    for (; r + 4 <= r1; r += 4)
+      for (int u = 0; u < 4; ++u) acc[u] += src[(int64_t)(r + u) * g.Nkv];
+    for (; r < r1; ++r) acc[0] += src[(int64_t)r * g.Nkv];
+  }
+  float* dst = a.dmask + (mh * a.Nqm + rq) * g.Nkv + k;
+  *dst += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) x[i] = 0.f;
 }
 
 // out[j] = 16-bit(sum over the G heads of acc[g * n + j]), j < n.
@@ -221,7 +295,8 @@ int bwd_check(const void* q, const void* k, const void* v, const void* o, const 
   if ((uintptr_t)lse & 3) return bfail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
   if (D < 64 || D > 1024 || D % 64 != 0)
     return bfail(FFPA_ERR_UNSUPPORTED, "head dim %lld: 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
-  if (Nq >= (1LL << 30) || Nkv >= (1LL << 30) || (Hq / Hkv) * Nq * Nkv >= (1LL << 38) || Nkv * D >= (1LL << 31))
+  // the elementwise kernels take one thread per score of a chunk: at most 2^32 threads per launch
+  if (Nq >= (1LL << 30) || Nkv >= (1LL << 30) || (Hq / Hkv) * Nq * Nkv > (1LL << 32) - 256 || Nkv * D >= (1LL << 31))
     return bfail(FFPA_ERR_UNSUPPORTED, "sizes beyond the backward's indexing");
   if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
     if (mask->kind < FFPA_MASK_BOOL_U8 || mask->kind > FFPA_MASK_ADD_FP16)
@@ -246,7 +321,8 @@ size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, i
 static int bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                     const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
                     int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* workspace,
-                    size_t workspace_bytes, void* stream, const uint32_t* keep, float dropout_p) {
+                    size_t workspace_bytes, void* stream, const uint32_t* keep, float dropout_p,
+                    float* dmask = nullptr) {
   const Workspace w = layout(B, Hq, Hkv, Nq, Nkv, D);
   if (workspace == nullptr || workspace_bytes < w.total || ((uintptr_t)workspace & 255))
     return bfail(FFPA_ERR_VALUE, "workspace must be 256-byte aligned and hold ffpa_bwd_workspace_size() = %zu bytes",
@@ -263,6 +339,18 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   uint16_t* P16 = (uint16_t*)(ws + w.p16);
   float* dKacc = (float*)(ws + w.dk);
   float* dVacc = (float*)(ws + w.dv);
+
+  MaskGradArgs ma{};
+  if (dmask != nullptr) {
+    ma.dmask = dmask;
+    ma.bcast_b = mask->stride_b == 0;
+    ma.bcast_h = mask->stride_h == 0;
+    ma.bcast_q = mask->stride_q == 0;
+    ma.Hm = ma.bcast_h ? 1 : (int)Hq;
+    ma.Nqm = ma.bcast_q ? 1 : (int)Nq;
+    const int64_t n = (ma.bcast_b ? 1 : B) * ma.Hm * ma.Nqm * Nkv;
+    hipLaunchKernelGGL(bwd_fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dmask, n);
+  }
 
   const int64_t rows = B * Hq * Nq;
   hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const uint16_t*)o,
@@ -323,6 +411,7 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
       ga.msh = mask->stride_h;
       ga.msq = mask->stride_q;
     }
+    ga.keep_ds = dmask != nullptr;
     const unsigned eblocks = (unsigned)(((int64_t)nh * sq + 255) / 256);
     rocblas_status r;
     // S^T[Nkv x Nq] = K Q^T  (per head of the chunk)
@@ -336,6 +425,15 @@ static int bwd_impl(const void* q, const void* k, const void* v, const void* o, 
     r = gemm(T_, N_, m, n, d, Vh, t16, d, kvs, dOg, t16, d, qh, dP, f32, m, sq, nh);
     if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dP failed (%d)", (int)r);
     hipLaunchKernelGGL(bwd_ds_kernel, dim3(eblocks), dim3(256), 0, s, S, dP, P16, ga);
+    if (dmask != nullptr) {
+      const int e = (int)u0 + nh;
+      if (!ma.bcast_b && !ma.bcast_h) ma.npairs = nh;
+      else if (!ma.bcast_b) ma.b0 = (int)(u0 / Hq), ma.npairs = (int)((e - 1) / Hq) - ma.b0 + 1;
+      else if (!ma.bcast_h) ma.npairs = nh < Hq ? nh : (int)Hq;
+      else ma.npairs = 1;
+      const int64_t nt = (int64_t)ma.npairs * ma.Nqm * Nkv;
+      hipLaunchKernelGGL(bwd_mask_grad_kernel, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, dP, ga, ma);
+    }
     // dQ^T[D x Nq] = K^T dS^T, written in the output dtype
     r = gemm(N_, N_, d, n, m, Kh, t16, d, kvs, P16, t16, m, sq, dQg, t16, d, qh, nh);
     if (r != rocblas_status_success) return bfail(FFPA_ERR_HIP, "GEMM dQ failed (%d)", (int)r);
@@ -375,6 +473,26 @@ int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
   if (keep == nullptr || ((uintptr_t)keep & 3)) return bfail(FFPA_ERR_VALUE, "keep must be non-null and 4-byte aligned");
   return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, workspace,
                   workspace_bytes, stream, keep, dropout_p);
+}
+
+int ffpa_bwd_mask_grad(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                       const ffpa_mask_t* mask, void* dq, void* dk, void* dv, float* dmask, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype,
+                       const uint32_t* keep, float dropout_p, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = bwd_check(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  if (mask == nullptr || mask->kind == FFPA_MASK_NONE || mask->kind == FFPA_MASK_BOOL_U8)
+    return bfail(FFPA_ERR_VALUE, "the mask's gradient needs an additive (float32, bf16 or fp16) mask");
+  if (dmask == nullptr || ((uintptr_t)dmask & 3)) return bfail(FFPA_ERR_VALUE, "dmask must be non-null and 4-byte aligned");
+  if (B * Hq >= (1LL << 31)) return bfail(FFPA_ERR_UNSUPPORTED, "B * Hq beyond the mask gradient's indexing");
+  if (keep == nullptr) {
+    if (dropout_p != 0.f) return bfail(FFPA_ERR_VALUE, "dropout_p must be 0 without keep words");
+  } else {
+    if (!(dropout_p >= 0.f && dropout_p < 1.f)) return bfail(FFPA_ERR_VALUE, "dropout probability must lie in [0, 1)");
+    if ((uintptr_t)keep & 3) return bfail(FFPA_ERR_VALUE, "keep must be 4-byte aligned");
+  }
+  return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, workspace,
+                  workspace_bytes, stream, keep, dropout_p, dmask);
 }
 
 }  // extern "C"

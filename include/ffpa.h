@@ -238,7 +238,31 @@ int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                      int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, const uint32_t* keep,
                      float dropout_p, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace ffpa_bwd and ffpa_bwd_dropout need for these sizes:
+/*
+ * ffpa_bwd_mask_grad -- ffpa_bwd (keep == NULL, dropout_p 0) or
+ * ffpa_bwd_dropout (keep, dropout_p as there), plus the gradient of the
+ * additive mask (ffpa-attn "API Reference": the attn_mask of the SDPA-style
+ * call; SDPA differentiates a floating mask as a bias added to the logits).
+ * The logits are scale * q.k + mask, so the mask's gradient is the logits'
+ * gradient P * (dout V^T [* M] - Delta), summed over every dimension along
+ * which the mask broadcasts (its stride 0: stride_b, stride_h or stride_q).
+ *   mask   additive (FFPA_MASK_ADD_F32 / _BF16 / _FP16); required.  Keys
+ *          contiguous (stride_k 1), as everywhere.
+ *   dmask  device, float32, written: dense [B', H', Nq', Nkv] with B' = 1 if
+ *          mask->stride_b is 0 and B otherwise, H' = 1 if stride_h is 0 and
+ *          Hq otherwise, Nq' = 1 if stride_q is 0 and Nq otherwise.
+ *          Entries the mask excludes (-inf, causal) get 0.  The sums run in a
+ *          fixed order: repeated calls give identical bits.
+ * dq, dk, dv as ffpa_bwd.  Errors as ffpa_bwd / ffpa_bwd_dropout, plus
+ * FFPA_ERR_VALUE for a missing or boolean mask, a null or misaligned dmask,
+ * or dropout_p != 0 without keep words.  Workspace: ffpa_bwd_workspace_size().
+ */
+int ffpa_bwd_mask_grad(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                       const ffpa_mask_t* mask, void* dq, void* dk, void* dv, float* dmask, int64_t B, int64_t Hq,
+                       int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype,
+                       const uint32_t* keep, float dropout_p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ffpa_bwd, ffpa_bwd_dropout and ffpa_bwd_mask_grad need for these sizes:
  * about C * (10 * Nq * Nkv + 8 * Nkv * D) + 4 * B * Hq * Nq, where C, the
  * query heads handled per step, is Hq/Hkv with grouped heads, and otherwise
  * as many heads (at most B * Hq, at least one) as keep C * (10 * Nq * Nkv +
