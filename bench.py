@@ -441,7 +441,7 @@ def main() -> int:
             tag = ("backward " if backward else ("dropout p=0.1 " if dropout else ("fp8 " if fp8 else ""))) + w2.name
             log(f"{tag}: {ms2:.4f} ms/launch, {tf2:.1f} TFLOPS ({100 * tf2 / peak:.1f}% of the "
                 f"{'fp8' if fp8 else 'bf16'} peak)")
-            kname = ("ffpa_bwd (library GEMMs + HIP kernels)" if backward else
+            kname = ("ffpa_bwd_kernel (dK/dV pass + dQ pass)" if backward else
                      ("ffpa_fwd_fp8_kernel" if fp8 else ffpa.kernel_name(w2.D)))
             secondary.append(dict(workload=tag, D=w2.D,
                                   dtype="e4m3" if fp8 else ("bf16" if w2.dtype == torch.bfloat16 else "fp16"),

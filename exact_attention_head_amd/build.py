@@ -27,7 +27,8 @@ def _dims(macro: str) -> list[int]:
     with open(os.path.join(CSRC, "ffpa_launch.hpp")) as f:
         txt = f.read()
     body = txt[txt.index(f"#define {macro}(X)"):]
-    body = body[:body.index("\n")] if macro == "FFPA_FP8_FOR_EACH_D" else body[:body.index("\n\n")]
+    one_line = macro != "FFPA_FOR_EACH_D"  # the others are one-line macros
+    body = body[:body.index("\n")] if one_line else body[:body.index("\n\n")]
     return [int(x) for x in re.findall(r"X\((\d+)\)", body)]
 
 
@@ -39,6 +40,16 @@ def head_dims() -> list[int]:
 def fp8_head_dims() -> list[int]:
     """Head dims with compiled fp8 kernels."""
     return _dims("FFPA_FP8_FOR_EACH_D")
+
+
+def bwd_kernel_dims() -> list[int]:
+    """Kernel head dims of the fused backward."""
+    return _dims("FFPA_BWD_FOR_EACH_KD")
+
+
+def bwd_pad_kernel_dims() -> list[int]:
+    """Kernel head dims of the fused backward that also serve smaller head dims (columns skipped)."""
+    return _dims("FFPA_BWD_PAD_KD")
 
 
 def _compile(src: str, obj: str, defines: list[str], remarks: bool = False) -> tuple[str, str]:
@@ -110,6 +121,13 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     for d in fp8_head_dims():
         tasks.append((os.path.join(CSRC, "ffpa_fp8.hip"), os.path.join(BUILD, f"ffpa_fp8_d{d}.o"),
                       [f"-DFFPA_FP8_D={d}"]))
+    # the fused backward: one object per kernel head dim (and one for its padded head dims)
+    for kd in bwd_kernel_dims():
+        tasks.append((os.path.join(CSRC, "ffpa_bwd_inst.hip"), os.path.join(BUILD, f"ffpa_bwdk_d{kd}.o"),
+                      [f"-DFFPA_BWD_KD={kd}", "-DFFPA_BWD_PAD=0"]))
+    for kd in bwd_pad_kernel_dims():
+        tasks.append((os.path.join(CSRC, "ffpa_bwd_inst.hip"), os.path.join(BUILD, f"ffpa_bwdk_d{kd}_p1.o"),
+                      [f"-DFFPA_BWD_KD={kd}", "-DFFPA_BWD_PAD=1"]))
     # largest kernels first
     kd = lambda path: re.search(r"_d(\d+)(_p\d)?\.o$", path)  # per-head-dim kernel objects
     tasks.sort(key=lambda t: -int(kd(t[1]).group(1)) if kd(t[1]) else 0)
@@ -140,10 +158,7 @@ def build(jobs: int | None = None, verbose: bool = True, report: bool = False) -
     if hazards:
         raise RuntimeError("MFMA / LDS hazards in the generated code:\n" + "\n".join(hazards[:20]))
     tmp = LIB + ".tmp"
-    # the backward's matrix products use the ROCm GEMM library
-    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(HIPCC))), "lib")
-    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, f"-L{rocm_lib}",
-                        "-lrocblas", f"-Wl,-rpath,{rocm_lib}"],
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")

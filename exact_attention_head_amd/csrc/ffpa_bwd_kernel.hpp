@@ -1,0 +1,527 @@
+// Fused backward of the attention forward on gfx950 (ffpa-attn "API Reference": the backward of
+// ffpa_attn_func, run as SDPA's backward): dQ, dK, dV, and the additive mask's gradient, from Q, K,
+// V, dO, the forward's fp32 LSE and Delta = rowsum(dO * O).  No score matrix is kept in memory.
+//
+// Two passes of one kernel template.  Each wave keeps its own block of 32 indices ("stationary") in
+// registers and loops over tiles of 32 indices of the other side, streamed through LDS:
+//   dQ pass: a wave owns 32 query rows (its Q and dO rows in VGPRs) and streams the K and V tiles
+//     of its KV head:   S^T = K Q^T,  dP^T = V dO^T,  dS^T = P^T * (dP^T - Delta),  dQ^T += K^T dS^T.
+//   dK/dV pass: a wave owns 32 keys (its K and V rows in VGPRs) and streams the Q and dO tiles of
+//     every query head of its KV group:   S = Q K^T,  dP = dO V^T,  dS = P * (dP - Delta),
+//     dV^T += dO^T P,  dK^T += Q^T dS.
+// P = exp(scale S + bias - LSE) is recomputed from the forward's LSE, so neither pass needs the
+// other's results and no row statistic is formed here.  The accumulators (dQ^T, or dK^T and dV^T)
+// live in AGPRs; dQ and dK take the softmax scale once, when they are stored.  With attention
+// dropout (keep bits M, factor 1/(1-p)): dV^T += dO^T (P M) and dS = P (dP M - Delta).
+//
+// Wave roles.  Two waves share a stationary block of 32 (four above D = 512): role A holds the
+// Q-side operand of the score product (dQ pass: Q; dK/dV pass: K) and forms S, role B the dO side
+// (dO; V) and forms dP, each over all columns (above 512: two waves per role, one per column half,
+// whose partial tiles are summed).  The finished tiles are exchanged through LDS, so that every
+// wave of the block holds S and dP and forms P and dS itself.  Then the dQ pass splits dQ's
+// columns among the block's waves; in the dK/dV pass role A accumulates dK and role B dV.  A wave
+// thus keeps one stationary operand (at most 128 VGPRs) and at most 256 accumulators.  Head dims
+// whose columns do not split into 32-column blocks this way run the next such kernel head dim with
+// the columns past D skipped.
+//
+// Products (v_mfma_f32_32x32x16, inline assembly as in the forward): a score tile is
+// (streamed x stationary), so lane l holds stationary index l % 32 and accumulator element i holds
+// streamed index 8 (i / 4) + 4 (l / 32) + i % 4.  Packed to 16 bits, element 8 kk + j of a lane is
+// the B operand of the accumulation products at contraction slot j of step kk, provided the
+// streamed index of slot j is read in that same order on the A side: the transposed LDS reads
+// (ds_read_b64_tr_b16) fetch rows 16 kk + 4 (l / 32) + 0..3 and, with a second read, + 8.
+//
+// LDS tiles: per tensor, 32-column blocks of [32 rows][64 bytes] (2 KiB), chunk c of row r stored
+// at position c ^ ((r >> 2) & 3) (conflict-free for the operand reads and the transposed reads),
+// filled by buffer_load_dwordx4 ... lds (rows past the tensor's end read as zero); the dK/dV pass
+// stages each tile's LSE, Delta and keep words beside it.  Tiles are double-buffered where two fit
+// next to the exchange slots (D <= 512), else the next tile is loaded once the current one has been
+// consumed.
+#pragma once
+
+#include <type_traits>
+
+#include "ffpa_launch.hpp"
+
+namespace ffpa {
+
+template <int KD>
+struct BwdTiling {
+  static constexpr int GW = KD <= 512 ? 2 : 4;  // waves per stationary block of 32
+  static constexpr int NH = GW / 2;             // column parts of the score products
+  static constexpr int SW = KD / NH;            // score columns per wave
+  static constexpr int NKS = SW / 16;           // 16-column steps of a score product
+  static constexpr int AWQ = KD / GW;           // dQ columns per wave
+  static constexpr int AWK = KD / NH;           // dK (or dV) columns per wave
+  static constexpr int RG = 4 / GW;             // stationary blocks per workgroup
+  static constexpr int NBLK = KD / 32;          // 32-column blocks per tensor tile
+  static constexpr int TILE = 2 * NBLK * 2048;  // the two streamed tensors of one 32-index tile
+  static constexpr int ROWS = 768;              // staged per-row data of a tile: LSE, Delta, keep words
+  static constexpr int BUF = TILE + ROWS;
+  static constexpr int EXCH = 4 * 4096;         // one partial score tile per wave
+  static constexpr int NBUF = 2 * BUF + EXCH <= 160 * 1024 ? 2 : 1;
+  static constexpr int LDS_BYTES = NBUF * BUF + EXCH;
+  static constexpr bool OK = KD % 64 == 0 && KD >= 64 && KD <= 1024 && AWQ % 32 == 0 && AWK % 32 == 0;
+};
+
+// The bias of one (row, key) of a runtime mask kind: -inf for an excluded boolean entry.
+__device__ inline float bwd_bias(const void* m, int kind, int64_t off) {
+  switch (kind) {
+    case kMaskBoolU8: return ((const unsigned char*)m)[off] ? 0.f : kNegInf;
+    case kMaskAddF32: return ((const float*)m)[off];
+    case kMaskAddBf16: return widen_bf16(((const uint16_t*)m)[off]);
+    case kMaskAddFp16: return widen_fp16(((const uint16_t*)m)[off]);
+    default: return 0.f;
+  }
+}
+
+// Completes this wave's LDS reads; the tied operands keep every use of the values after it.
+__device__ inline void bwd_lds_wait(f32x4 (&x)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])::"memory");
+}
+__device__ inline void bwd_lds_wait3(f32x4& x, f32x4& y, f32x4& z) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z)::"memory");
+}
+
+// Score products: d = a * b (+ d) into VGPRs.  The leading s_nop 1 gives the 2 wait states a
+// product needs after a VALU write of an operand - the compiler may move a stationary fragment
+// between register files (v_accvgpr_read) right before its use.
+template <typename T>
+__device__ inline void bwd_mma_first(f32x16& d, const i32x4& a, const i32x4& b) {
+  if constexpr (std::is_same<T, Bf16>::value)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+template <typename T>
+__device__ inline void bwd_mma_acc(f32x16& d, const i32x4& a, const i32x4& b) {
+  if constexpr (std::is_same<T, Bf16>::value)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
+// Roles.  The GW waves of a stationary block split the work by tensor: role A holds the Q side of
+// the score product (dQ pass: Q; dK/dV pass: K) and forms S, role B the dO side (dO; V) and forms
+// dP; above D = 512 each role is split once more by columns (h).  They exchange the finished tiles
+// through LDS, so every wave of the block holds S and dP.  Accumulation: dQ pass, wave gw takes
+// columns [gw AWQ, (gw + 1) AWQ) of dQ; dK/dV pass, role A takes dK and role B dV, columns
+// [h AWK, (h + 1) AWK).
+template <typename T, int KD, bool DQ, bool PAD>
+__global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
+  using BT = BwdTiling<KD>;
+  using E = Elem<T>;
+  static_assert(BT::OK, "unsupported kernel head dim");
+  constexpr int GW = BT::GW, NH = BT::NH, SW = BT::SW, NKS = BT::NKS, RG = BT::RG, NBLK = BT::NBLK;
+  constexpr int AW = DQ ? BT::AWQ : BT::AWK;
+  constexpr int NCB = AW / 32;
+  constexpr int BUF = BT::BUF, TILE = BT::TILE, NBUF = BT::NBUF;
+  __shared__ __attribute__((aligned(1024))) char smem[BT::LDS_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, in an SGPR
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int rg = wave / GW, gw = wave % GW;
+  const int role = gw / NH, h = gw % NH;
+  const int sc0 = h * SW;                       // first score column of this wave
+  const int ac0 = DQ ? gw * AW : h * AW;        // first accumulated column
+  const int D = a.D;                            // columns in memory (the row stride); D <= KD
+  const int G = a.Hq / a.Hkv;
+  const int NS = DQ ? a.Nq : a.Nkv;  // stationary extent
+  const int NT = DQ ? a.Nkv : a.Nq;  // streamed extent
+  const int nsb = (NS + 32 * RG - 1) / (32 * RG);
+  const int nblk = (DQ ? a.B * a.Hq : a.B * a.Hkv) * nsb;
+  // blocks are dealt to the 8 XCDs in turn: give each XCD a contiguous run of blocks (heads), so
+  // that the workgroups streaming one head's tiles share that XCD's L2
+  int blk = (int)blockIdx.x;
+  {
+    const int per = nblk / 8;
+    if (blk < per * 8) blk = (blk % 8) * per + blk / 8;
+  }
+  const int head = blk / nsb, sb = blk % nsb;
+  const int b = DQ ? head / a.Hq : head / a.Hkv;
+  const int hq = DQ ? head % a.Hq : 0;
+  const int hkv = DQ ? hq / G : head % a.Hkv;
+  const int s0wg = sb * 32 * RG;
+  const int s0 = s0wg + rg * 32;  // this wave's stationary block
+  const int coff = a.Nkv - a.Nq;  // causal: key k is visible from row r when k <= r + coff
+  const int s = s0 + l32;         // this lane's stationary index
+  const int sc = s < NS ? s : NS - 1;
+  const int64_t kvh = (int64_t)(b * a.Hkv + hkv) * a.Nkv * D;
+
+  // ---- this wave's stationary rows (its score columns) as B operands: lane -> index s, 8 columns.
+  // The dK/dV pass at D = 1024 keeps its last NRL fragments in L2 instead, re-read at every tile
+  // (the 256 accumulators and the other 24 fragments leave no room for them).
+  constexpr int NRL = (!DQ && KD == 1024) ? 8 : 0;
+  constexpr int NKR = NKS - NRL;  // fragments held in registers
+  i32x4 xf[NKS];
+  const uint16_t* xrow;  // the lane's stationary row, from the wave's first score column
+  {
+    const uint16_t* xb;
+    if constexpr (DQ) xb = (role == 0 ? a.q : a.dout) + (int64_t)(b * a.Hq + hq) * a.Nq * D;
+    else xb = (role == 0 ? a.k : a.v) + kvh;
+    xrow = xb + (int64_t)sc * D + sc0 + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKR; ++kk) {
+      const bool in = !PAD || sc0 + 16 * kk < D;
+      xf[kk] = in ? *(const i32x4*)(xrow + 16 * kk) : i32x4{0, 0, 0, 0};
+    }
+    vm_wait<0>();
+#pragma unroll
+    for (int kk = 0; kk < NKR; ++kk) asm volatile("" : "+v"(xf[kk]));
+  }
+  // dQ pass: the lane's row statistics
+  float lse_s = 0.f, dl_s = 0.f;
+  if constexpr (DQ) {
+    const int64_t ri = (int64_t)(b * a.Hq + hq) * a.Nq + sc;
+    lse_s = a.lse[ri];
+    dl_s = a.delta[ri];
+  }
+
+  // ---- streamed tiles
+  int ntiles, rb0 = 0, nrbh = 1;
+  if constexpr (DQ) {
+    int kend = a.Nkv;
+    if (a.causal) {
+      const int rlast = (s0wg + 32 * RG < a.Nq ? s0wg + 32 * RG : a.Nq) - 1;
+      kend = rlast + coff + 1 < a.Nkv ? rlast + coff + 1 : a.Nkv;
+    }
+    ntiles = (kend + 31) / 32;
+  } else {
+    const int nrb = (a.Nq + 31) / 32;
+    if (a.causal) rb0 = (s0wg - coff > 0 ? s0wg - coff : 0) / 32;
+    nrbh = nrb - rb0;
+    ntiles = G * nrbh;
+  }
+  // tile t: the streamed index of its row 0, and the query head it belongs to (dK/dV pass)
+  auto tile_pos = [&](int t, int& t0, int& qh) {
+    if constexpr (DQ) {
+      t0 = 32 * t;
+      qh = hq;
+    } else {
+      const int g = t / nrbh;
+      t0 = 32 * (rb0 + t % nrbh);
+      qh = hkv * G + g;
+    }
+  };
+
+  // loads: wave w fills 1 KiB pieces w, w + 4, ... of each tensor's tile; piece j = rows 16 (j % 2)
+  // .. +15 of 32-column block j / 2; lane t takes row 16 (j % 2) + t / 4, physical chunk t % 4,
+  // i.e. logical chunk (t % 4) ^ ((row >> 2) & 3).  Piece 4c + w is block 2c + w / 2, rows
+  // 16 (w % 2) ..: the lane's byte offset is fixed, the block step 128 c a scalar offset, and the
+  // tile's first row the descriptor's base (its record count ends at the tensor's last row, so rows past
+  // it read as zero).
+  const uint32_t smem_addr = lds_addr(smem);
+  const bool has_drop = a.keep != nullptr;
+  uint32_t vlane;
+  {
+    const int lrow = 16 * (wave & 1) + (lane >> 2);
+    const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+    vlane = (uint32_t)(lrow * D + (wave >> 1) * 32 + lchunk * 8) * 2u;
+  }
+  auto issue_tile = [&](int t, int buf) {
+    int t0, qh;
+    tile_pos(t, t0, qh);
+    const uint16_t* ub;
+    const uint16_t* wb;
+    if constexpr (DQ) {
+      ub = a.k + kvh;
+      wb = a.v + kvh;
+    } else {
+      ub = a.q + (int64_t)(b * a.Hq + qh) * a.Nq * D;
+      wb = a.dout + (int64_t)(b * a.Hq + qh) * a.Nq * D;
+    }
+    ub += (int64_t)t0 * D;
+    wb += (int64_t)t0 * D;
+    const int bytes = (int)((int64_t)(NT - t0) * D * 2);  // the descriptor's 32-bit record count
+    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wb, (short)0, bytes, 0x00020000);
+    // LDS destinations from the 32-bit LDS address (no generic-pointer conversion); made opaque
+    // here so that the compiler forms each one before its load instead of keeping them all in
+    // SGPRs across the loop
+    uint32_t dst = smem_addr + (uint32_t)(buf * BUF + wave * 1024);
+    asm volatile("" : "+s"(dst));
+    static_for<NBLK / 2>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      if (!PAD || (2 * c + (wave >> 1)) * 32 < D) {
+        // the block step goes in the scalar offset: the instruction's immediate offset would move
+        // the LDS destination as well
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (FFPA_LDS void*)(uintptr_t)(dst + 4 * c * 1024), 16, vlane,
+                                                 128 * c, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (FFPA_LDS void*)(uintptr_t)(dst + NBLK * 2048 + 4 * c * 1024), 16,
+                                                 vlane, 128 * c, 0, 0);
+      }
+    });
+    if constexpr (!DQ) {
+      // the tile's rows: LSE and Delta (lane l -> row l % 32), keep words of the workgroup's keys
+      // (lane l -> row l % 32, word s0wg / 32 + l / 32); rows past Nq read as zero
+      if (wave == 0) {
+        const int64_t fr = (int64_t)(b * a.Hq + qh) * a.Nq + t0;
+        const int nb = (a.Nq - t0) * 4;
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + fr), (short)0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.delta + fr), (short)0, nb, 0x00020000);
+        const uint32_t rows = smem_addr + (uint32_t)(buf * BUF + TILE);
+        const uint32_t ro = (uint32_t)l32 * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FFPA_LDS void*)(uintptr_t)rows, 4, ro, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FFPA_LDS void*)(uintptr_t)(rows + 256), 4, ro, 0, 0, 0);
+        if (has_drop) {
+          const int kb = (int)((int64_t)(a.Nq - t0) * a.keep_w * 4);
+          const __amdgpu_buffer_rsrc_t rk =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(a.keep + fr * a.keep_w), (short)0, kb, 0x00020000);
+          const uint32_t ko = ((uint32_t)l32 * (uint32_t)a.keep_w + (uint32_t)(s0wg / 32 + hi)) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FFPA_LDS void*)(uintptr_t)(rows + 512), 4, ko, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---- per-lane LDS addresses (block offsets are immediates; buffer offsets added at run time)
+  // score operand read: row l32 of the role's tensor, 16-column step q of a block: chunk 2q + hi
+  const uint32_t sbase = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 32) * 2048);
+  uint32_t fa[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) fa[q] = sbase + l32 * 64 + (((2 * q + hi) ^ ((l32 >> 2) & 3)) * 16);
+  // transposed read (accumulation products): lanes of a 16-lane group read rows 4 (l / 32) + i16 / 4
+  // (and + 8), columns 16 ((l / 16) % 2) + 4 (i16 % 4) .. + 3 of a block; the lane receives column
+  // l % 32 of rows 4 (l / 32) + 0..3 (and + 8)
+  const int atens = DQ ? 0 : role;  // dQ: K^T; dK: Q^T; dV: dO^T
+  const uint32_t abase = smem_addr + (uint32_t)(atens * NBLK * 2048 + (ac0 / 32) * 2048);
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int trow = 4 * (g16 >> 1) + (i16 >> 2);
+  const int tchunk = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  const uint32_t ta = abase + trow * 64 + ((tchunk ^ ((trow >> 2) & 3)) * 16) + 8 * (i16 & 1);
+  const uint32_t tb = abase + (trow + 8) * 64 + ((tchunk ^ (((trow + 8) >> 2) & 3)) * 16) + 8 * (i16 & 1);
+  // partial-tile exchange: slot per wave, 16 bytes per lane in four 1 KiB pieces
+  const uint32_t ex_base = smem_addr + NBUF * BUF;
+  const uint32_t ex_mine = ex_base + wave * 4096 + lane * 16;
+  // dst = (ADD ? dst : 0) + the partial tile of slot, read a quarter at a time
+  auto take_partial = [&](f32x16& dst, int slot, auto add_c) {
+    constexpr bool ADD = decltype(add_c)::value;
+    const uint32_t pa = ex_base + (uint32_t)(slot * 4096) + lane * 16;
+    f32x4 p[4];
+    p[0] = lds_read_f4_async<0>(pa);
+    p[1] = lds_read_f4_async<1024>(pa);
+    p[2] = lds_read_f4_async<2048>(pa);
+    p[3] = lds_read_f4_async<3072>(pa);
+    bwd_lds_wait(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (ADD) dst[4 * j + e] += p[j][e];
+        else dst[4 * j + e] = p[j][e];
+      }
+  };
+
+  const bool has_mask = a.mask_kind != kMaskNone;
+  const float scale = a.scale;
+  const int64_t mask_b = (int64_t)b * a.msb;
+
+  f32x16 acc[NCB];  // dQ^T, dK^T or dV^T columns of this wave
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) acc[c] = f32x16{};
+
+  if (ntiles > 0) issue_tile(0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = NBUF == 2 ? (t & 1) : 0;
+    int t0, qh;
+    tile_pos(t, t0, qh);
+    vm_wait<0>();
+    block_sync();  // tile t visible; every wave is done with tile t - 1 (and its buffer)
+    uint32_t kw = 0;
+    if constexpr (DQ) {
+      // requested before the next tile's loads, so that waiting for it does not wait for those
+      if (has_drop) kw = a.keep[((int64_t)(b * a.Hq + hq) * a.Nq + sc) * a.keep_w + t];
+    }
+    if (NBUF == 2 && t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    const uint32_t boff = (uint32_t)(buf * BUF);
+    if constexpr (NRL > 0) {
+      // (the address is made opaque so that the loads stay inside the loop)
+      const uint16_t* xr = xrow;
+      asm volatile("" : "+v"(xr));
+#pragma unroll
+      for (int kk = NKR; kk < NKS; ++kk) {
+        const bool in = !PAD || sc0 + 16 * kk < D;
+        xf[kk] = in ? *(const i32x4*)(xr + 16 * kk) : i32x4{0, 0, 0, 0};
+      }
+    }
+
+    // ---- the role's score product over its columns (fragments read PF products ahead)
+    f32x16 own;
+    // fragments read PF products ahead (two where the dK/dV pass's 256 accumulators and a
+    // 512-column stationary operand leave no room for more)
+    constexpr int PF = (!DQ && KD > 896) ? 2 : 4;
+    i32x4 fr[PF + 1];
+    auto read_s = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr uint32_t off = (uint32_t)((m / 2) * 2048);
+      static_assert(off < 65536, "ds offset field");
+      fr[m % (PF + 1)] = lds_read_b128_async<off>(fa[m % 2] + boff);
+    };
+    static_for<PF>([&](auto mc) {
+      if constexpr (decltype(mc)::value < NKS) read_s(mc);
+    });
+    static_for<NKS>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (m + PF < NKS) read_s(std::integral_constant<int, m + PF>{});
+      constexpr int after = (m + PF < NKS ? m + PF : NKS - 1) - m;
+      lgkm_wait<after>();
+      if (!PAD || sc0 + 16 * m < D) {
+        if constexpr (m == 0) bwd_mma_first<T>(own, fr[m % (PF + 1)], xf[m]);
+        else bwd_mma_acc<T>(own, fr[m % (PF + 1)], xf[m]);
+      }
+    });
+    mma_guard_s(own);
+
+    // ---- exchange: S = sum over h of role A's partial tiles, dP = likewise for role B
+    static_for<4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      lds_write_b128_async<j * 1024>(ex_mine, f32x4{own[4 * j], own[4 * j + 1], own[4 * j + 2], own[4 * j + 3]});
+    });
+    block_sync();
+    // (two terms per sum: their order does not change the rounded result, so every wave of the
+    // block holds the same S and dP)
+    f32x16 sS, sP;
+    {
+      const int slot0 = rg * GW;
+      const std::true_type add;
+      const std::false_type set;
+      if (role == 0) {
+        sS = own;
+        if constexpr (NH == 2) take_partial(sS, slot0 + (h ^ 1), add);
+        take_partial(sP, slot0 + NH, set);
+        if constexpr (NH == 2) take_partial(sP, slot0 + NH + 1, add);
+      } else {
+        sP = own;
+        if constexpr (NH == 2) take_partial(sP, slot0 + NH + (h ^ 1), add);
+        take_partial(sS, slot0, set);
+        if constexpr (NH == 2) take_partial(sS, slot0 + 1, add);
+      }
+    }
+
+    // ---- probabilities and the logits' gradient of the lane's 16 elements
+    // the accumulation product's B operand: dS, or for dV (role B of the dK/dV pass) the dropped-out P
+    const bool use_p = !DQ && role == 1;
+    uint32_t gw2[8];  // the operand's 16 values, two per dword
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 lse4, dl4, kw4;
+      if constexpr (!DQ) {
+        const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
+        lse4 = lds_read_f4_async<0>(ra);
+        dl4 = lds_read_f4_async<256>(ra);
+        kw4 = lds_read_f4_async<0>(ra + 512 + (uint32_t)(rg * 128));
+        bwd_lds_wait3(lse4, dl4, kw4);
+      }
+      float gv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * g + e;
+        const int ti = t0 + 8 * g + 4 * hi + e;
+        const int row = DQ ? s : ti, key = DQ ? ti : s;
+        const float lse = DQ ? lse_s : lse4[e];
+        const float dl = DQ ? dl_s : dl4[e];
+        const bool valid = row < a.Nq && key < a.Nkv && (!a.causal || key <= row + coff) && lse != kNegInf;
+        float x = sS[i] * scale;
+        if (has_mask) {
+          const int64_t off = mask_b + (int64_t)(DQ ? hq : qh) * a.msh + (int64_t)(row < a.Nq ? row : a.Nq - 1) * a.msq +
+                              (key < a.Nkv ? key : a.Nkv - 1);
+          x += bwd_bias(a.mask, a.mask_kind, off);
+        }
+        const float p = valid ? exp2f((x - lse) * kLog2e) : 0.f;
+        float m = 1.f;
+        if (has_drop) {
+          const uint32_t w = DQ ? kw : (uint32_t)__float_as_uint(kw4[e]);
+          const int bit = DQ ? (8 * g + 4 * hi + e) : (key & 31);
+          m = ((w >> bit) & 1u) ? a.drop_scale : 0.f;
+        }
+        const float ds = p * (sP[i] * m - dl);
+        gv[e] = use_p ? p * m : ds;
+        if constexpr (DQ) {
+          if (a.dmask != nullptr && gw == 0 && row < a.Nq && key < a.Nkv) {
+            const int64_t di = (((int64_t)(a.dm_bb ? 0 : b) * a.dm_hm + (a.dm_bh ? 0 : hq)) * a.dm_nqm +
+                                (a.dm_bq ? 0 : row)) * a.Nkv + key;
+            if (a.dm_atomic) atomicAdd(a.dmask + di, ds);
+            else a.dmask[di] = ds;
+          }
+        }
+      }
+      gw2[2 * g] = pack2<T>(gv[0], gv[1]);
+      gw2[2 * g + 1] = pack2<T>(gv[2], gv[3]);
+    }
+    const i32x4 g0 = i32x4{(int)gw2[0], (int)gw2[1], (int)gw2[2], (int)gw2[3]};
+    const i32x4 g1 = i32x4{(int)gw2[4], (int)gw2[5], (int)gw2[6], (int)gw2[7]};
+
+    // ---- accumulation products: acc[cb] += (tensor^T) G over this wave's columns
+    constexpr int NA = NCB * 2;
+    i32x2 tl[PF + 1], th[PF + 1];
+    auto read_a = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int cb = m / 2, kk = m % 2;
+      constexpr uint32_t off = (uint32_t)(cb * 2048 + kk * 1024);
+      static_assert(off < 65536, "ds offset field");
+      tl[m % (PF + 1)] = lds_read_tr_async<off>(ta + boff);
+      th[m % (PF + 1)] = lds_read_tr_async<off>(tb + boff);
+    };
+    static_for<PF>([&](auto mc) {
+      if constexpr (decltype(mc)::value < NA) read_a(mc);
+    });
+    static_for<NA>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int cb = m / 2, kk = m % 2;
+      if constexpr (m + PF < NA) read_a(std::integral_constant<int, m + PF>{});
+      constexpr int after = 2 * ((m + PF < NA ? m + PF : NA - 1) - m);
+      lgkm_wait<after>();
+      if (!PAD || ac0 + 32 * cb < D) {
+        const i32x4 af = i32x4{tl[m % (PF + 1)][0], tl[m % (PF + 1)][1], th[m % (PF + 1)][0], th[m % (PF + 1)][1]};
+        E::mma_acc_agpr(acc[cb], af, kk == 0 ? g0 : g1);
+      }
+    });
+
+    // keeps the accumulators in AGPRs across the loop, after the wait states their last products need
+    mma_guard_all<NCB>(acc);
+
+    if constexpr (NBUF == 1) {
+      if (t + 1 < ntiles) {
+        block_sync();  // every wave is done with the buffer
+        issue_tile(t + 1, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: lane -> stationary index s, element i -> column ac0 + 32 cb + 8 (i / 4) + 4 hi + i % 4
+  mma_guard_all<NCB>(acc);
+  if (s < NS) {
+    uint16_t* out;
+    if constexpr (DQ) out = a.dq + (int64_t)(b * a.Hq + hq) * a.Nq * D;
+    else out = (role == 0 ? a.dk : a.dv) + kvh;
+    const float f = (DQ || role == 0) ? scale : 1.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      if (PAD && ac0 + 32 * cb >= D) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = ac0 + 32 * cb + 8 * g + 4 * hi;
+        const uint32_t w0 = pack2<T>(acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f);
+        const uint32_t w1 = pack2<T>(acc[cb][4 * g + 2] * f, acc[cb][4 * g + 3] * f);
+        *(i32x2*)(out + (int64_t)s * D + col) = i32x2{(int)w0, (int)w1};
+      }
+    }
+  }
+}
+
+// Both passes on one stream: dK/dV first, then dQ.
+template <typename T, int KD, bool PAD>
+hipError_t launch_bwd_fused(const BwdArgs& a, hipStream_t stream) {
+  using BT = BwdTiling<KD>;
+  const int nsk = (a.Nkv + 32 * BT::RG - 1) / (32 * BT::RG);
+  const int nsq = (a.Nq + 32 * BT::RG - 1) / (32 * BT::RG);
+  hipLaunchKernelGGL((ffpa_bwd_kernel<T, KD, false, PAD>), dim3((unsigned)(a.B * a.Hkv * nsk)), dim3(256), 0, stream,
+                     a);
+  hipLaunchKernelGGL((ffpa_bwd_kernel<T, KD, true, PAD>), dim3((unsigned)(a.B * a.Hq * nsq)), dim3(256), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace ffpa

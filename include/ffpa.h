@@ -17,13 +17,11 @@
  * the page's varlen entry returns.  A row whose keys are all excluded gets
  * O = 0 and LSE = -inf.
  *
- * Every step of the forward entries and of the dropout keep-bit generator
- * runs in hand-written HIP kernels on the caller's stream; they allocate
- * nothing, keep no pointer after a call returns and need no workspace.  The
- * backward entries (ffpa_bwd, ffpa_bwd_dropout) run their matrix products as
- * ROCm library GEMMs over a caller-provided workspace, and the GEMM library
- * keeps one handle per device, created on first use.  Apart from those
- * handles the only state is a thread-local error message, so calls from
+ * Every step of every entry runs in hand-written HIP kernels on the caller's
+ * stream; no entry allocates, and none keeps a pointer after a call returns.
+ * The forward entries and the dropout keep-bit generator need no workspace;
+ * the backward entries take a small caller-provided one (one float per query
+ * row).  The only state is a thread-local error message, so calls from
  * several host threads are safe.
  */
 #ifndef FFPA_H_
@@ -192,9 +190,9 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
 /*
  * ffpa_bwd -- enqueue the backward of ffpa_fwd on `stream`: the gradients of
  * O with respect to Q, K and V, given dout = dL/dO (the ffpa-attn "API
- * Reference" page supports the backward of ffpa_attn_func; the mask is a
- * constant and gets no gradient).  With P the softmax of the forward's
- * logits and Delta[r] = <dout[r], o[r]>:
+ * Reference" page supports the backward of ffpa_attn_func; here the mask is a
+ * constant - ffpa_bwd_mask_grad also returns its gradient).  With P the
+ * softmax of the forward's logits and Delta[r] = <dout[r], o[r]>:
  *   dV = sum over a KV head's group of P^T dout
  *   dS = P * (dout V^T - Delta),  dQ = scale dS K,
  *   dK = scale * sum over the group of dS^T Q.
@@ -207,15 +205,15 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
  *   dq   device, [B, Hq, Nq, D]; dk, dv device, [B, Hkv, Nkv, D]; written,
  *        in the input dtype
  *   workspace  device, 256-byte aligned, at least ffpa_bwd_workspace_size()
- *        bytes, owned by the caller; its contents are scratch
+ *        bytes, owned by the caller; it receives Delta (scratch)
  *
- * The products run as library GEMMs (bf16/fp16 in, fp32 accumulate) on the
- * score matrices of one chunk of query heads at a time (a KV group, or
- * several ungrouped heads), held in the workspace; the softmax
- * recompute, the Delta term and the group sums run in this library's kernels.
- * On the first call on a device the GEMM library creates a handle (and its own
- * device workspace), kept until the process ends; calls are serialised on it.
- * Errors as for ffpa_fwd; FFPA_ERR_VALUE also for a missing or short workspace.
+ * Three kernels on `stream`: Delta; a KV-stationary pass forming dK and dV
+ * (each workgroup loops over the query rows of every head of its KV group);
+ * a Q-stationary pass forming dQ.  Both passes recompute P from q, k, the
+ * mask and the LSE, so no score matrix is stored.  Head dims: 64 <= D <=
+ * 1024 with D % 64 == 0.  Products take bf16/fp16 operands (P and dS rounded
+ * once to the input type) with fp32 accumulation.  Errors as for ffpa_fwd;
+ * FFPA_ERR_VALUE also for a missing or short workspace.
  */
 int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
@@ -251,8 +249,11 @@ int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
  *   dmask  device, float32, written: dense [B', H', Nq', Nkv] with B' = 1 if
  *          mask->stride_b is 0 and B otherwise, H' = 1 if stride_h is 0 and
  *          Hq otherwise, Nq' = 1 if stride_q is 0 and Nq otherwise.
- *          Entries the mask excludes (-inf, causal) get 0.  The sums run in a
- *          fixed order: repeated calls give identical bits.
+ *          Entries the mask excludes (-inf, causal) get 0.  Without
+ *          broadcast dimensions (B' = B, H' = Hq, Nq' = Nq, or those of size
+ *          1) each element is written once and repeated calls give identical
+ *          bits; the sums over broadcast dimensions use float atomic adds,
+ *          whose order may vary from call to call.
  * dq, dk, dv as ffpa_bwd.  Errors as ffpa_bwd / ffpa_bwd_dropout, plus
  * FFPA_ERR_VALUE for a missing or boolean mask, a null or misaligned dmask,
  * or dropout_p != 0 without keep words.  Workspace: ffpa_bwd_workspace_size().
@@ -263,10 +264,7 @@ int ffpa_bwd_mask_grad(const void* q, const void* k, const void* v, const void* 
                        const uint32_t* keep, float dropout_p, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace ffpa_bwd, ffpa_bwd_dropout and ffpa_bwd_mask_grad need for these sizes:
- * about C * (10 * Nq * Nkv + 8 * Nkv * D) + 4 * B * Hq * Nq, where C, the
- * query heads handled per step, is Hq/Hkv with grouped heads, and otherwise
- * as many heads (at most B * Hq, at least one) as keep C * (10 * Nq * Nkv +
- * 8 * Nkv * D) within 4 GiB.  0 for invalid sizes.  Host-only. */
+ * 4 * B * Hq * Nq (Delta), rounded up to 256.  0 for invalid sizes.  Host-only. */
 size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D);
 
 /* The host-side argument check ffpa_fwd performs, without enqueuing anything

@@ -367,3 +367,25 @@ def test_fp8_kernel_head_dim():
         assert lib.ffpa_fp8_kernel_head_dim(D) == want, D
     for bad in (0, 8, 100, 520, 1040, 2048):
         assert lib.ffpa_fp8_kernel_head_dim(bad) == 0
+
+
+# ---- backward entries: host checks and the workspace (one float per query row, for Delta)
+def test_bwd_workspace_is_delta_only():
+    for (B, Hq, Hkv, Nq, Nkv, D) in [(1, 8, 8, 4096, 4096, 512), (2, 3, 1, 5, 7, 64), (4, 16, 16, 1024, 4096, 1024)]:
+        want = (4 * B * Hq * Nq + 255) // 256 * 256
+        assert ffpa.ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D) == want
+    assert ffpa.ffpa_bwd_workspace_size(1, 3, 2, 8, 8, 64) == 0  # Hq not a multiple of Hkv
+
+
+def bwd(D=512, Nq=100, Nkv=130, B=1, Hq=2, Hkv=1, causal=False, ws=M, nbytes=1 << 20):
+    return ffpa.ffpa_bwd(Q, K, V, O, O + 0x1000_0000, L, None, DQ, DK, DV, B, Hq, Hkv, Nq, Nkv, D, math.nan, causal,
+                         ffpa.FFPA_BF16, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), ffpa.ERR_UNSUPPORTED), (dict(D=1088), ffpa.ERR_UNSUPPORTED), (dict(D=32), ffpa.ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE), (dict(causal=True, Nq=200, Nkv=100), ffpa.ERR_VALUE),
+    (dict(Nq=(1 << 31) // 512), ffpa.ERR_UNSUPPORTED), (dict(ws=None), ffpa.ERR_VALUE),
+    (dict(nbytes=16), ffpa.ERR_VALUE), (dict(ws=M + 16), ffpa.ERR_VALUE)])
+def test_bwd_argument_errors(kw, status):
+    assert bwd(**kw) == status, detail()

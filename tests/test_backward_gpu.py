@@ -1,4 +1,4 @@
-"""Parity of the backward (ffpa_bwd, through the C ABI) with the fp64 oracle's gradients, on the GPU.
+"""Parity of the fused backward (ffpa_bwd, through the C ABI) with the fp64 oracle's gradients, on the GPU.
 
 The forward runs first (its O and LSE feed the backward, as in training); the gradients are compared
 element by element with the oracle's exact gradients of the same inputs.  The bar, derived from the
@@ -55,10 +55,45 @@ def _log(name, m):
     print(f"[bwd] {name}: {json.dumps(m)}", flush=True)
 
 
-@pytest.mark.parametrize("D", [64, 128, 256, 320, 512, 640, 1024])
+# every kernel head dim of the fused backward, and the head dims that run a larger one with the
+# columns past D skipped (576, 704, 832, 960)
+@pytest.mark.parametrize("D", [64, 128, 192, 256, 320, 384, 448, 512, 576, 640, 704, 768, 832, 896, 960, 1024])
 def test_backward_head_dims(D):
     q, k, v, do = _case(1, 2, 2, 130, 200, D, seed=D)
     _log(f"D={D}", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
+
+
+@pytest.mark.parametrize("D", [128, 576, 1024])
+def test_backward_fp16_head_dims(D):
+    q, k, v, do = _case(2, 2, 1, 97, 161, D, dtype=torch.float16, seed=D + 1)
+    _log(f"fp16 D={D}", _compare(_grads_gpu(q, k, v, do, is_causal=True), q, k, v, do, is_causal=True))
+
+
+def test_backward_tiny_and_single_rows():
+    for (Nq, Nkv) in [(1, 40), (2, 3), (33, 33), (31, 95)]:
+        q, k, v, do = _case(1, 3, 1, Nq, Nkv, 128, seed=Nq + Nkv)
+        _log(f"Nq={Nq} Nkv={Nkv}", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
+
+
+def test_backward_single_key():
+    """One key: the softmax is constant, so dQ and dK are exactly zero (the kernels leave rounding
+    noise of Delta's 16-bit O) and dV = sum over the group of dO."""
+    q, k, v, do = _case(1, 3, 1, 5, 1, 128, seed=3)
+    dq, dk, dv = _grads_gpu(q, k, v, do)
+    want = oracle.attention_backward(q, k, v, do)
+    assert np.abs(want[0]).max() == 0 and np.abs(want[1]).max() == 0
+    scale_v = float(np.abs(want[2]).max())
+    assert float(dq.abs().max()) <= 1e-3 * scale_v and float(dk.abs().max()) <= 1e-3 * scale_v
+    g = dv.double().numpy()
+    assert np.linalg.norm(g - want[2]) <= REL_L2 * np.linalg.norm(want[2])
+
+
+def test_backward_full_size_self_attention():
+    """The D=512 self-attention workload (B=1, H=8, N=4096) that the bench times, all gradients."""
+    w = W.large_d_self()
+    q, k, v = W.random_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, seed=101)
+    do = torch.randn(w.B, w.Hq, w.Nq, w.D, generator=torch.Generator().manual_seed(102)).to(torch.bfloat16)
+    _log("B1 H8 N4096 D512", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
 
 
 @pytest.mark.parametrize("Nq,Nkv", [(64, 64), (100, 333), (257, 260)])

@@ -64,7 +64,14 @@ def _run(B, Hq, Hkv, Nq, Nkv, D, shape, *, dtype=torch.bfloat16, mdtype=torch.fl
     again = ffpa.attn_backward(qd, kd, vd, o, dod, lse, attn_mask=md, is_causal=causal, dropout_p=p,
                                dropout_keep=keep, mask_grad=True)[3]
     torch.cuda.synchronize()
-    assert torch.equal(got[3], again), "the mask gradient is not reproducible bit for bit"
+    full = len(shape) == 4 and tuple(shape) == (B, Hq, Nq, Nkv)
+    if full:
+        # one writer per element: identical bits on every call
+        assert torch.equal(got[3], again), "the mask gradient is not reproducible bit for bit"
+    else:
+        # broadcast dimensions are summed with atomic adds, in an order that may vary: up to B Hq Nq
+        # fp32 terms per element, whose rounding differences stay far below the parity bar below
+        assert torch.allclose(got[3], again, rtol=0, atol=1e-3 * float(again.abs().max()) + 1e-30)
     assert got[3].dtype == torch.float32 and tuple(got[3].shape) == tuple(shape)
     want = oracle.attention_backward(q, k, v, do, mask=mask, is_causal=causal, keep_bits=words, dropout_p=p,
                                      want_dmask=True)
@@ -126,12 +133,11 @@ def test_mask_grad_tiny_and_single_key():
 
 
 @pytest.mark.parametrize("kind", ["batch-bcast", "key-padding"])
-def test_mask_grad_across_chunks(kind):
-    """Nq = Nkv = 4096 over 32 heads: the backward takes 25 query heads per step, so steps cross a
-    batch's boundary and a mask head's sum is spread over two steps."""
+def test_mask_grad_large(kind):
+    """Nq = Nkv = 4096 over 32 heads: every workgroup of many heads adds into the broadcast mask's
+    gradient."""
     B, Hq, N, D = 2, 16, 4096, 64
-    assert ffpa.ffpa_bwd_workspace_size(B, Hq, Hq, N, N, D) < 25 * (10 * N * N + 8 * N * D) + 4 * B * Hq * N + 4096
-    _run(B, Hq, Hq, N, N, D, SHAPES[kind](B, Hq, N, N), seed=23, name=f"chunks {kind}")
+    _run(B, Hq, Hq, N, N, D, SHAPES[kind](B, Hq, N, N), seed=23, name=f"large {kind}")
 
 
 def test_autograd_mask_gradient():
