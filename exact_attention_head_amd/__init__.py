@@ -24,7 +24,7 @@ from typing import Optional
 
 __all__ = ["attn", "attn_varlen", "attn_fp8", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fwd", "ffpa_check_args", "ffpa_fwd_varlen", "ffpa_check_varlen_args",
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
-           "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_bwd_mask_grad", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
+           "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_bwd_mask_grad", "ffpa_bwd_noalloc", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
            "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_head_dim", "kernel_name", "FFPA_BF16", "FFPA_FP16",
            "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
 
@@ -40,7 +40,7 @@ EXPORTED = ("ffpa_fwd", "ffpa_check_args", "ffpa_status_string", "ffpa_last_erro
             "ffpa_fwd_strided", "ffpa_check_strided_args", "ffpa_bwd", "ffpa_bwd_workspace_size",
             "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args", "ffpa_bwd_dropout",
             "ffpa_kernel_head_dim", "ffpa_fwd_fp8", "ffpa_check_fp8_args", "ffpa_fp8_kernel_head_dim",
-            "ffpa_clock_stamps", "ffpa_bwd_mask_grad")
+            "ffpa_clock_stamps", "ffpa_bwd_mask_grad", "ffpa_bwd_noalloc")
 
 
 class MaskDesc(ctypes.Structure):
@@ -114,6 +114,9 @@ def library() -> ctypes.CDLL:
     lib.ffpa_bwd_mask_grad.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, p, i64, i64, i64, i64, i64,
                                        i64, f32, i32, i32, p, f32, p, ctypes.c_size_t, p]
     lib.ffpa_bwd_mask_grad.restype = i32
+    lib.ffpa_bwd_noalloc.argtypes = [p, p, p, p, p, p, ctypes.POINTER(MaskDesc), p, p, p, i64, i64, i64, i64, i64, i64,
+                                     f32, i32, i32, p]
+    lib.ffpa_bwd_noalloc.restype = i32
     lib.ffpa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64]
     lib.ffpa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffpa_dropout_keep.argtypes = [p, i64, i64, i64, i64, f32, ctypes.c_uint64, ctypes.c_uint32, p]
@@ -582,6 +585,15 @@ def ffpa_bwd_mask_grad(q, k, v, o, dout, lse, mask: MaskDesc, dq, dk, dv, dmask,
     return library().ffpa_bwd_mask_grad(q, k, v, o, dout, lse, m, dq, dk, dv, dmask, B, Hq, Hkv, Nq, Nkv, D,
                                         ctypes.c_float(scale), int(is_causal), dtype, keep, ctypes.c_float(dropout_p),
                                         workspace, workspace_bytes, stream)
+
+
+def ffpa_bwd_noalloc(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale,
+                     is_causal, dtype, stream) -> int:
+    """The raw backward entry point that takes no workspace (its Delta buffer is built into the
+    library, at most 2^22 query rows); returns the status code."""
+    m = ctypes.byref(mask) if mask is not None else None
+    return library().ffpa_bwd_noalloc(q, k, v, o, dout, lse, m, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D,
+                                      ctypes.c_float(scale), int(is_causal), dtype, stream)
 
 
 def ffpa_bwd_workspace_size(B, Hq, Hkv, Nq, Nkv, D) -> int:

@@ -17,6 +17,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "../../include/ffpa.h"
 #include "ffpa_launch.hpp"
@@ -64,6 +65,14 @@ __global__ __launch_bounds__(256) void bwd_fill_zero_kernel(float* __restrict__ 
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ffpa_bwd_noalloc's Delta buffer: a device array in the code object (each GPU holds its own copy
+// for as long as the library is loaded), 4 Mi rows = 16 MiB.  Host code reaches it only through
+// the address hipGetSymbolAddress returns for the current device.
+constexpr int64_t kNoAllocRows = 1LL << 22;
+static __device__ __align__(256) float scratch[kNoAllocRows];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device, set on the first call there
 
 int bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
               const ffpa_mask_t* mask, const void* dq, const void* dk, const void* dv, int64_t B, int64_t Hq,
@@ -203,6 +212,32 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (st != FFPA_OK) return st;
   return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, workspace,
                   workspace_bytes, stream, nullptr, 0.f);
+}
+
+int ffpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* stream) {
+  const int st = bwd_check(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
+  if (st != FFPA_OK) return st;
+  if (B * Hq * Nq > kNoAllocRows)
+    return bfail(FFPA_ERR_UNSUPPORTED, "B * Hq * Nq = %lld query rows exceed the %lld of the built-in buffer",
+                 (long long)(B * Hq * Nq), (long long)kNoAllocRows);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return bfail(FFPA_ERR_HIP, "no current device");
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return bfail(FFPA_ERR_HIP, "could not find the built-in buffer's address: %s", hipGetErrorString(e));
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return bwd_impl(q, k, v, o, dout, lse, mask, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype, ws,
+                  (size_t)kNoAllocRows * 4, stream, nullptr, 0.f);
 }
 
 int ffpa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -221,6 +221,21 @@ int ffpa_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* stream);
 
 /*
+ * ffpa_bwd_noalloc -- ffpa_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and results.  Its Delta buffer is a device array built into the
+ * library, at most 4,194,304 (2^22) query rows (B * Hq * Nq); larger sizes
+ * return FFPA_ERR_UNSUPPORTED.  It calls no allocating routine; the first
+ * call on a device looks up that device's copy of the array.  Every call on
+ * one GPU shares that array: calls that overlap on one GPU (two streams, two
+ * host threads) race and must be serialised by the caller.
+ */
+int ffpa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     const ffpa_mask_t* mask, void* dq, void* dk, void* dv, int64_t B, int64_t Hq, int64_t Hkv,
+                     int64_t Nq, int64_t Nkv, int64_t D, float scale, int is_causal, int dtype, void* stream);
+
+/*
  * ffpa_bwd_dropout -- the backward of ffpa_fwd_dropout: as ffpa_bwd, with
  * the forward's keep words `keep` (device, [B, Hq, Nq, ceil(Nkv / 32)]
  * uint32, read only) and dropout_p.  With M = keep / (1 - dropout_p) a
