@@ -219,7 +219,9 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
     vlane = (uint32_t)(lrow * D + (wave >> 1) * 32 + lchunk * 8) * 2u;
   }
-  auto issue_tile = [&](int t, int buf) {
+  // PARTS: 1 the U tile (K, or Q), 2 the W tile (V, or dO), 4 the staged rows (dK/dV pass)
+  auto issue_tile = [&](int t, int buf, auto parts_c) {
+    constexpr int PARTS = decltype(parts_c)::value;
     int t0, qh;
     tile_pos(t, t0, qh);
     const uint16_t* ub;
@@ -246,13 +248,15 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       if (!PAD || (2 * c + (wave >> 1)) * 32 < D) {
         // the block step goes in the scalar offset: the instruction's immediate offset would move
         // the LDS destination as well
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (FFPA_LDS void*)(uintptr_t)(dst + 4 * c * 1024), 16, vlane,
-                                                 128 * c, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (FFPA_LDS void*)(uintptr_t)(dst + NBLK * 2048 + 4 * c * 1024), 16,
-                                                 vlane, 128 * c, 0, 0);
+        if constexpr ((PARTS & 1) != 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (FFPA_LDS void*)(uintptr_t)(dst + 4 * c * 1024), 16, vlane,
+                                                   128 * c, 0, 0);
+        if constexpr ((PARTS & 2) != 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (FFPA_LDS void*)(uintptr_t)(dst + NBLK * 2048 + 4 * c * 1024),
+                                                   16, vlane, 128 * c, 0, 0);
       }
     });
-    if constexpr (!DQ) {
+    if constexpr (!DQ && (PARTS & 4) != 0) {
       // the tile's rows: LSE and Delta (lane l -> row l % 32), keep words of the workgroup's keys
       // (lane l -> row l % 32, word s0wg / 32 + l / 32); rows past Nq read as zero
       if (wave == 0) {
@@ -322,7 +326,8 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
 #pragma unroll
   for (int c = 0; c < NCB; ++c) acc[c] = f32x16{};
 
-  if (ntiles > 0) issue_tile(0, 0);
+  constexpr std::integral_constant<int, 7> kAll{};
+  if (ntiles > 0) issue_tile(0, 0, kAll);
   for (int t = 0; t < ntiles; ++t) {
     const int buf = NBUF == 2 ? (t & 1) : 0;
     int t0, qh;
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       // requested before the next tile's loads, so that waiting for it does not wait for those
       if (has_drop) kw = a.keep[((int64_t)(b * a.Hq + hq) * a.Nq + sc) * a.keep_w + t];
     }
-    if (NBUF == 2 && t + 1 < ntiles) issue_tile(t + 1, buf ^ 1);
+    if (NBUF == 2 && t + 1 < ntiles) issue_tile(t + 1, buf ^ 1, kAll);
     const uint32_t boff = (uint32_t)(buf * BUF);
     if constexpr (NRL > 0) {
       // (the address is made opaque so that the loads stay inside the loop)
@@ -380,6 +385,11 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       lds_write_b128_async<j * 1024>(ex_mine, f32x4{own[4 * j], own[4 * j + 1], own[4 * j + 2], own[4 * j + 3]});
     });
     block_sync();
+    // single buffer, dQ pass: V has been read for the last time (by the dP products); its next tile
+    // can be loaded while K is still needed
+    if constexpr (NBUF == 1 && DQ) {
+      if (t + 1 < ntiles) issue_tile(t + 1, 0, std::integral_constant<int, 2>{});
+    }
     // (two terms per sum: their order does not change the rounded result, so every wave of the
     // block holds the same S and dP)
     f32x16 sS, sP;
@@ -393,8 +403,10 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         take_partial(sP, slot0 + NH, set);
         if constexpr (NH == 2) take_partial(sP, slot0 + NH + 1, add);
       } else {
-        sP = own;
-        if constexpr (NH == 2) take_partial(sP, slot0 + NH + (h ^ 1), add);
+        if constexpr (DQ) {  // (the dV side of the dK/dV pass needs S only)
+          sP = own;
+          if constexpr (NH == 2) take_partial(sP, slot0 + NH + (h ^ 1), add);
+        }
         take_partial(sS, slot0, set);
         if constexpr (NH == 2) take_partial(sS, slot0 + 1, add);
       }
@@ -403,62 +415,88 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     // ---- probabilities and the logits' gradient of the lane's 16 elements
     // the accumulation product's B operand: dS, or for dV (role B of the dK/dV pass) the dropped-out P
     const bool use_p = !DQ && role == 1;
+    // tiles with every element in range and visible and no mask skip the per-element tests (no row
+    // can then have LSE = -inf)
+    const bool inner = !has_mask && t0 + 32 <= NT && s0 + 32 <= NS &&
+                       (!a.causal || (DQ ? t0 + 31 <= s0 + coff : s0 + 31 <= t0 + coff));
+    const float sl2 = scale * kLog2e;
     uint32_t gw2[8];  // the operand's 16 values, two per dword
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 lse4, dl4, kw4;
-      if constexpr (!DQ) {
-        const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
-        lse4 = lds_read_f4_async<0>(ra);
-        dl4 = lds_read_f4_async<256>(ra);
-        kw4 = lds_read_f4_async<0>(ra + 512 + (uint32_t)(rg * 128));
-        bwd_lds_wait3(lse4, dl4, kw4);
-      }
-      float gv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * g + e;
-        const int ti = t0 + 8 * g + 4 * hi + e;
-        const int row = DQ ? s : ti, key = DQ ? ti : s;
-        const float lse = DQ ? lse_s : lse4[e];
-        const float dl = DQ ? dl_s : dl4[e];
-        const bool valid = row < a.Nq && key < a.Nkv && (!a.causal || key <= row + coff) && lse != kNegInf;
-        float x = sS[i] * scale;
-        if (has_mask) {
-          const int64_t off = mask_b + (int64_t)(DQ ? hq : qh) * a.msh + (int64_t)(row < a.Nq ? row : a.Nq - 1) * a.msq +
-                              (key < a.Nkv ? key : a.Nkv - 1);
-          x += bwd_bias(a.mask, a.mask_kind, off);
+    // rows 8g + 4 (l / 32) + 0..3 of the tile (elements 4g .. 4g + 3)
+    auto elem_group = [&](auto g_c, auto inner_c) {
+      constexpr int g = decltype(g_c)::value;
+      constexpr bool INNER = decltype(inner_c)::value;
+      {
+        f32x4 lse4, dl4, kw4;
+        if constexpr (!DQ) {
+          const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
+          lse4 = lds_read_f4_async<0>(ra);
+          dl4 = lds_read_f4_async<256>(ra);
+          kw4 = lds_read_f4_async<0>(ra + 512 + (uint32_t)(rg * 128));
+          bwd_lds_wait3(lse4, dl4, kw4);
         }
-        const float p = valid ? exp2f((x - lse) * kLog2e) : 0.f;
-        float m = 1.f;
-        if (has_drop) {
-          const uint32_t w = DQ ? kw : (uint32_t)__float_as_uint(kw4[e]);
-          const int bit = DQ ? (8 * g + 4 * hi + e) : (key & 31);
-          m = ((w >> bit) & 1u) ? a.drop_scale : 0.f;
-        }
-        const float ds = p * (sP[i] * m - dl);
-        gv[e] = use_p ? p * m : ds;
-        if constexpr (DQ) {
-          if (a.dmask != nullptr && gw == 0 && row < a.Nq && key < a.Nkv) {
-            const int64_t di = (((int64_t)(a.dm_bb ? 0 : b) * a.dm_hm + (a.dm_bh ? 0 : hq)) * a.dm_nqm +
-                                (a.dm_bq ? 0 : row)) * a.Nkv + key;
-            if (a.dm_atomic) atomicAdd(a.dmask + di, ds);
-            else a.dmask[di] = ds;
+        float gv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const int ti = t0 + 8 * g + 4 * hi + e;
+          const int row = DQ ? s : ti, key = DQ ? ti : s;
+          const float lse = DQ ? lse_s : lse4[e];
+          const float dl = DQ ? dl_s : dl4[e];
+          float p;
+          if constexpr (INNER) {
+            p = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[i], sl2, -lse * kLog2e));
+          } else {
+            const bool valid = row < a.Nq && key < a.Nkv && (!a.causal || key <= row + coff) && lse != kNegInf;
+            float x = sS[i] * scale;
+            if (has_mask) {
+              const int64_t off = mask_b + (int64_t)(DQ ? hq : qh) * a.msh +
+                                  (int64_t)(row < a.Nq ? row : a.Nq - 1) * a.msq + (key < a.Nkv ? key : a.Nkv - 1);
+              x += bwd_bias(a.mask, a.mask_kind, off);
+            }
+            // exp2 of -inf is 0
+            p = valid ? __builtin_amdgcn_exp2f((x - lse) * kLog2e) : 0.f;
+          }
+          float m = 1.f;
+          if (has_drop) {
+            const uint32_t w = DQ ? kw : (uint32_t)__float_as_uint(kw4[e]);
+            const int bit = DQ ? (8 * g + 4 * hi + e) : (key & 31);
+            m = ((w >> bit) & 1u) ? a.drop_scale : 0.f;
+          }
+          if (use_p) {
+            gv[e] = p * m;
+          } else {
+            const float ds = p * (sP[i] * m - dl);
+            gv[e] = ds;
+            if constexpr (DQ) {
+              if (a.dmask != nullptr && gw == 0 && row < a.Nq && key < a.Nkv) {
+                const int64_t di = (((int64_t)(a.dm_bb ? 0 : b) * a.dm_hm + (a.dm_bh ? 0 : hq)) * a.dm_nqm +
+                                    (a.dm_bq ? 0 : row)) * a.Nkv + key;
+                if (a.dm_atomic) atomicAdd(a.dmask + di, ds);
+                else a.dmask[di] = ds;
+              }
+            }
           }
         }
+        gw2[2 * g] = pack2<T>(gv[0], gv[1]);
+        gw2[2 * g + 1] = pack2<T>(gv[2], gv[3]);
       }
-      gw2[2 * g] = pack2<T>(gv[0], gv[1]);
-      gw2[2 * g + 1] = pack2<T>(gv[2], gv[3]);
-    }
+    };
+    auto run_group = [&](auto g_c) {
+      if (inner) elem_group(g_c, std::true_type{});
+      else elem_group(g_c, std::false_type{});
+    };
+    run_group(std::integral_constant<int, 0>{});
+    run_group(std::integral_constant<int, 1>{});
     const i32x4 g0 = i32x4{(int)gw2[0], (int)gw2[1], (int)gw2[2], (int)gw2[3]};
-    const i32x4 g1 = i32x4{(int)gw2[4], (int)gw2[5], (int)gw2[6], (int)gw2[7]};
+    i32x4 g1;
 
-    // ---- accumulation products: acc[cb] += (tensor^T) G over this wave's columns
+    // ---- accumulation products: acc[cb] += (tensor^T) G over this wave's columns, step 0 (rows
+    // 0-15, elements 0-7) of every block first; element groups 2 and 3 are formed in between
     constexpr int NA = NCB * 2;
     i32x2 tl[PF + 1], th[PF + 1];
     auto read_a = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = m / 2, kk = m % 2;
+      constexpr int cb = m % NCB, kk = m / NCB;
       constexpr uint32_t off = (uint32_t)(cb * 2048 + kk * 1024);
       static_assert(off < 65536, "ds offset field");
       tl[m % (PF + 1)] = lds_read_tr_async<off>(ta + boff);
@@ -469,13 +507,20 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     });
     static_for<NA>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = m / 2, kk = m % 2;
+      constexpr int cb = m % NCB, kk = m / NCB;
       if constexpr (m + PF < NA) read_a(std::integral_constant<int, m + PF>{});
       constexpr int after = 2 * ((m + PF < NA ? m + PF : NA - 1) - m);
       lgkm_wait<after>();
       if (!PAD || ac0 + 32 * cb < D) {
         const i32x4 af = i32x4{tl[m % (PF + 1)][0], tl[m % (PF + 1)][1], th[m % (PF + 1)][0], th[m % (PF + 1)][1]};
         E::mma_acc_agpr(acc[cb], af, kk == 0 ? g0 : g1);
+      }
+      // (an element group's LDS reads wait for every LDS read issued before them, so the waits of
+      // the later products stay correct)
+      if constexpr (m == (NCB >= 2 ? NCB / 2 - 1 : 0)) run_group(std::integral_constant<int, 2>{});
+      if constexpr (m == NCB - 1) {
+        run_group(std::integral_constant<int, 3>{});
+        g1 = i32x4{(int)gw2[4], (int)gw2[5], (int)gw2[6], (int)gw2[7]};
       }
     });
 
@@ -485,7 +530,8 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     if constexpr (NBUF == 1) {
       if (t + 1 < ntiles) {
         block_sync();  // every wave is done with the buffer
-        issue_tile(t + 1, 0);
+        if constexpr (DQ) issue_tile(t + 1, 0, std::integral_constant<int, 1>{});
+        else issue_tile(t + 1, 0, kAll);
       }
     }
   }
