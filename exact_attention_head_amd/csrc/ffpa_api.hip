@@ -73,8 +73,9 @@ int64_t kernel_dim(int64_t D) {
 }
 
 // Elements from a tensor's first element to one past its last: (B-1)*sb + (H-1)*sh + (N-1)*sn + D.
-int64_t extent(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t D) {
-  return (B - 1) * st[0] + (H - 1) * st[1] + (N - 1) * st[2] + D;
+// (in 128-bit arithmetic: caller strides may be as large as int64_t allows)
+__int128 extent(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64_t D) {
+  return (__int128)(B - 1) * st[0] + (__int128)(H - 1) * st[1] + (__int128)(N - 1) * st[2] + D;
 }
 
 // True when no two elements of a [B, H, N, D] tensor with strides st (and unit head-dim stride)
@@ -87,11 +88,11 @@ bool non_overlapping(const int64_t st[3], int64_t B, int64_t H, int64_t N, int64
       std::swap(dims[j][0], dims[j - 1][0]);
       std::swap(dims[j][1], dims[j - 1][1]);
     }
-  int64_t span = 0;  // elements covered by the smaller dimensions, minus one
+  __int128 span = 0;  // elements covered by the smaller dimensions, minus one
   for (int i = 0; i < 4; ++i) {
     if (dims[i][1] <= 1) continue;
     if (dims[i][0] <= span) return false;
-    span += (dims[i][1] - 1) * dims[i][0];
+    span += (__int128)(dims[i][1] - 1) * dims[i][0];
   }
   return true;
 }
@@ -151,12 +152,14 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
                 (long long)D);
   if (!fp8 && (D > 1024 || kernel_dim(D) == 0))
     return fail(FFPA_ERR_UNSUPPORTED, "head dim %lld: kernels cover 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
-  // grid size and 32-bit in-kernel indexing
+  // 32-bit in-kernel indexing, then the grid size (each factor bounded first, so that no product
+  // below overflows)
+  if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B > (1LL << 30) || Hq > (1LL << 30) || B * Hq > (1LL << 30) ||
+      B * Hkv > (1LL << 30))
+    return fail(FFPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit row indexing of the kernels");
   const int br = fp8 ? (D <= 512 ? 128 : 64) : rows_for(kernel_dim(D));
   const int64_t nqt = (Nq + br - 1) / br;
   if (B * Hq * nqt > 0x7fffffffLL) return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
-  if (Nq > (1LL << 30) || Nkv > (1LL << 30) || B * Hq > (1LL << 30) || B * Hkv > (1LL << 30))
-    return fail(FFPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit row indexing of the kernels");
   if (Nq * D * 2 >= (1LL << 31) || Nkv * D * 2 >= (1LL << 31))
     return fail(FFPA_ERR_UNSUPPORTED, "one head of Q or K/V must stay below 2 GiB (buffer addressing)");
   if (lay != nullptr) {
@@ -168,10 +171,14 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
   size_t qbytes = (size_t)(B * Hq * Nq * D) * esz, kbytes = (size_t)(B * Hkv * Nkv * D) * esz;
   size_t vbytes = kbytes, obytes = (size_t)(B * Hq * Nq * D) * 2;
   if (lay != nullptr) {
-    qbytes = (size_t)extent(lay->q, B, Hq, Nq, D) * esz;
-    kbytes = (size_t)extent(lay->k, B, Hkv, Nkv, D) * esz;
-    vbytes = (size_t)extent(lay->v, B, Hkv, Nkv, D) * esz;
-    obytes = (size_t)extent(lay->o, B, Hq, Nq, D) * esz;
+    const __int128 eq = extent(lay->q, B, Hq, Nq, D), ek = extent(lay->k, B, Hkv, Nkv, D),
+                   ev = extent(lay->v, B, Hkv, Nkv, D), eo = extent(lay->o, B, Hq, Nq, D);
+    const __int128 lim = (__int128)1 << 60;  // no tensor spans an exabyte
+    if (eq > lim || ek > lim || ev > lim || eo > lim) return fail(FFPA_ERR_UNSUPPORTED, "strides too large");
+    qbytes = (size_t)eq * esz;
+    kbytes = (size_t)ek * esz;
+    vbytes = (size_t)ev * esz;
+    obytes = (size_t)eo * esz;
   }
   const size_t lbytes = lse ? (size_t)(B * Hq * Nq) * 4 : 0;
   if (ranges_overlap(o, obytes, q, qbytes) || ranges_overlap(o, obytes, k, kbytes) ||
@@ -191,8 +198,9 @@ int check(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, 
       if (mask->stride_b < 0 || mask->stride_h < 0 || mask->stride_q < 0)
         return fail(FFPA_ERR_VALUE, "mask strides must be >= 0");
       if ((uintptr_t)mask->data % msz) return fail(FFPA_ERR_VALUE, "mask data misaligned for its element type");
-      const int64_t last = (B - 1) * mask->stride_b + (Hq - 1) * mask->stride_h + (Nq - 1) * mask->stride_q + Nkv;
-      if (last > (1LL << 62) / (int64_t)msz) return fail(FFPA_ERR_UNSUPPORTED, "mask too large");
+      const __int128 last = (__int128)(B - 1) * mask->stride_b + (__int128)(Hq - 1) * mask->stride_h +
+                            (__int128)(Nq - 1) * mask->stride_q + Nkv;
+      if (last > ((__int128)1 << 62) / (int64_t)msz) return fail(FFPA_ERR_UNSUPPORTED, "mask too large");
       const size_t mbytes = (size_t)last * msz;
       if (ranges_overlap(o, obytes, mask->data, mbytes) || ranges_overlap(lse, lbytes, mask->data, mbytes))
         return fail(FFPA_ERR_VALUE, "o and lse must not overlap the mask");

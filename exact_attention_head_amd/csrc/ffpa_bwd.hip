@@ -92,8 +92,10 @@ int bwd_check(const void* q, const void* k, const void* v, const void* o, const 
   if ((uintptr_t)lse & 3) return bfail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
   if (D < 64 || D > 1024 || D % 64 != 0)
     return bfail(FFPA_ERR_UNSUPPORTED, "head dim %lld: 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
-  // 32-bit row indexing and buffer offsets of one head (rows up to 64 past its end included)
-  if ((Nq + 64) * D >= (1LL << 31) || (Nkv + 64) * D >= (1LL << 31) || B * Hq >= (1LL << 31))
+  // 32-bit row indexing and buffer offsets of one head (rows up to 64 past its end included); each
+  // factor bounded first, so that no product overflows
+  if (Nq >= (1LL << 31) || Nkv >= (1LL << 31) || B >= (1LL << 31) || Hq >= (1LL << 31) ||
+      (Nq + 64) * D >= (1LL << 31) || (Nkv + 64) * D >= (1LL << 31) || B * Hq >= (1LL << 31))
     return bfail(FFPA_ERR_UNSUPPORTED, "sizes beyond the backward's indexing");
   if (mask != nullptr && mask->kind != FFPA_MASK_NONE) {
     if (mask->kind < FFPA_MASK_BOOL_U8 || mask->kind > FFPA_MASK_ADD_FP16)
@@ -112,6 +114,7 @@ extern "C" {
 
 size_t ffpa_bwd_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nkv < 1 || D < 1 || Hq % Hkv != 0) return 0;
+  if (B >= (1LL << 31) || Hq >= (1LL << 31) || Nq >= (1LL << 31) || B * Hq >= (1LL << 31)) return 0;
   return align256((size_t)(B * Hq * Nq) * 4);  // Delta
 }
 
