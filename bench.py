@@ -334,7 +334,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_d_self",
                     help="tiny | large_d_self | gqa_causal | cross_mask | sweep:<D>[:fp16] | varlen_causal | "
-                         "fp8:<one of those> (the fp8 forward on the workload quantised per head)")
+                         "fp8:<one of those> (the fp8 forward on the workload quantised per head) | "
+                         "bwd:<a dense one> (the backward alone)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -368,9 +369,24 @@ def main() -> int:
         return getattr(W, name)()
 
     fp8_main = args.workload.startswith("fp8:")
-    w = pick(args.workload[4:] if fp8_main else args.workload)
+    bwd_main = args.workload.startswith("bwd:")
+    w = pick(args.workload[4:] if fp8_main or bwd_main else args.workload)
     log(f"workload {'fp8 ' if fp8_main else ''}{w.name}: warmup {args.warmup}, steps {args.steps}")
     packed = isinstance(w, W.VarlenWorkload)
+    if bwd_main:
+        # the backward alone (profiling runs): one JSON line, five products' FLOPs against the peak
+        st = time_backward(w, args.steps, args.warmup)
+        tf = 2.5 * w.flops / (st["median_ms"] * 1e-3) / 1e12
+        log(f"backward {w.name}: median {st['median_ms']:.4f} ms/call, {tf:.1f} TFLOPS "
+            f"({100 * tf / PEAK_TFLOPS:.1f}% of peak)")
+        print(json.dumps({"metric": "backward TFLOPS", "value": round(tf, 2), "unit": "TFLOPS", "n_gpus": 1,
+                          "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(st["median_ms"], 5),
+                          "higher_is_better": True, "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp16",
+                          "data": "synthetic", "config": w.describe(),
+                          "roofline": dict(bound="mfma", achieved=round(tf, 2), peak=PEAK_TFLOPS, unit="TFLOP/s",
+                                           frac=round(tf / PEAK_TFLOPS, 4),
+                                           kernel="ffpa_bwd_kernel (dK/dV pass + dQ pass)")}), flush=True)
+        return 0
     if fp8_main:
         # the fp8 forward alone (profiling runs): one JSON line against the fp8 peak, no CPU leg
         st = time_fp8(w, args.steps, args.warmup, clock=True)
