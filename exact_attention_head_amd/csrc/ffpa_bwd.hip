@@ -90,8 +90,8 @@ int bwd_check(const void* q, const void* k, const void* v, const void* o, const 
        (uintptr_t)dv) & 15)
     return bfail(FFPA_ERR_VALUE, "tensors must be 16-byte aligned");
   if ((uintptr_t)lse & 3) return bfail(FFPA_ERR_VALUE, "lse must be 4-byte aligned");
-  if (D < 64 || D > 1024 || D % 64 != 0)
-    return bfail(FFPA_ERR_UNSUPPORTED, "head dim %lld: 64 <= D <= 1024 with D %% 64 == 0", (long long)D);
+  if (D < 8 || D > 1024 || D % 8 != 0)
+    return bfail(FFPA_ERR_UNSUPPORTED, "head dim %lld: 8 <= D <= 1024 with D %% 8 == 0", (long long)D);
   // 32-bit row indexing and buffer offsets of one head (rows up to 64 past its end included); each
   // factor bounded first, so that no product overflows
   if (Nq >= (1LL << 31) || Nkv >= (1LL << 31) || B >= (1LL << 31) || Hq >= (1LL << 31) ||
@@ -125,14 +125,11 @@ namespace {
 template <typename T>
 hipError_t launch_fused(int kd, bool pad, const ffpa::BwdArgs& a, hipStream_t s) {
   switch (kd) {
-#define FFPA_BWD_CASE(KDv) \
-  case KDv: return ffpa::launch_bwd_fused<T, KDv, false>(a, s);
 #define FFPA_BWD_CASE_PAD(KDv) \
   case KDv: return pad ? ffpa::launch_bwd_fused<T, KDv, true>(a, s) : ffpa::launch_bwd_fused<T, KDv, false>(a, s);
-    FFPA_BWD_CASE(64) FFPA_BWD_CASE(128) FFPA_BWD_CASE(192) FFPA_BWD_CASE(256) FFPA_BWD_CASE(320)
-    FFPA_BWD_CASE(384) FFPA_BWD_CASE(448) FFPA_BWD_CASE(512)
+    FFPA_BWD_CASE_PAD(64) FFPA_BWD_CASE_PAD(128) FFPA_BWD_CASE_PAD(192) FFPA_BWD_CASE_PAD(256)
+    FFPA_BWD_CASE_PAD(320) FFPA_BWD_CASE_PAD(384) FFPA_BWD_CASE_PAD(448) FFPA_BWD_CASE_PAD(512)
     FFPA_BWD_CASE_PAD(640) FFPA_BWD_CASE_PAD(768) FFPA_BWD_CASE_PAD(896) FFPA_BWD_CASE_PAD(1024)
-#undef FFPA_BWD_CASE
 #undef FFPA_BWD_CASE_PAD
     default: return hipErrorInvalidValue;
   }

@@ -20,9 +20,11 @@
 // whose partial tiles are summed).  The finished tiles are exchanged through LDS, so that every
 // wave of the block holds S and dP and forms P and dS itself.  Then the dQ pass splits dQ's
 // columns among the block's waves; in the dK/dV pass role A accumulates dK and role B dV.  A wave
-// thus keeps one stationary operand (at most 128 VGPRs) and at most 256 accumulators.  Head dims
-// whose columns do not split into 32-column blocks this way run the next such kernel head dim with
-// the columns past D skipped.
+// thus keeps one stationary operand (at most 128 VGPRs) and at most 256 accumulators.  Other head
+// dims (multiples of 8) run the next kernel head dim: the stationary columns past D load as zero, the
+// products of 32-column blocks wholly past D are skipped, and outputs past D are not stored.  The
+// streamed tiles' last partial block holds the next row's (finite) values past D, which meet only
+// zero operands or accumulator columns that are never stored.
 //
 // Products (v_mfma_f32_32x32x16, inline assembly as in the forward): a score tile is
 // (streamed x stationary), so lane l holds stationary index l % 32 and accumulator element i holds
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     xrow = xb + (int64_t)sc * D + sc0 + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < NKR; ++kk) {
-      const bool in = !PAD || sc0 + 16 * kk < D;
+      const bool in = !PAD || sc0 + 16 * kk + 8 * hi < D;
       xf[kk] = in ? *(const i32x4*)(xrow + 16 * kk) : i32x4{0, 0, 0, 0};
     }
     vm_wait<0>();
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       asm volatile("" : "+v"(xr));
 #pragma unroll
       for (int kk = NKR; kk < NKS; ++kk) {
-        const bool in = !PAD || sc0 + 16 * kk < D;
+        const bool in = !PAD || sc0 + 16 * kk + 8 * hi < D;
         xf[kk] = in ? *(const i32x4*)(xr + 16 * kk) : i32x4{0, 0, 0, 0};
       }
     }
@@ -549,6 +551,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = ac0 + 32 * cb + 8 * g + 4 * hi;
+        if (PAD && col >= D) continue;
         const uint32_t w0 = pack2<T>(acc[cb][4 * g] * f, acc[cb][4 * g + 1] * f);
         const uint32_t w1 = pack2<T>(acc[cb][4 * g + 2] * f, acc[cb][4 * g + 3] * f);
         *(i32x2*)(out + (int64_t)s * D + col) = i32x2{(int)w0, (int)w1};

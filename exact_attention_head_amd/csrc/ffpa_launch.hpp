@@ -71,17 +71,17 @@ struct BwdArgs {
   int causal;
 };
 
-// The kernel head dim serving head dim D (D % 64 == 0): D itself where its columns split into
-// 32-column blocks per wave, else the next one that does (576 -> 640, 704 -> 768, 832 -> 896,
-// 960 -> 1024).
+// The kernel head dim serving head dim D (D % 8 == 0): the smallest of 64, 128, ..., 512, 640, 768,
+// 896, 1024 that is at least D (a multiple of 64 up to 512 is its own; 576 -> 640, 704 -> 768,
+// 832 -> 896, 960 -> 1024).
 constexpr int bwd_kernel_dim(int D) {
-  return D <= 512 ? D : (D <= 640 ? 640 : (D <= 768 ? 768 : (D <= 896 ? 896 : 1024)));
+  return D <= 512 ? (D + 63) / 64 * 64 : (D <= 640 ? 640 : (D <= 768 ? 768 : (D <= 896 ? 896 : 1024)));
 }
 
 template <typename T, int KD, bool PAD>
 hipError_t launch_bwd_fused(const BwdArgs& a, hipStream_t stream);
 #define FFPA_BWD_FOR_EACH_KD(X) X(64) X(128) X(192) X(256) X(320) X(384) X(448) X(512) X(640) X(768) X(896) X(1024)
-#define FFPA_BWD_PAD_KD(X) X(640) X(768) X(896) X(1024)
+#define FFPA_BWD_PAD_KD(X) X(64) X(128) X(192) X(256) X(320) X(384) X(448) X(512) X(640) X(768) X(896) X(1024)
 #define FFPA_BWD_DECLARE(KDv)                                                             \
   extern template hipError_t launch_bwd_fused<Bf16, KDv, false>(const BwdArgs&, hipStream_t); \
   extern template hipError_t launch_bwd_fused<Fp16, KDv, false>(const BwdArgs&, hipStream_t);

@@ -210,8 +210,10 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
  * Three kernels on `stream`: Delta; a KV-stationary pass forming dK and dV
  * (each workgroup loops over the query rows of every head of its KV group);
  * a Q-stationary pass forming dQ.  Both passes recompute P from q, k, the
- * mask and the LSE, so no score matrix is stored.  Head dims: 64 <= D <=
- * 1024 with D % 64 == 0.  Products take bf16/fp16 operands (P and dS rounded
+ * mask and the LSE, so no score matrix is stored.  Head dims: 8 <= D <=
+ * 1024 with D % 8 == 0 (as for the forward, kernels exist for multiples of
+ * 64 and other head dims run the next one up; the inputs must then hold
+ * finite values).  Products take bf16/fp16 operands (P and dS rounded
  * once to the input type) with fp32 accumulation.  Errors as for ffpa_fwd;
  * FFPA_ERR_VALUE also for a missing or short workspace.
  */

@@ -105,7 +105,7 @@ int main() {
 
   // backward (host checks only: invalid arguments return before any HIP call)
   void *dq = (void*)P(10), *dk = (void*)P(11), *dv = (void*)P(12), *ws = (void*)P(13);
-  EXPECT(ffpa_bwd(q, k, v, o, o, lse, nullptr, dq, dk, dv, 1, 2, 1, 100, 130, 96, nan, 0, FFPA_BF16, ws, 1 << 20,
+  EXPECT(ffpa_bwd(q, k, v, o, o, lse, nullptr, dq, dk, dv, 1, 2, 1, 100, 130, 100, nan, 0, FFPA_BF16, ws, 1 << 20,
                   nullptr), FFPA_ERR_UNSUPPORTED);
   EXPECT(ffpa_bwd(q, k, v, o, o, lse, nullptr, dq, dk, dv, 1, 2, 1, 100, 130, 512, nan, 0, FFPA_BF16, ws, 16, nullptr),
          FFPA_ERR_VALUE);

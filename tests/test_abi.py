@@ -383,7 +383,7 @@ def bwd(D=512, Nq=100, Nkv=130, B=1, Hq=2, Hkv=1, causal=False, ws=M, nbytes=1 <
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=96), ffpa.ERR_UNSUPPORTED), (dict(D=1088), ffpa.ERR_UNSUPPORTED), (dict(D=32), ffpa.ERR_UNSUPPORTED),
+    (dict(D=100), ffpa.ERR_UNSUPPORTED), (dict(D=1088), ffpa.ERR_UNSUPPORTED), (dict(D=4), ffpa.ERR_UNSUPPORTED),
     (dict(Hq=3, Hkv=2), ffpa.ERR_VALUE), (dict(causal=True, Nq=200, Nkv=100), ffpa.ERR_VALUE),
     (dict(Nq=(1 << 31) // 512), ffpa.ERR_UNSUPPORTED), (dict(ws=None), ffpa.ERR_VALUE),
     (dict(nbytes=16), ffpa.ERR_VALUE), (dict(ws=M + 16), ffpa.ERR_VALUE)])

@@ -63,6 +63,21 @@ def test_backward_head_dims(D):
     _log(f"D={D}", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
 
 
+# head dims that are multiples of 8 but not of 64: the next kernel head dim, columns past D skipped
+@pytest.mark.parametrize("D", [8, 40, 72, 80, 96, 120, 136, 200, 264, 328, 456, 520, 600, 712, 776, 840, 1000, 1016])
+def test_backward_head_dims_by_8(D):
+    q, k, v, do = _case(1, 2, 1, 97, 150, D, seed=D + 7)
+    _log(f"D={D}", _compare(_grads_gpu(q, k, v, do), q, k, v, do))
+
+
+@pytest.mark.parametrize("D", [24, 248, 968])
+def test_backward_head_dims_by_8_causal_mask(D):
+    q, k, v, do = _case(2, 4, 2, 70, 133, D, seed=D + 9)
+    mask = torch.randn(2, 1, 70, 133, generator=torch.Generator().manual_seed(D))
+    _log(f"D={D} causal+mask", _compare(_grads_gpu(q, k, v, do, mask=mask, is_causal=True), q, k, v, do, mask=mask,
+                                        is_causal=True))
+
+
 @pytest.mark.parametrize("D", [128, 576, 1024])
 def test_backward_fp16_head_dims(D):
     q, k, v, do = _case(2, 2, 1, 97, 161, D, dtype=torch.float16, seed=D + 1)
