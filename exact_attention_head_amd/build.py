@@ -24,7 +24,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 
 def _dims(macro: str) -> list[int]:
-    with open(os.path.join(CSRC, "ffpa_launch.hpp")) as f:
+    src = "ffpa_bwd_launch.hpp" if macro.startswith("FFPA_BWD") else "ffpa_launch.hpp"
+    with open(os.path.join(CSRC, src)) as f:
         txt = f.read()
     body = txt[txt.index(f"#define {macro}(X)"):]
     one_line = macro != "FFPA_FOR_EACH_D"  # the others are one-line macros

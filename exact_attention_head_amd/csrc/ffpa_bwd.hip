@@ -20,7 +20,7 @@
 #include <mutex>
 
 #include "../../include/ffpa.h"
-#include "ffpa_launch.hpp"
+#include "ffpa_bwd_launch.hpp"
 
 namespace ffpa {
 // the thread's error detail (ffpa_last_error_detail), kept by the C-ABI object

@@ -43,7 +43,7 @@
 
 #include <type_traits>
 
-#include "ffpa_launch.hpp"
+#include "ffpa_bwd_launch.hpp"
 
 namespace ffpa {
 
