@@ -166,15 +166,18 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const int col0 = dg * DW;
   clock_stamp(a.stamps, 0);
 
-  // ---- work item (b, hq, q tile), XCD-contiguous, heaviest causal tiles first
+  // ---- work item (b, KV head, q tile, query head), XCD-contiguous, heaviest causal tiles first
   const int nqt = (a.Nq + BR - 1) / BR;
   const int total = a.B * a.Hq * nqt;
   int id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  int qt = id % nqt;
-  const int bh = id / nqt;
-  const int hq = bh % a.Hq;
-  const int b = bh / a.Hq;
+  // the query heads of a KV group fastest: they take the same query tile together and stream the
+  // same K/V tiles at the same time
+  const int g = id % a.group, rest = id / a.group;
+  int qt = rest % nqt;
+  const int bk = rest / nqt, hkv = a.Hkv;
+  const int b = bk / hkv;
+  const int hq = (bk % hkv) * a.group + g;
   if (a.causal) qt = nqt - 1 - qt;
   const int hk = hq / a.group;
   const int r0 = qt * BR;

@@ -724,10 +724,20 @@ __global__ __launch_bounds__(256) void ffpa_fwd_kernel(FwdArgs a) {
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
   // packed: head-major order, so that each XCD's share holds whole heads over every sequence (the
   // sequences' lengths differ; the heads' work does not)
-  int qt = id % nqt;
-  const int bh = id / nqt;
-  const int hq = packed ? bh / a.B : bh % a.Hq;
-  const int b = packed ? bh % a.B : bh / a.Hq;
+  // dense: the query heads of a KV group fastest (they then stream the same K/V tiles together)
+  int qt, hq, b;
+  if (packed) {
+    qt = id % nqt;
+    const int bh = id / nqt;
+    hq = bh / a.B;
+    b = bh % a.B;
+  } else {
+    const int g = id % a.group, rest = id / a.group;
+    qt = rest % nqt;
+    const int bk = rest / nqt, hkv = a.Hkv;
+    b = bk / hkv;
+    hq = (bk % hkv) * a.group + g;
+  }
   if (a.causal) qt = nqt - 1 - qt;  // longest tiles of a head first
   const int hk = hq / a.group;
   const int r0 = qt * BR;              // first query row of the workgroup

@@ -326,12 +326,28 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
   // packed: head-major order, so that each XCD's share holds whole heads over every sequence (the
   // sequences' lengths differ; the heads' work does not)
-  int qt = id % nqt;
-  const int bh = id / nqt;
+  // dense: items (b, KV head, q tile, query head of the group) with the group's query heads
+  // fastest, so that the G heads sharing a KV head take the same query tile together and stream the
+  // same K/V tiles at the same time (one copy in L2)
+  int qt, hq, b;
   const bool head_major = VL && a.cu_q != nullptr;
-  const int hq = head_major ? bh / a.B : bh % a.Hq;
-  const int b = head_major ? bh % a.B : bh / a.Hq;
+  if (head_major) {
+    qt = id % nqt;
+    const int bh = id / nqt;
+    hq = bh / a.B;
+    b = bh % a.B;
+  } else {
+    const int g = id % a.group, rest = id / a.group;
+    qt = rest % nqt;
+    const int bk = rest / nqt, hkv = a.Hkv;
+    b = bk / hkv;
+    hq = (bk % hkv) * a.group + g;
+  }
   if (a.causal) qt = nqt - 1 - qt;  // heaviest tiles first
+  // wave-uniform: kept in SGPRs (the divisions above run on the vector unit)
+  qt = __builtin_amdgcn_readfirstlane(qt);
+  hq = __builtin_amdgcn_readfirstlane(hq);
+  b = __builtin_amdgcn_readfirstlane(b);
   const int hk = hq / a.group;
   const int r0 = qt * BR;
   int Nq = a.Nq, Nkv = a.Nkv;
