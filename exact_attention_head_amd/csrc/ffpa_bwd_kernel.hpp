@@ -140,10 +140,24 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     const int per = nblk / 8;
     if (blk < per * 8) blk = (blk % 8) * per + blk / 8;
   }
-  const int head = blk / nsb, sb = blk % nsb;
-  const int b = DQ ? head / a.Hq : head / a.Hkv;
-  const int hq = DQ ? head % a.Hq : 0;
-  const int hkv = DQ ? hq / G : head % a.Hkv;
+  // dQ pass: blocks (b, KV head, row block, query head of the group) with the group's query heads
+  // fastest, so that the G heads sharing K/V stream the same K/V tiles together (one L2 copy);
+  // dK/dV pass: blocks (b, KV head, key block)
+  int b, hq, hkv, sb;
+  if constexpr (DQ) {
+    const int g = blk % G, rest = blk / G;
+    sb = rest % nsb;
+    const int bk = rest / nsb;
+    b = bk / a.Hkv;
+    hkv = bk % a.Hkv;
+    hq = hkv * G + g;
+  } else {
+    const int head = blk / nsb;
+    sb = blk % nsb;
+    b = head / a.Hkv;
+    hq = 0;
+    hkv = head % a.Hkv;
+  }
   const int s0wg = sb * 32 * RG;
   const int s0 = s0wg + rg * 32;  // this wave's stationary block
   const int coff = a.Nkv - a.Nq;  // causal: key k is visible from row r when k <= r + coff
