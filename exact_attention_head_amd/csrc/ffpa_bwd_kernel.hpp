@@ -77,10 +77,12 @@ __device__ inline float bwd_bias(const void* m, int kind, int64_t off) {
   }
 }
 
-// Completes this wave's LDS reads; the tied operands keep every use of the values after it.
-__device__ inline void bwd_lds_wait(f32x4 (&x)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])::"memory");
+// Marks the values as written here, after a wait that completed the LDS reads filling them: every
+// use of them then stays behind that wait.
+__device__ inline void bwd_tie(f32x4 (&x)[4]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
 }
+// Completes this wave's LDS reads; the tied operands keep every use of the values after it.
 __device__ inline void bwd_lds_wait3(f32x4& x, f32x4& y, f32x4& z) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(x), "+v"(y), "+v"(z)::"memory");
 }
@@ -235,8 +237,14 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
     vlane = (uint32_t)(lrow * D + (wave >> 1) * 32 + lchunk * 8) * 2u;
   }
-  // PARTS: 1 the U tile (K, or Q), 2 the W tile (V, or dO), 4 the staged rows (dK/dV pass)
-  auto issue_tile = [&](int t, int buf, auto parts_c) {
+  // A tile's loads: NLD per wave, load j the U piece (K, or Q) of block step j / 2 for even j, the W
+  // piece (V, or dO) for odd j.  prep_tile forms the two descriptors and the LDS destination and
+  // issues the staged rows (PARTS: 1 the U tile, 2 the W tile, 4 the staged rows of the dK/dV pass);
+  // issue_load then issues one load.  A tile that is not `valid` (past the last) gets descriptors of
+  // no records, so that its loads read nothing and write zeros.
+  constexpr int NLD = NBLK;
+  auto prep_tile = [&](int t, int buf, __amdgpu_buffer_rsrc_t& ru, __amdgpu_buffer_rsrc_t& rw, uint32_t& dst,
+                       auto parts_c, bool valid) {
     constexpr int PARTS = decltype(parts_c)::value;
     int t0, qh;
     tile_pos(t, t0, qh);
@@ -251,31 +259,18 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     }
     ub += (int64_t)t0 * D;
     wb += (int64_t)t0 * D;
-    const int bytes = (int)((int64_t)(NT - t0) * D * 2);  // the descriptor's 32-bit record count
-    const __amdgpu_buffer_rsrc_t ru = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)wb, (short)0, bytes, 0x00020000);
+    const int bytes = valid ? (int)((int64_t)(NT - t0) * D * 2) : 0;  // the descriptor's 32-bit record count
+    ru = __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0, bytes, 0x00020000);
+    rw = __builtin_amdgcn_make_buffer_rsrc((void*)wb, (short)0, bytes, 0x00020000);
     // LDS destinations from the 32-bit LDS address (no generic-pointer conversion); made opaque
     // here so that the compiler forms each one before its load instead of keeping them all in
     // SGPRs across the loop
-    uint32_t dst = smem_addr + (uint32_t)(buf * BUF + wave * 1024);
+    dst = smem_addr + (uint32_t)(buf * BUF + wave * 1024);
     asm volatile("" : "+s"(dst));
-    static_for<NBLK / 2>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      if (!PAD || (2 * c + (wave >> 1)) * 32 < D) {
-        // the block step goes in the scalar offset: the instruction's immediate offset would move
-        // the LDS destination as well
-        if constexpr ((PARTS & 1) != 0)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (FFPA_LDS void*)(uintptr_t)(dst + 4 * c * 1024), 16, vlane,
-                                                   128 * c, 0, 0);
-        if constexpr ((PARTS & 2) != 0)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (FFPA_LDS void*)(uintptr_t)(dst + NBLK * 2048 + 4 * c * 1024),
-                                                   16, vlane, 128 * c, 0, 0);
-      }
-    });
     if constexpr (!DQ && (PARTS & 4) != 0) {
       // the tile's rows: LSE and Delta (lane l -> row l % 32), keep words of the workgroup's keys
       // (lane l -> row l % 32, word s0wg / 32 + l / 32); rows past Nq read as zero
-      if (wave == 0) {
+      if (wave == 0 && valid) {
         const int64_t fr = (int64_t)(b * a.Hq + qh) * a.Nq + t0;
         const int nb = (a.Nq - t0) * 4;
         const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + fr), (short)0, nb, 0x00020000);
@@ -294,6 +289,27 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         }
       }
     }
+  };
+  auto issue_load = [&](const __amdgpu_buffer_rsrc_t& ru, const __amdgpu_buffer_rsrc_t& rw, uint32_t dst, auto j_c,
+                        auto parts_c) {
+    constexpr int j = decltype(j_c)::value, PARTS = decltype(parts_c)::value;
+    constexpr int c = j / 2;
+    if (!PAD || (2 * c + (wave >> 1)) * 32 < D) {
+      // the block step goes in the scalar offset: the instruction's immediate offset would move the
+      // LDS destination as well
+      if constexpr (j % 2 == 0 && (PARTS & 1) != 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ru, (FFPA_LDS void*)(uintptr_t)(dst + 4 * c * 1024), 16, vlane,
+                                                 128 * c, 0, 0);
+      if constexpr (j % 2 == 1 && (PARTS & 2) != 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (FFPA_LDS void*)(uintptr_t)(dst + NBLK * 2048 + 4 * c * 1024),
+                                                 16, vlane, 128 * c, 0, 0);
+    }
+  };
+  auto issue_tile = [&](int t, int buf, auto parts_c) {
+    __amdgpu_buffer_rsrc_t ru, rw;
+    uint32_t dst;
+    prep_tile(t, buf, ru, rw, dst, parts_c, true);
+    static_for<NLD>([&](auto j_c) { issue_load(ru, rw, dst, j_c, parts_c); });
   };
 
   // ---- per-lane LDS addresses (block offsets are immediates; buffer offsets added at run time)
@@ -315,32 +331,30 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
   // partial-tile exchange: slot per wave, 16 bytes per lane in four 1 KiB pieces
   const uint32_t ex_base = smem_addr + NBUF * BUF;
   const uint32_t ex_mine = ex_base + wave * 4096 + lane * 16;
-  // dst = (ADD ? dst : 0) + the partial tile of slot, read a quarter at a time
-  auto take_partial = [&](f32x16& dst, int slot, auto add_c) {
-    constexpr bool ADD = decltype(add_c)::value;
-    const uint32_t pa = ex_base + (uint32_t)(slot * 4096) + lane * 16;
-    f32x4 p[4];
-    p[0] = lds_read_f4_async<0>(pa);
-    p[1] = lds_read_f4_async<1024>(pa);
-    p[2] = lds_read_f4_async<2048>(pa);
-    p[3] = lds_read_f4_async<3072>(pa);
-    bwd_lds_wait(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (ADD) dst[4 * j + e] += p[j][e];
-        else dst[4 * j + e] = p[j][e];
-      }
-  };
 
   const bool has_mask = a.mask_kind != kMaskNone;
   const float scale = a.scale;
   const int64_t mask_b = (int64_t)b * a.msb;
+  // the dQ pass writes the logits' gradient into the mask gradient from one wave per block
+  const bool dm_on = DQ && a.dmask != nullptr && gw == 0;
 
   f32x16 acc[NCB];  // dQ^T, dK^T or dV^T columns of this wave
 #pragma unroll
   for (int c = 0; c < NCB; ++c) acc[c] = f32x16{};
+
+  // The tile's products run in NKS + NA slots, the score products first.  Double-buffered, the next
+  // tile's NLD loads are spread over the first LSPAN slots, load j after slot j * LSPAN / NLD: issued
+  // all at once they hold the wave at the load unit's queue for about as long as the direct-load
+  // path needs to move the tile, with no product issued meanwhile.
+  constexpr int NA = NCB * 2;
+  // fragments read PF products ahead (two where the dK/dV pass's 256 accumulators and a 512-column
+  // stationary operand leave no room for more)
+  constexpr int PF = (!DQ && KD > 896) ? 2 : 4;
+  constexpr int LSPAN = NKS;
+  // the staged rows' LSE and Delta of all four element groups are read at the start of a tile where
+  // two tiles are buffered and no column is padded (otherwise, and for the keep words, at their
+  // group's first element: the registers they would hold across the score products are not there)
+  constexpr bool HOIST = NBUF == 2 && !PAD;
 
   constexpr std::integral_constant<int, 7> kAll{};
   if (ntiles > 0) issue_tile(0, 0, kAll);
@@ -350,13 +364,41 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     tile_pos(t, t0, qh);
     vm_wait<0>();
     block_sync();  // tile t visible; every wave is done with tile t - 1 (and its buffer)
+    const uint32_t boff = (uint32_t)(buf * BUF);
     uint32_t kw = 0;
     if constexpr (DQ) {
-      // requested before the next tile's loads, so that waiting for it does not wait for those
-      if (has_drop) kw = a.keep[((int64_t)(b * a.Hq + hq) * a.Nq + sc) * a.keep_w + t];
+      // one load whether or not there is dropout (LSE's first word stands in): the compiler can then
+      // count it exactly, where a conditional load makes it wait for every load in flight
+      const uint32_t* kp = has_drop ? a.keep + ((int64_t)(b * a.Hq + hq) * a.Nq + sc) * a.keep_w + t
+                                    : (const uint32_t*)a.lse;
+      kw = *kp;
     }
-    if (NBUF == 2 && t + 1 < ntiles) issue_tile(t + 1, buf ^ 1, kAll);
-    const uint32_t boff = (uint32_t)(buf * BUF);
+    const bool more = t + 1 < ntiles;
+    // (after the last tile the loads still run, reading nothing: loads issued on every path let the
+    // compiler count exactly what a wait for an earlier load must let pass)
+    __amdgpu_buffer_rsrc_t nru, nrw;
+    uint32_t ndst = 0;
+    if constexpr (NBUF == 2) prep_tile(t + 1, buf ^ 1, nru, nrw, ndst, kAll, more);
+    // the next tile's loads that follow slot u
+    auto loads_after = [&](auto u_c) {
+      if constexpr (NBUF == 2) {
+        constexpr int u = decltype(u_c)::value;
+        static_for<NLD>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          if constexpr (j * LSPAN / NLD == u) issue_load(nru, nrw, ndst, j_c, kAll);
+        });
+      }
+    };
+    f32x4 lse4[4], dl4[4], kw4[4];
+    if constexpr (!DQ && HOIST) {
+      // (in LDS order, so the products' fragment waits below cover them)
+      const uint32_t ra = smem_addr + boff + TILE + (uint32_t)(16 * hi);
+      static_for<4>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        lse4[g] = lds_read_f4_async<32 * g>(ra);
+        dl4[g] = lds_read_f4_async<256 + 32 * g>(ra);
+      });
+    }
     if constexpr (NRL > 0) {
       // (the address is made opaque so that the loads stay inside the loop)
       const uint16_t* xr = xrow;
@@ -370,9 +412,6 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
 
     // ---- the role's score product over its columns (fragments read PF products ahead)
     f32x16 own;
-    // fragments read PF products ahead (two where the dK/dV pass's 256 accumulators and a
-    // 512-column stationary operand leave no room for more)
-    constexpr int PF = (!DQ && KD > 896) ? 2 : 4;
     i32x4 fr[PF + 1];
     auto read_s = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -388,14 +427,23 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       if constexpr (m + PF < NKS) read_s(std::integral_constant<int, m + PF>{});
       constexpr int after = (m + PF < NKS ? m + PF : NKS - 1) - m;
       lgkm_wait<after>();
+      if constexpr (m == 0 && !DQ && HOIST) {
+        // every LDS read issued before fragment 0 is complete: the staged rows are in registers
+        asm volatile("" : "+v"(lse4[0]), "+v"(lse4[1]), "+v"(lse4[2]), "+v"(lse4[3]), "+v"(dl4[0]), "+v"(dl4[1]),
+                     "+v"(dl4[2]), "+v"(dl4[3]));
+      }
       if (!PAD || sc0 + 16 * m < D) {
         if constexpr (m == 0) bwd_mma_first<T>(own, fr[m % (PF + 1)], xf[m]);
         else bwd_mma_acc<T>(own, fr[m % (PF + 1)], xf[m]);
       }
+      if constexpr (NBUF == 2) {
+        __builtin_amdgcn_sched_barrier(0);  // (the loads stay between the products)
+        loads_after(mc);
+      }
     });
     mma_guard_s(own);
 
-    // ---- exchange: S = sum over h of role A's partial tiles, dP = likewise for role B
+    // ---- exchange: S = the sum over h of role A's partial tiles, dP likewise for role B
     static_for<4>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       lds_write_b128_async<j * 1024>(ex_mine, f32x4{own[4 * j], own[4 * j + 1], own[4 * j + 2], own[4 * j + 3]});
@@ -404,60 +452,90 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     // single buffer, dQ pass: V has been read for the last time (by the dP products); its next tile
     // can be loaded while K is still needed
     if constexpr (NBUF == 1 && DQ) {
-      if (t + 1 < ntiles) issue_tile(t + 1, 0, std::integral_constant<int, 2>{});
+      if (more) issue_tile(t + 1, 0, std::integral_constant<int, 2>{});
     }
-    // (two terms per sum: their order does not change the rounded result, so every wave of the
-    // block holds the same S and dP)
+    // every wave reads the finished tiles back from the slots, in the same order (two terms per sum:
+    // their order does not change the rounded result, so every wave of the block holds the same S
+    // and dP).  (The dV side of the dK/dV pass needs S only, but reads dP as well: a read on one
+    // path only lets the compiler move its registers before the wait.)
     f32x16 sS, sP;
     {
-      const int slot0 = rg * GW;
-      const std::true_type add;
-      const std::false_type set;
-      if (role == 0) {
-        sS = own;
-        if constexpr (NH == 2) take_partial(sS, slot0 + (h ^ 1), add);
-        take_partial(sP, slot0 + NH, set);
-        if constexpr (NH == 2) take_partial(sP, slot0 + NH + 1, add);
-      } else {
-        if constexpr (DQ) {  // (the dV side of the dK/dV pass needs S only)
-          sP = own;
-          if constexpr (NH == 2) take_partial(sP, slot0 + NH + (h ^ 1), add);
+      const uint32_t pa = ex_base + (uint32_t)(rg * GW * 4096) + lane * 16;
+      // slot q's tile into x (four 1 KiB pieces)
+      auto read_slot = [&](f32x4(&x)[4], auto q_c) {
+        constexpr int q = decltype(q_c)::value;
+        x[0] = lds_read_f4_async<q * 4096 + 0>(pa);
+        x[1] = lds_read_f4_async<q * 4096 + 1024>(pa);
+        x[2] = lds_read_f4_async<q * 4096 + 2048>(pa);
+        x[3] = lds_read_f4_async<q * 4096 + 3072>(pa);
+      };
+      f32x4 xs[4], xp[4];
+      read_slot(xs, std::integral_constant<int, 0>{});
+      read_slot(xp, std::integral_constant<int, NH>{});
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      bwd_tie(xs);
+      bwd_tie(xp);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sS[4 * j + e] = xs[j][e];
+          sP[4 * j + e] = xp[j][e];
         }
-        take_partial(sS, slot0, set);
-        if constexpr (NH == 2) take_partial(sS, slot0 + 1, add);
+      if constexpr (NH == 2) {
+        // the second halves, in a second round (registers)
+        read_slot(xs, std::integral_constant<int, 1>{});
+        read_slot(xp, std::integral_constant<int, 3>{});
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        bwd_tie(xs);
+        bwd_tie(xp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sS[4 * j + e] += xs[j][e];
+            sP[4 * j + e] += xp[j][e];
+          }
       }
     }
 
-    // ---- probabilities and the logits' gradient of the lane's 16 elements
+    // ---- probabilities and the logits' gradient of the lane's 16 elements, in one of two versions
+    // picked once per tile: interior tiles without dropout (every element in range and visible, no
+    // mask: no row can then have LSE = -inf), in straight-line code, and the general version with the
+    // per-element tests.
     // the accumulation product's B operand: dS, or for dV (role B of the dK/dV pass) the dropped-out P
     const bool use_p = !DQ && role == 1;
-    // tiles with every element in range and visible and no mask skip the per-element tests (no row
-    // can then have LSE = -inf)
     const bool inner = !has_mask && t0 + 32 <= NT && s0 + 32 <= NS &&
                        (!a.causal || (DQ ? t0 + 31 <= s0 + coff : s0 + 31 <= t0 + coff));
     const float sl2 = scale * kLog2e;
-    uint32_t gw2[8];  // the operand's 16 values, two per dword
-    // rows 8g + 4 (l / 32) + 0..3 of the tile (elements 4g .. 4g + 3)
-    auto elem_group = [&](auto g_c, auto inner_c) {
-      constexpr int g = decltype(g_c)::value;
-      constexpr bool INNER = decltype(inner_c)::value;
-      {
-        f32x4 lse4, dl4, kw4;
-        if constexpr (!DQ) {
-          const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
-          lse4 = lds_read_f4_async<0>(ra);
-          dl4 = lds_read_f4_async<256>(ra);
-          kw4 = lds_read_f4_async<0>(ra + 512 + (uint32_t)(rg * 128));
-          bwd_lds_wait3(lse4, dl4, kw4);
-        }
+    // the operand of k-step kk: elements 8 kk .. 8 kk + 7, two per dword (each group packed as soon as
+    // it is complete)
+    i32x4 gk[2];
+    // MODE 0: interior, no dropout; 2: general
+    auto elements = [&](auto mode_c) {
+      constexpr int MODE = decltype(mode_c)::value;
+      constexpr bool INNER = MODE == 0;
+      static_for<4>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
         float gv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
+        if constexpr (!DQ) {
+          // the group's staged rows not read yet (waits for every LDS read issued before them)
+          const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
+          if constexpr (!HOIST) {
+            lse4[g] = lds_read_f4_async<0>(ra);
+            dl4[g] = lds_read_f4_async<256>(ra);
+          }
+          if (MODE == 2 && has_drop) kw4[g] = lds_read_f4_async<0>(ra + 512 + (uint32_t)(rg * 128));
+          if constexpr (!HOIST || MODE != 0) bwd_lds_wait3(lse4[g], dl4[g], kw4[g]);
+        }
+        // element e: row 8g + 4 (l / 32) + e of the tile (element 4g + e)
+        static_for<4>([&](auto e_c) {
+          constexpr int e = decltype(e_c)::value;
+          constexpr int i = 4 * g + e;  // the element
           const int ti = t0 + 8 * g + 4 * hi + e;
           const int row = DQ ? s : ti, key = DQ ? ti : s;
-          const float lse = DQ ? lse_s : lse4[e];
-          const float dl = DQ ? dl_s : dl4[e];
+          const float lse = DQ ? lse_s : lse4[g][e];
+          const float dl = DQ ? dl_s : dl4[g][e];
           float p;
           if constexpr (INNER) {
             p = __builtin_amdgcn_exp2f(__builtin_fmaf(sS[i], sl2, -lse * kLog2e));
@@ -472,43 +550,45 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
             // exp2 of -inf is 0
             p = valid ? __builtin_amdgcn_exp2f((x - lse) * kLog2e) : 0.f;
           }
-          float m = 1.f;
-          if (has_drop) {
-            const uint32_t w = DQ ? kw : (uint32_t)__float_as_uint(kw4[e]);
-            const int bit = DQ ? (8 * g + 4 * hi + e) : (key & 31);
-            m = ((w >> bit) & 1u) ? a.drop_scale : 0.f;
-          }
-          if (use_p) {
-            gv[e] = p * m;
+          if constexpr (MODE == 0) {
+            gv[e] = use_p ? p : p * (sP[i] - dl);
           } else {
-            const float ds = p * (sP[i] * m - dl);
-            gv[e] = ds;
-            if constexpr (DQ) {
-              if (a.dmask != nullptr && gw == 0 && row < a.Nq && key < a.Nkv) {
+            float m = 1.f;
+            if (has_drop) {
+              const uint32_t w = DQ ? kw : (uint32_t)__float_as_uint(kw4[g][e]);
+              const int bit = DQ ? (8 * g + 4 * hi + e) : (key & 31);
+              m = ((w >> bit) & 1u) ? a.drop_scale : 0.f;
+            }
+            gv[e] = use_p ? p * m : p * (sP[i] * m - dl);
+          }
+        });
+        gk[g / 2][2 * (g % 2)] = (int)pack2<T>(gv[0], gv[1]);
+        gk[g / 2][2 * (g % 2) + 1] = (int)pack2<T>(gv[2], gv[3]);
+        // the dQ pass stores the mask gradient (a requested one implies a mask, so only the general
+        // version does)
+        if constexpr (DQ && !INNER) {
+          if (dm_on) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = t0 + 8 * g + 4 * hi + e;
+              if (s < a.Nq && key < a.Nkv) {
                 const int64_t di = (((int64_t)(a.dm_bb ? 0 : b) * a.dm_hm + (a.dm_bh ? 0 : hq)) * a.dm_nqm +
-                                    (a.dm_bq ? 0 : row)) * a.Nkv + key;
-                if (a.dm_atomic) atomicAdd(a.dmask + di, ds);
-                else a.dmask[di] = ds;
+                                    (a.dm_bq ? 0 : s)) * a.Nkv + key;
+                if (a.dm_atomic) atomicAdd(a.dmask + di, gv[e]);
+                else a.dmask[di] = gv[e];
               }
             }
           }
         }
-        gw2[2 * g] = pack2<T>(gv[0], gv[1]);
-        gw2[2 * g + 1] = pack2<T>(gv[2], gv[3]);
-      }
+      });
     };
-    auto run_group = [&](auto g_c) {
-      if (inner) elem_group(g_c, std::true_type{});
-      else elem_group(g_c, std::false_type{});
-    };
-    run_group(std::integral_constant<int, 0>{});
-    run_group(std::integral_constant<int, 1>{});
-    const i32x4 g0 = i32x4{(int)gw2[0], (int)gw2[1], (int)gw2[2], (int)gw2[3]};
-    i32x4 g1;
+    // (padded head dims take the general version on every tile: the interior one would cost the
+    // padded dK/dV pass at 512 columns registers it does not have)
+    if (!PAD && inner && !has_drop) elements(std::integral_constant<int, 0>{});
+    else elements(std::integral_constant<int, 2>{});
 
     // ---- accumulation products: acc[cb] += (tensor^T) G over this wave's columns, step 0 (rows
-    // 0-15, elements 0-7) of every block first; element groups 2 and 3 are formed in between
-    constexpr int NA = NCB * 2;
+    // 0-15) of every block first
     i32x2 tl[PF + 1], th[PF + 1];
     auto read_a = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
@@ -529,14 +609,11 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       lgkm_wait<after>();
       if (!PAD || ac0 + 32 * cb < D) {
         const i32x4 af = i32x4{tl[m % (PF + 1)][0], tl[m % (PF + 1)][1], th[m % (PF + 1)][0], th[m % (PF + 1)][1]};
-        E::mma_acc_agpr(acc[cb], af, kk == 0 ? g0 : g1);
+        E::mma_acc_agpr(acc[cb], af, gk[kk]);
       }
-      // (an element group's LDS reads wait for every LDS read issued before them, so the waits of
-      // the later products stay correct)
-      if constexpr (m == (NCB >= 2 ? NCB / 2 - 1 : 0)) run_group(std::integral_constant<int, 2>{});
-      if constexpr (m == NCB - 1) {
-        run_group(std::integral_constant<int, 3>{});
-        g1 = i32x4{(int)gw2[4], (int)gw2[5], (int)gw2[6], (int)gw2[7]};
+      if constexpr (NBUF == 2 && LSPAN > NKS) {
+        __builtin_amdgcn_sched_barrier(0);
+        loads_after(std::integral_constant<int, NKS + m>{});
       }
     });
 
@@ -544,13 +621,14 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     mma_guard_all<NCB>(acc);
 
     if constexpr (NBUF == 1) {
-      if (t + 1 < ntiles) {
+      if (more) {
         block_sync();  // every wave is done with the buffer
         if constexpr (DQ) issue_tile(t + 1, 0, std::integral_constant<int, 1>{});
         else issue_tile(t + 1, 0, kAll);
       }
     }
   }
+  vm_wait<0>();  // (the loads after the last tile)
 
   // ---- epilogue: lane -> stationary index s, element i -> column ac0 + 32 cb + 8 (i / 4) + 4 hi + i % 4
   mma_guard_all<NCB>(acc);
