@@ -343,14 +343,17 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
   for (int c = 0; c < NCB; ++c) acc[c] = f32x16{};
 
   // The tile's products run in NKS + NA slots, the score products first.  Double-buffered, the next
-  // tile's NLD loads are spread over the first LSPAN slots, load j after slot j * LSPAN / NLD: issued
-  // all at once they hold the wave at the load unit's queue for about as long as the direct-load
-  // path needs to move the tile, with no product issued meanwhile.
+  // tile's NLD loads are spread over the first LSPAN slots (the score products and the first half of
+  // the accumulation products), load j after slot j * LSPAN / NLD: issued all at once they hold the
+  // wave at the load unit's queue for about as long as the direct-load path needs to move the tile,
+  // with no product issued meanwhile.
   constexpr int NA = NCB * 2;
   // fragments read PF products ahead (two where the dK/dV pass's 256 accumulators and a 512-column
   // stationary operand leave no room for more)
   constexpr int PF = (!DQ && KD > 896) ? 2 : 4;
-  constexpr int LSPAN = NKS;
+  // (padded head dims: over the score products only; in the accumulation products the padded dK/dV
+  // pass at 512 columns has no registers for them)
+  constexpr int LSPAN = PAD ? NKS : NKS + NA / 2;
   // the staged rows' LSE and Delta of all four element groups are read at the start of a tile where
   // two tiles are buffered and no column is padded (otherwise, and for the keep words, at their
   // group's first element: the registers they would hold across the score products are not there)
