@@ -58,10 +58,12 @@ struct BwdTiling {
   static constexpr int RG = 4 / GW;             // stationary blocks per workgroup
   static constexpr int NBLK = KD / 32;          // 32-column blocks per tensor tile
   static constexpr int TILE = 2 * NBLK * 2048;  // the two streamed tensors of one 32-index tile
-  static constexpr int ROWS = 768;              // staged per-row data of a tile: LSE, Delta, keep words
-  static constexpr int BUF = TILE + ROWS;
+  static constexpr int ROW1 = 768;              // staged per-row data of a tile: LSE, Delta, keep words
   static constexpr int EXCH = 4 * 4096;         // one partial score tile per wave
-  static constexpr int NBUF = 2 * BUF + EXCH <= 160 * 1024 ? 2 : 1;
+  static constexpr int NBUF = 2 * (TILE + ROW1) + EXCH <= 160 * 1024 ? 2 : 1;
+  // single-buffered, the dK/dV pass has every wave load its own copy of the staged rows
+  static constexpr int ROWS = NBUF == 1 ? 4 * ROW1 : ROW1;
+  static constexpr int BUF = TILE + ROWS;
   static constexpr int LDS_BYTES = NBUF * BUF + EXCH;
   static constexpr bool OK = KD % 64 == 0 && KD >= 64 && KD <= 1024 && AWQ % 32 == 0 && AWK % 32 == 0;
 };
@@ -311,6 +313,79 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     prep_tile(t, buf, ru, rw, dst, parts_c, true);
     static_for<NLD>([&](auto j_c) { issue_load(ru, rw, dst, j_c, parts_c); });
   };
+  // Single-buffered, the dK/dV pass's waves each read only their own quarter of a tile (their
+  // role's tensor, their column half), so each loads its quarter itself, as soon as its own
+  // products of the tile before are done, with no barrier, and its score products wait block by
+  // block for just the blocks they read.  Its stationary fragments kept in L2 (padded head dims: at
+  // the tile start, as their registers allow) and its copy of the staged rows are loaded first, so
+  // that the quarter's blocks are its youngest loads, two per block.
+  constexpr bool OWN = !DQ && NBUF == 1;
+  constexpr int NBH = SW / 32;  // blocks of a column half
+  uint32_t vown[2];
+#pragma unroll
+  for (int rh = 0; rh < 2; ++rh) {
+    const int lrow = 16 * rh + (lane >> 2);
+    const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+    vown[rh] = (uint32_t)(lrow * D + lchunk * 8) * 2u;
+  }
+  // (the quarter's descriptor and LDS destination, between own_head and the block loads)
+  __amdgpu_buffer_rsrc_t own_rt;
+  uint32_t own_dst = 0;
+  auto own_head = [&](int t) {
+    if constexpr (OWN) {
+      int t0, qh;
+      tile_pos(t, t0, qh);
+      if constexpr (NRL > 0 && !PAD) {
+        // (the address is made opaque so that the loads stay where they are)
+        const uint16_t* xr = xrow;
+        asm volatile("" : "+v"(xr));
+#pragma unroll
+        for (int kk = NKR; kk < NKS; ++kk) {
+          const bool in = !PAD || sc0 + 16 * kk + 8 * hi < D;
+          xf[kk] = in ? *(const i32x4*)(xr + 16 * kk) : i32x4{0, 0, 0, 0};
+        }
+      }
+      const int64_t fr = (int64_t)(b * a.Hq + qh) * a.Nq + t0;
+      {
+        // this wave's copy of the tile's rows: LSE and Delta (lane l -> row l % 32), keep words of the
+        // workgroup's keys (lane l -> row l % 32, word s0wg / 32 + l / 32); rows past Nq read as zero
+        const int nb = (a.Nq - t0) * 4;
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + fr), (short)0, nb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rd =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.delta + fr), (short)0, nb, 0x00020000);
+        const uint32_t rows = smem_addr + (uint32_t)(TILE + wave * BT::ROW1);
+        const uint32_t ro = (uint32_t)l32 * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FFPA_LDS void*)(uintptr_t)rows, 4, ro, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FFPA_LDS void*)(uintptr_t)(rows + 256), 4, ro, 0, 0, 0);
+        if (has_drop) {
+          const int kb = (int)((int64_t)(a.Nq - t0) * a.keep_w * 4);
+          const __amdgpu_buffer_rsrc_t rk =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(a.keep + fr * a.keep_w), (short)0, kb, 0x00020000);
+          const uint32_t ko = ((uint32_t)l32 * (uint32_t)a.keep_w + (uint32_t)(s0wg / 32 + hi)) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FFPA_LDS void*)(uintptr_t)(rows + 512), 4, ko, 0, 0, 0);
+        }
+      }
+      const uint16_t* tb = (role == 0 ? a.q : a.dout) + fr * D;
+      const int bytes = (int)((int64_t)(NT - t0) * D * 2);  // the descriptor's 32-bit record count
+      own_rt = __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, 0x00020000);
+      own_dst = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 32) * 2048);
+      asm volatile("" : "+s"(own_dst));
+    }
+  };
+  // block c of the quarter: rows 0-15 and 16-31, the column offset in the scalar offset (the
+  // instruction's immediate offset would move the LDS destination as well)
+  auto own_block = [&](auto c_c) {
+    if constexpr (OWN) {
+      constexpr int c = decltype(c_c)::value;
+      if (!PAD || sc0 + 32 * c < D) {
+        const int soff = (sc0 + 32 * c) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(own_rt, (FFPA_LDS void*)(uintptr_t)(own_dst + c * 2048), 16, vown[0],
+                                                 soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(own_rt, (FFPA_LDS void*)(uintptr_t)(own_dst + c * 2048 + 1024), 16,
+                                                 vown[1], soff, 0, 0);
+      }
+    }
+  };
 
   // ---- per-lane LDS addresses (block offsets are immediates; buffer offsets added at run time)
   // score operand read: row l32 of the role's tensor, 16-column step q of a block: chunk 2q + hi
@@ -360,13 +435,33 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
   constexpr bool HOIST = NBUF == 2 && !PAD;
 
   constexpr std::integral_constant<int, 7> kAll{};
-  if (ntiles > 0) issue_tile(0, 0, kAll);
+  if (ntiles > 0) {
+    if constexpr (OWN) {
+      own_head(0);
+      static_for<NBH>([&](auto c_c) { own_block(c_c); });
+    } else {
+      issue_tile(0, 0, kAll);
+    }
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int buf = NBUF == 2 ? (t & 1) : 0;
     int t0, qh;
     tile_pos(t, t0, qh);
-    vm_wait<0>();
-    block_sync();  // tile t visible; every wave is done with tile t - 1 (and its buffer)
+    // tile t visible, every wave done with tile t - 1 (its buffer, the exchange slots); a wave that
+    // loads its own quarter waits for it block by block below (padded head dims: all of it here,
+    // some of their blocks not being loaded)
+    if constexpr (!OWN || PAD) vm_wait<0>();
+    block_sync();
+    if constexpr (NRL > 0 && PAD) {
+      // (the address is made opaque so that the loads stay inside the loop)
+      const uint16_t* xr = xrow;
+      asm volatile("" : "+v"(xr));
+#pragma unroll
+      for (int kk = NKR; kk < NKS; ++kk) {
+        const bool in = sc0 + 16 * kk + 8 * hi < D;
+        xf[kk] = in ? *(const i32x4*)(xr + 16 * kk) : i32x4{0, 0, 0, 0};
+      }
+    }
     const uint32_t boff = (uint32_t)(buf * BUF);
     uint32_t kw = 0;
     if constexpr (DQ) {
@@ -402,16 +497,6 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         dl4[g] = lds_read_f4_async<256 + 32 * g>(ra);
       });
     }
-    if constexpr (NRL > 0) {
-      // (the address is made opaque so that the loads stay inside the loop)
-      const uint16_t* xr = xrow;
-      asm volatile("" : "+v"(xr));
-#pragma unroll
-      for (int kk = NKR; kk < NKS; ++kk) {
-        const bool in = !PAD || sc0 + 16 * kk + 8 * hi < D;
-        xf[kk] = in ? *(const i32x4*)(xr + 16 * kk) : i32x4{0, 0, 0, 0};
-      }
-    }
 
     // ---- the role's score product over its columns (fragments read PF products ahead)
     f32x16 own;
@@ -420,6 +505,9 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       constexpr int m = decltype(mc)::value;
       constexpr uint32_t off = (uint32_t)((m / 2) * 2048);
       static_assert(off < 65536, "ds offset field");
+      // own quarter: block m / 2 is complete once at most the two loads of each later block are
+      // outstanding
+      if constexpr (OWN && !PAD && m % 2 == 0) vm_wait<2 * (NBH - 1 - m / 2)>();
       fr[m % (PF + 1)] = lds_read_b128_async<off>(fa[m % 2] + boff);
     };
     static_for<PF>([&](auto mc) {
@@ -523,7 +611,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         float gv[4];
         if constexpr (!DQ) {
           // the group's staged rows not read yet (waits for every LDS read issued before them)
-          const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((8 * g + 4 * hi) * 4);
+          const uint32_t ra = smem_addr + boff + TILE + (uint32_t)((OWN ? wave * BT::ROW1 : 0) + (8 * g + 4 * hi) * 4);
           if constexpr (!HOIST) {
             lse4[g] = lds_read_f4_async<0>(ra);
             dl4[g] = lds_read_f4_async<256>(ra);
@@ -591,11 +679,17 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     else elements(std::integral_constant<int, 2>{});
 
     // ---- accumulation products: acc[cb] += (tensor^T) G over this wave's columns, step 0 (rows
-    // 0-15) of every block first
+    // 0-15) of every block first.  A wave that loads its own quarter takes the blocks one at a time
+    // instead (both steps of block cb, then block cb + 1) and loads the next tile's block cb as soon
+    // as its second step is done: the loads then leave one by one between the products, where all
+    // at once they would hold the wave at the load unit's queue for the length of the transfer.
+    if constexpr (OWN) {
+      if (more) own_head(t + 1);  // (this wave has read its staged rows and re-read fragments)
+    }
     i32x2 tl[PF + 1], th[PF + 1];
     auto read_a = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = m % NCB, kk = m / NCB;
+      constexpr int cb = OWN ? m / 2 : m % NCB, kk = OWN ? m % 2 : m / NCB;
       constexpr uint32_t off = (uint32_t)(cb * 2048 + kk * 1024);
       static_assert(off < 65536, "ds offset field");
       tl[m % (PF + 1)] = lds_read_tr_async<off>(ta + boff);
@@ -606,7 +700,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     });
     static_for<NA>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = m % NCB, kk = m / NCB;
+      constexpr int cb = OWN ? m / 2 : m % NCB, kk = OWN ? m % 2 : m / NCB;
       if constexpr (m + PF < NA) read_a(std::integral_constant<int, m + PF>{});
       constexpr int after = 2 * ((m + PF < NA ? m + PF : NA - 1) - m);
       lgkm_wait<after>();
@@ -618,16 +712,20 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         loads_after(std::integral_constant<int, NKS + m>{});
       }
+      if constexpr (OWN && kk == 1) {
+        // block cb's reads are complete (waited before this product)
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) own_block(std::integral_constant<int, cb>{});
+      }
     });
 
     // keeps the accumulators in AGPRs across the loop, after the wait states their last products need
     mma_guard_all<NCB>(acc);
 
-    if constexpr (NBUF == 1) {
+    if constexpr (!OWN && NBUF == 1) {
       if (more) {
         block_sync();  // every wave is done with the buffer
-        if constexpr (DQ) issue_tile(t + 1, 0, std::integral_constant<int, 1>{});
-        else issue_tile(t + 1, 0, kAll);
+        issue_tile(t + 1, 0, std::integral_constant<int, 1>{});
       }
     }
   }
