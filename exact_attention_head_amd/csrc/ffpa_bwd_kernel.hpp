@@ -33,10 +33,10 @@
 // streamed index of slot j is read in that same order on the A side: the transposed LDS reads
 // (ds_read_b64_tr_b16) fetch rows 16 kk + 4 (l / 32) + 0..3 and, with a second read, + 8.
 //
-// LDS tiles: per tensor, 32-column blocks of [32 rows][64 bytes] (2 KiB), chunk c of row r stored
-// at position c ^ ((r >> 2) & 3) (conflict-free for the operand reads and the transposed reads),
-// filled by buffer_load_dwordx4 ... lds (rows past the tensor's end read as zero); the dK/dV pass
-// stages each tile's LSE, Delta and keep words beside it.  Tiles are double-buffered where two fit
+// LDS tiles: per tensor, 64-column blocks of [32 rows][128 bytes] (4 KiB), 16-byte chunk c of row r
+// stored at position c ^ bwd_swz(r) (conflict-free for the operand reads and the transposed reads),
+// filled by buffer_load_dwordx4 ... lds with whole 128-byte row segments (rows past the tensor's end
+// read as zero); the dK/dV pass stages each tile's LSE, Delta and keep words beside it.  Tiles are double-buffered where two fit
 // next to the exchange slots (D <= 512), else the next tile is loaded once the current one has been
 // consumed.
 #pragma once
@@ -67,6 +67,20 @@ struct BwdTiling {
   static constexpr int LDS_BYTES = NBUF * BUF + EXCH;
   static constexpr bool OK = KD % 64 == 0 && KD >= 64 && KD <= 1024 && AWQ % 32 == 0 && AWK % 32 == 0;
 };
+
+// Position of the 16-byte chunks of LDS tile row r: logical chunk c of a 64-column block's row r
+// sits at c ^ bwd_swz(r).  A bijection of bits 1-3 of r, so that the 16 rows a 16-byte operand
+// read takes at once fill 16 distinct 16-byte slots of 256 bytes, and rows r and r + 2 of a
+// transposed read fall in different halves of their 128-byte rows.
+__device__ inline int bwd_swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// addr with bit 6 flipped, formed where it is used (opaque to the compiler, which would otherwise
+// keep it in a register of its own across the loop)
+__device__ inline uint32_t bwd_flip64(uint32_t addr) {
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, 64, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
 
 // The bias of one (row, key) of a runtime mask kind: -inf for an excluded boolean entry.
 __device__ inline float bwd_bias(const void* m, int kind, int64_t off) {
@@ -225,22 +239,21 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     }
   };
 
-  // loads: wave w fills 1 KiB pieces w, w + 4, ... of each tensor's tile; piece j = rows 16 (j % 2)
-  // .. +15 of 32-column block j / 2; lane t takes row 16 (j % 2) + t / 4, physical chunk t % 4,
-  // i.e. logical chunk (t % 4) ^ ((row >> 2) & 3).  Piece 4c + w is block 2c + w / 2, rows
-  // 16 (w % 2) ..: the lane's byte offset is fixed, the block step 128 c a scalar offset, and the
-  // tile's first row the descriptor's base (its record count ends at the tensor's last row, so rows past
-  // it read as zero).
+  // loads: whole 128-byte row segments.  Wave w fills rows 8w .. 8w + 7 of every 64-column block of
+  // each tensor's tile, one 1 KiB load per block; lane t takes row 8w + t / 8, physical chunk t % 8,
+  // i.e. logical chunk (t % 8) ^ bwd_swz(row).  The lane's byte offset is fixed, the block step
+  // 128 c a scalar offset, and the tile's first row the descriptor's base (its record count ends at
+  // the tensor's last row, so rows past it read as zero).
   const uint32_t smem_addr = lds_addr(smem);
   const bool has_drop = a.keep != nullptr;
   uint32_t vlane;
   {
-    const int lrow = 16 * (wave & 1) + (lane >> 2);
-    const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
-    vlane = (uint32_t)(lrow * D + (wave >> 1) * 32 + lchunk * 8) * 2u;
+    const int lrow = 8 * wave + (lane >> 3);
+    const int lchunk = (lane & 7) ^ bwd_swz(lrow);
+    vlane = (uint32_t)(lrow * D + lchunk * 8) * 2u;
   }
-  // A tile's loads: NLD per wave, load j the U piece (K, or Q) of block step j / 2 for even j, the W
-  // piece (V, or dO) for odd j.  prep_tile forms the two descriptors and the LDS destination and
+  // A tile's loads: NLD per wave, load j the U piece (K, or Q) of 64-column block j / 2 for even j,
+  // the W piece (V, or dO) for odd j.  prep_tile forms the two descriptors and the LDS destination and
   // issues the staged rows (PARTS: 1 the U tile, 2 the W tile, 4 the staged rows of the dK/dV pass);
   // issue_load then issues one load.  A tile that is not `valid` (past the last) gets descriptors of
   // no records, so that its loads read nothing and write zeros.
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
                         auto parts_c) {
     constexpr int j = decltype(j_c)::value, PARTS = decltype(parts_c)::value;
     constexpr int c = j / 2;
-    if (!PAD || (2 * c + (wave >> 1)) * 32 < D) {
+    if (!PAD || 64 * c < D) {
       // the block step goes in the scalar offset: the instruction's immediate offset would move the
       // LDS destination as well
       if constexpr (j % 2 == 0 && (PARTS & 1) != 0)
@@ -318,15 +331,17 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
   // products of the tile before are done, with no barrier, and its score products wait block by
   // block for just the blocks they read.  Its stationary fragments kept in L2 (padded head dims: at
   // the tile start, as their registers allow) and its copy of the staged rows are loaded first, so
-  // that the quarter's blocks are its youngest loads, two per block.
+  // that the quarter's blocks are its youngest loads, four per 64-column block.
   constexpr bool OWN = !DQ && NBUF == 1;
-  constexpr int NBH = SW / 32;  // blocks of a column half
+  constexpr int NBH = SW / 64;  // 64-column blocks of a column half
+  // rows 8 r .. 8 r + 7 (the lane layout of the tile loads above): rows 16 .. 31 take the lane
+  // offsets of rows 0 .. 15 (bwd_swz ignores bit 4) and 16 rows more in the scalar offset
   uint32_t vown[2];
 #pragma unroll
-  for (int rh = 0; rh < 2; ++rh) {
-    const int lrow = 16 * rh + (lane >> 2);
-    const int lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
-    vown[rh] = (uint32_t)(lrow * D + lchunk * 8) * 2u;
+  for (int r = 0; r < 2; ++r) {
+    const int lrow = 8 * r + (lane >> 3);
+    const int lchunk = (lane & 7) ^ bwd_swz(lrow);
+    vown[r] = (uint32_t)(lrow * D + lchunk * 8) * 2u;
   }
   // (the quarter's descriptor and LDS destination, between own_head and the block loads)
   __amdgpu_buffer_rsrc_t own_rt;
@@ -368,41 +383,57 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
       const uint16_t* tb = (role == 0 ? a.q : a.dout) + fr * D;
       const int bytes = (int)((int64_t)(NT - t0) * D * 2);  // the descriptor's 32-bit record count
       own_rt = __builtin_amdgcn_make_buffer_rsrc((void*)tb, (short)0, bytes, 0x00020000);
-      own_dst = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 32) * 2048);
+      own_dst = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 64) * 4096);
       asm volatile("" : "+s"(own_dst));
     }
   };
-  // block c of the quarter: rows 0-15 and 16-31, the column offset in the scalar offset (the
-  // instruction's immediate offset would move the LDS destination as well)
+  // 64-column block c of the quarter: four loads of 8 rows, the column offset in the scalar offset
+  // (the instruction's immediate offset would move the LDS destination as well)
   auto own_block = [&](auto c_c) {
     if constexpr (OWN) {
       constexpr int c = decltype(c_c)::value;
-      if (!PAD || sc0 + 32 * c < D) {
-        const int soff = (sc0 + 32 * c) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(own_rt, (FFPA_LDS void*)(uintptr_t)(own_dst + c * 2048), 16, vown[0],
-                                                 soff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(own_rt, (FFPA_LDS void*)(uintptr_t)(own_dst + c * 2048 + 1024), 16,
-                                                 vown[1], soff, 0, 0);
+      if (!PAD || sc0 + 64 * c < D) {
+        const int soff = (sc0 + 64 * c) * 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(own_rt, (FFPA_LDS void*)(uintptr_t)(own_dst + c * 4096 + r * 1024), 16,
+                                                   vown[r % 2], soff + (r / 2) * 16 * D * 2, 0, 0);
       }
     }
   };
 
   // ---- per-lane LDS addresses (block offsets are immediates; buffer offsets added at run time)
-  // score operand read: row l32 of the role's tensor, 16-column step q of a block: chunk 2q + hi
-  const uint32_t sbase = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 32) * 2048);
-  uint32_t fa[2];
+  // score operand read: row l32 of the role's tensor, 16-column step q of a 64-column block: chunk
+  // 2q + hi (the wave's first score column is a multiple of 64)
+  const uint32_t sbase = smem_addr + (uint32_t)(role * NBLK * 2048 + (sc0 / 64) * 4096);
+  // (steps 2 and 3 differ from steps 0 and 1 in chunk bit 2 only: their addresses are those of
+  // steps 0 and 1 with bit 6 flipped.  FLIP variants form them at each read, which costs an
+  // instruction in front of the read but the registers the dK/dV pass at 1024 columns, and padded
+  // at 512, do not have.)
+  constexpr bool FLIP = !DQ && (KD == 1024 || (KD == 512 && PAD));
+  uint32_t fa[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) fa[q] = sbase + l32 * 64 + (((2 * q + hi) ^ ((l32 >> 2) & 3)) * 16);
+  for (int q = 0; q < 4; ++q) fa[q] = sbase + l32 * 128 + (((2 * q + hi) ^ bwd_swz(l32)) * 16);
   // transposed read (accumulation products): lanes of a 16-lane group read rows 4 (l / 32) + i16 / 4
-  // (and + 8), columns 16 ((l / 16) % 2) + 4 (i16 % 4) .. + 3 of a block; the lane receives column
-  // l % 32 of rows 4 (l / 32) + 0..3 (and + 8)
+  // (and + 8), columns 16 ((l / 16) % 2) + 4 (i16 % 4) .. + 3 of a 32-column block; the lane
+  // receives column l % 32 of rows 4 (l / 32) + 0..3 (and + 8).  The wave's 32-column block cb is
+  // global block a0b + cb: half (a0b + cb) % 2 of 64-column block (a0b + cb) / 2, so even and odd cb
+  // take different bases (t?[0], t?[1]) and share the immediate offset (cb / 2) 4096 + kk 2048.
+  // In the dK/dV pass a0b is even, and the odd bases are the even ones with bit 6 flipped (formed at
+  // each read in FLIP variants).
   const int atens = DQ ? 0 : role;  // dQ: K^T; dK: Q^T; dV: dO^T
-  const uint32_t abase = smem_addr + (uint32_t)(atens * NBLK * 2048 + (ac0 / 32) * 2048);
+  const int a0b = ac0 / 32;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int trow = 4 * (g16 >> 1) + (i16 >> 2);
   const int tchunk = 2 * (g16 & 1) + ((i16 & 3) >> 1);
-  const uint32_t ta = abase + trow * 64 + ((tchunk ^ ((trow >> 2) & 3)) * 16) + 8 * (i16 & 1);
-  const uint32_t tb = abase + (trow + 8) * 64 + ((tchunk ^ (((trow + 8) >> 2) & 3)) * 16) + 8 * (i16 & 1);
+  uint32_t ta[2], tb[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int g = a0b + par;  // the global 32-column block of local cb = par
+    const uint32_t blk = smem_addr + (uint32_t)(atens * NBLK * 2048 + (g >> 1) * 4096) + 8 * (i16 & 1);
+    ta[par] = blk + trow * 128 + (((4 * (g & 1) + tchunk) ^ bwd_swz(trow)) * 16);
+    tb[par] = blk + (trow + 8) * 128 + (((4 * (g & 1) + tchunk) ^ bwd_swz(trow + 8)) * 16);
+  }
   // partial-tile exchange: slot per wave, 16 bytes per lane in four 1 KiB pieces
   const uint32_t ex_base = smem_addr + NBUF * BUF;
   const uint32_t ex_mine = ex_base + wave * 4096 + lane * 16;
@@ -503,12 +534,13 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     i32x4 fr[PF + 1];
     auto read_s = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr uint32_t off = (uint32_t)((m / 2) * 2048);
+      constexpr uint32_t off = (uint32_t)((m / 4) * 4096);
       static_assert(off < 65536, "ds offset field");
-      // own quarter: block m / 2 is complete once at most the two loads of each later block are
-      // outstanding
-      if constexpr (OWN && !PAD && m % 2 == 0) vm_wait<2 * (NBH - 1 - m / 2)>();
-      fr[m % (PF + 1)] = lds_read_b128_async<off>(fa[m % 2] + boff);
+      // own quarter: 64-column block m / 4 is complete once at most the four loads of each later
+      // block are outstanding
+      if constexpr (OWN && !PAD && m % 4 == 0) vm_wait<4 * (NBH - 1 - m / 4)>();
+      if constexpr (FLIP && m % 4 >= 2) fr[m % (PF + 1)] = lds_read_b128_async<off>(bwd_flip64(fa[m % 2]) + boff);
+      else fr[m % (PF + 1)] = lds_read_b128_async<off>(fa[m % 4] + boff);
     };
     static_for<PF>([&](auto mc) {
       if constexpr (decltype(mc)::value < NKS) read_s(mc);
@@ -690,10 +722,15 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     auto read_a = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
       constexpr int cb = OWN ? m / 2 : m % NCB, kk = OWN ? m % 2 : m / NCB;
-      constexpr uint32_t off = (uint32_t)(cb * 2048 + kk * 1024);
+      constexpr uint32_t off = (uint32_t)((cb / 2) * 4096 + kk * 2048);
       static_assert(off < 65536, "ds offset field");
-      tl[m % (PF + 1)] = lds_read_tr_async<off>(ta + boff);
-      th[m % (PF + 1)] = lds_read_tr_async<off>(tb + boff);
+      if constexpr (FLIP && cb % 2 == 1) {
+        tl[m % (PF + 1)] = lds_read_tr_async<off>(bwd_flip64(ta[0]) + boff);
+        th[m % (PF + 1)] = lds_read_tr_async<off>(bwd_flip64(tb[0]) + boff);
+      } else {
+        tl[m % (PF + 1)] = lds_read_tr_async<off>(ta[cb % 2] + boff);
+        th[m % (PF + 1)] = lds_read_tr_async<off>(tb[cb % 2] + boff);
+      }
     };
     static_for<PF>([&](auto mc) {
       if constexpr (decltype(mc)::value < NA) read_a(mc);
@@ -712,10 +749,10 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         loads_after(std::integral_constant<int, NKS + m>{});
       }
-      if constexpr (OWN && kk == 1) {
-        // block cb's reads are complete (waited before this product)
+      if constexpr (OWN && kk == 1 && cb % 2 == 1) {
+        // the reads of 64-column block cb / 2 are complete (waited before this product)
         __builtin_amdgcn_sched_barrier(0);
-        if (more) own_block(std::integral_constant<int, cb>{});
+        if (more) own_block(std::integral_constant<int, cb / 2>{});
       }
     });
 
