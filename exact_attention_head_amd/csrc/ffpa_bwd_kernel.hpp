@@ -333,6 +333,12 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
   // the tile start, as their registers allow) and its copy of the staged rows are loaded first, so
   // that the quarter's blocks are its youngest loads, four per 64-column block.
   constexpr bool OWN = !DQ && NBUF == 1;
+  // Single-buffered, the dQ pass streams the next tile into the buffer during the accumulation
+  // products, where each wave's dQ columns are whole 64-column blocks of K: V is free once the
+  // exchange is passed (only the dP products read it), and a K block once its owner (the one wave
+  // whose dQ columns it holds) has taken its accumulation products; the next tile's barrier then
+  // publishes both.
+  constexpr bool STREAM = DQ && NBUF == 1 && BT::AWQ % 64 == 0;
   constexpr int NBH = SW / 64;  // 64-column blocks of a column half
   // rows 8 r .. 8 r + 7 (the lane layout of the tile loads above): rows 16 .. 31 take the lane
   // offsets of rows 0 .. 15 (bwd_swz ignores bit 4) and 16 rows more in the scalar offset
@@ -574,7 +580,9 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     block_sync();
     // single buffer, dQ pass: V has been read for the last time (by the dP products); its next tile
     // can be loaded while K is still needed
-    if constexpr (NBUF == 1 && DQ) {
+    if constexpr (STREAM) {
+      if (more) prep_tile(t + 1, 0, nru, nrw, ndst, kAll, true);
+    } else if constexpr (NBUF == 1 && DQ) {
       if (more) issue_tile(t + 1, 0, std::integral_constant<int, 2>{});
     }
     // every wave reads the finished tiles back from the slots, in the same order (two terms per sum:
@@ -718,10 +726,11 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     if constexpr (OWN) {
       if (more) own_head(t + 1);  // (this wave has read its staged rows and re-read fragments)
     }
+    constexpr bool BM = OWN || STREAM;  // block-major order
     i32x2 tl[PF + 1], th[PF + 1];
     auto read_a = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = OWN ? m / 2 : m % NCB, kk = OWN ? m % 2 : m / NCB;
+      constexpr int cb = BM ? m / 2 : m % NCB, kk = BM ? m % 2 : m / NCB;
       constexpr uint32_t off = (uint32_t)((cb / 2) * 4096 + kk * 2048);
       static_assert(off < 65536, "ds offset field");
       if constexpr (FLIP && cb % 2 == 1) {
@@ -737,7 +746,7 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
     });
     static_for<NA>([&](auto mc) {
       constexpr int m = decltype(mc)::value;
-      constexpr int cb = OWN ? m / 2 : m % NCB, kk = OWN ? m % 2 : m / NCB;
+      constexpr int cb = BM ? m / 2 : m % NCB, kk = BM ? m % 2 : m / NCB;
       if constexpr (m + PF < NA) read_a(std::integral_constant<int, m + PF>{});
       constexpr int after = 2 * ((m + PF < NA ? m + PF : NA - 1) - m);
       lgkm_wait<after>();
@@ -754,12 +763,34 @@ __global__ __launch_bounds__(256) void ffpa_bwd_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (more) own_block(std::integral_constant<int, cb / 2>{});
       }
+      if constexpr (STREAM) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          // the next V: this wave's row group of 64-column block c after product c * NA / NVB
+          static_for<NBLK / 2>([&](auto c_c) {
+            constexpr int c = decltype(c_c)::value;
+            if constexpr (c * NA / (NBLK / 2) == m) issue_load(nru, nrw, ndst, std::integral_constant<int, 2 * c + 1>{}, kAll);
+          });
+          // the next K block this wave owns, once its products here are done (its reads waited
+          // before this product): all four row groups
+          if constexpr (kk == 1 && cb % 2 == 1) {
+            const int blk = ac0 / 64 + cb / 2;
+            if (!PAD || 64 * blk < D) {
+              const uint32_t kd = smem_addr + (uint32_t)(blk * 4096);
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(nru, (FFPA_LDS void*)(uintptr_t)(kd + r * 1024), 16, vown[r % 2],
+                                                         blk * 128 + (r / 2) * 16 * D * 2, 0, 0);
+            }
+          }
+        }
+      }
     });
 
     // keeps the accumulators in AGPRs across the loop, after the wait states their last products need
     mma_guard_all<NCB>(acc);
 
-    if constexpr (!OWN && NBUF == 1) {
+    if constexpr (!OWN && !STREAM && NBUF == 1) {
       if (more) {
         block_sync();  // every wave is done with the buffer
         issue_tile(t + 1, 0, std::integral_constant<int, 1>{});
