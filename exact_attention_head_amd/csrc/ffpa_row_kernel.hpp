@@ -511,7 +511,11 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   };
 
   const int64_t mask_bh = (int64_t)b * a.msb + (int64_t)hq * a.msh;
-  const bool has_mask = a.mask_kind != kMaskNone;
+  // (the staged-mask modes always have one)
+  const bool has_mask = MASK_LDS || a.mask_kind != kMaskNone;
+  // explicit logits are formed in natural units, scale S + bias in one operation, and enter the
+  // log2-domain softmax through its maximum and exponent
+  const float scale_nat = a.scale_log2 * kLn2;
 
   // partial-S exchange (two column groups): [wave][4 x 1 KiB], 16 bytes per lane, one block at a time
   const uint32_t ex_mine = ring_addr + RT::RING + wave * 4096 + lane * 16;
@@ -570,14 +574,17 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   }
   float m_run = kNegInf;  // running reference maximum of this lane's row (log2 domain)
   float l_lane = 0.f;     // sum of this lane's probabilities (the other half-wave holds the rest)
-  auto tile_body = [&](const int j, auto raw_c) {
+  // EDGE: the tile may touch the key tail or the causal diagonal (explicit tiles test each entry
+  // then); tiles known to be clear of both skip the tests
+  auto tile_body = [&](const int j, auto raw_c, auto edge_c) {
     constexpr bool RAW = decltype(raw_c)::value;
+    constexpr bool EDGE = decltype(edge_c)::value;
     constexpr int NLP = row_sm_logit_pieces(RAW);
     constexpr int NSP = row_sm_pieces(RAW);
     const int key0 = j * BC;
     const bool tail = key0 + BC > Nkv;
     const bool diag = a.causal && (key0 + BC - 1 > rw0 + off);
-    const bool edge = RAW ? false : (tail || diag);
+    const bool edge = RAW || !EDGE ? false : (tail || diag);
     // last key of the tile this lane's row may see (keys past Nkv and past the causal limit are
     // excluded), relative to the tile's first key
     int edge_lim = Nkv - 1;
@@ -633,14 +640,15 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           for (int e = e0; e < e0 + 2; ++e) {
             float x = s_acc[kb][4 * g + e];
             if constexpr (DG == 2) x += part[kb][g][e];
-            x *= a.scale_log2;
             if constexpr (MASK_U8) {
               // byte e of word g: nonzero takes part (through a scalar: a bit cast of the vector
               // element itself would read element 0)
               const float wf = bias[kb][0][g];
-              x = ((__builtin_bit_cast(uint32_t, wf) >> (8 * e)) & 0xffu) ? x : kNegInf;
+              x = ((__builtin_bit_cast(uint32_t, wf) >> (8 * e)) & 0xffu) ? x * scale_nat : kNegInf;
             } else if (has_mask) {
-              x = __builtin_fmaf(bias[kb][g][e], kLog2e, x);
+              x = __builtin_fmaf(x, scale_nat, bias[kb][g][e]);
+            } else {
+              x *= scale_nat;
             }
             if (edge) x = 8 * g + e > lim ? kNegInf : x;
             mx = __builtin_fmaxf(mx, x);
@@ -650,7 +658,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
           asm volatile("" : "+v"(s_acc[kb]), "+v"(lmax[kb]));
         }
       } else if (k == NLP) {
-        mt[kb] = RAW ? max_halves(lmax[kb]) * a.scale_log2 : max_halves(lmax[kb]);
+        mt[kb] = max_halves(lmax[kb]) * (RAW ? a.scale_log2 : kLog2e);
         m_old[kb] = m_run;
         asm volatile("" : "+v"(mt[kb]), "+v"(m_old[kb]));
       } else if (k == NLP + 1) {
@@ -674,7 +682,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
         const int i = k - NLP - 3;  // key 0..15 of this lane's 16 in the block
         const int g = i >> 2, e = i & 3;
         const float sv = s_acc[kb][4 * g + e];
-        const float x = RAW ? __builtin_fmaf(sv, a.scale_log2, -mref[kb]) : sv - mref[kb];
+        const float x = __builtin_fmaf(sv, RAW ? a.scale_log2 : kLog2e, -mref[kb]);
         const float p = __builtin_amdgcn_exp2f(x);
         psum[kb] += p;
         float pd = p;  // the weight that enters P V
@@ -829,19 +837,25 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     });
   };
+  // tiles whose keys all lie below Nkv and (causal) whose last key is visible to the workgroup's
+  // first row are whole for all its rows
+  int nwhole = (a.causal ? r0 + off + 1 : Nkv) / BC;
+  nwhole = nwhole < ntiles ? nwhole : ntiles;
+  nwhole = nwhole > 0 ? nwhole : 0;
   if constexpr (MODE == kRowRaw) {
-    for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{});
+    for (int j = 0; j < ntiles; ++j) tile_body(j, std::true_type{}, std::false_type{});
   } else if constexpr (MODE == kRowGeneral || MODE == kRowMaskF32 || MODE == kRowMaskU8) {
-    for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{});
+    // (the dropout variant at D = 1024 has no registers for a second tile body: one loop, tested)
+    if constexpr (DROP && D == 1024) {
+      for (int j = 0; j < ntiles; ++j) tile_body(j, std::false_type{}, std::true_type{});
+    } else {
+      for (int j = 0; j < nwhole; ++j) tile_body(j, std::false_type{}, std::false_type{});
+      for (int j = nwhole; j < ntiles; ++j) tile_body(j, std::false_type{}, std::true_type{});
+    }
   } else {
     static_assert(MODE == kRowSplit, "tile mode");
-    // tiles whose keys all lie below Nkv and (causal) whose last key is visible to the workgroup's
-    // first row are whole for all its rows
-    int nraw = (a.causal ? r0 + off + 1 : Nkv) / BC;
-    nraw = nraw < ntiles ? nraw : ntiles;
-    nraw = nraw > 0 ? nraw : 0;
-    for (int j = 0; j < nraw; ++j) tile_body(j, std::true_type{});
-    for (int j = nraw; j < ntiles; ++j) tile_body(j, std::false_type{});
+    for (int j = 0; j < nwhole; ++j) tile_body(j, std::true_type{}, std::false_type{});
+    for (int j = nwhole; j < ntiles; ++j) tile_body(j, std::false_type{}, std::true_type{});
   }
   vm_wait<0>();
   // the last tile read the next tile's first fragments (never used): their registers stay reserved until
