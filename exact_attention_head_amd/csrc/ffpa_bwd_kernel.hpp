@@ -36,9 +36,12 @@
 // LDS tiles: per tensor, 64-column blocks of [32 rows][128 bytes] (4 KiB), 16-byte chunk c of row r
 // stored at position c ^ bwd_swz(r) (conflict-free for the operand reads and the transposed reads),
 // filled by buffer_load_dwordx4 ... lds with whole 128-byte row segments (rows past the tensor's end
-// read as zero); the dK/dV pass stages each tile's LSE, Delta and keep words beside it.  Tiles are double-buffered where two fit
-// next to the exchange slots (D <= 512), else the next tile is loaded once the current one has been
-// consumed.
+// read as zero); the dK/dV pass stages each tile's LSE, Delta and keep words beside it.  Tiles are
+// double-buffered where two fit next to the exchange slots (D <= 512), the next tile's loads spread
+// over the current tile's products.  Above that, one buffer: in the dK/dV pass each wave reloads its
+// own quarter of the tile block by block as its products release it; the dQ pass streams the next
+// tile in during its accumulation products where its waves' dQ columns are whole 64-column blocks
+// (768 and 1024 columns), and otherwise loads it once the current one has been consumed.
 #pragma once
 
 #include <type_traits>
