@@ -403,7 +403,7 @@ def attn_fp8(query, key, value, q_descale=None, k_descale=None, v_descale=None, 
     torch.float8_e4m3fn tensors on the GPU; q_descale [B, Hq], k_descale and v_descale [B, Hkv] are
     positive float32 per-head dequantisation factors (None = 1), so that the attention runs over
     descale * tensor.  O is returned in out_dtype (torch.bfloat16 by default, or torch.float16), and
-    with return_lse also the fp32 [B, Hq, Nq] LSE.  Other arguments as for ``attn``; 16 <= D <= 512
+    with return_lse also the fp32 [B, Hq, Nq] LSE.  Other arguments as for ``attn``; 16 <= D <= 1024
     with D % 16 == 0.  Non-contiguous inputs are copied to contiguous ones first."""
     import torch
 

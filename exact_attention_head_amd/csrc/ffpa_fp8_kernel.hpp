@@ -205,23 +205,6 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const uint8_t* kg = (const uint8_t*)a.k + (int64_t)(b * a.Hkv + hk) * Nkv * kv_rs;
   const uint8_t* vg = (const uint8_t*)a.v + (int64_t)(b * a.Hkv + hk) * Nkv * kv_rs;
 
-  // ---- Q rows in VGPRs: step s holds bytes col0 + 64 s + 32 hi .. +31 of row l32 (zero past dcols)
-  i32x8 qf[NS];
-  {
-    const int qrow = row < Nq ? row : Nq - 1;
-    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 32);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int c = col0 + 64 * s + 32 * hi;
-      const i32x4 lo = c < a.dcols ? src[4 * s] : i32x4{0, 0, 0, 0};
-      const i32x4 up = c + 16 < a.dcols ? src[4 * s + 1] : i32x4{0, 0, 0, 0};
-      qf[s] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
-    }
-    vm_wait<0>();
-#pragma unroll
-    for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qf[s]));
-  }
-
   // ---- ring loads: wave w fills rows 8w .. 8w+7 of a group (lane t: row 8w + t/8, physical chunk t%8
   // holding logical chunk (t%8) ^ pi((row >> 1) & 7)); the row part of the offset is a scalar
   auto pi7 = [](int x) { return ((x & 1) << 2) | (x >> 1); };
@@ -317,13 +300,39 @@ __global__ __launch_bounds__(256) void ffpa_fwd_fp8_kernel(FwdArgs a) {
   const uint32_t ex_partner = ring_addr + FT::NG * 4096 + (wave ^ 1) * 8192 + lane * 16;
   f32x4 part[4];  // the partner's partial of the block being published
 
-  // ---- prologue: epochs 0 .. LA-1 in flight, epoch 0 visible, the first PF fragments requested
+  // ---- prologue: the Q rows in VGPRs (step s holds bytes col0 + 64 s + 32 hi .. +31 of row l32,
+  // zero past dcols), then epochs 0 .. LA-1 in flight behind them, so that the Q rows and the ring's
+  // first keys are fetched together; then Q and epoch 0 visible, the first PF fragments requested
+  i32x8 qf[NS];
+  {
+    const int qrow = row < Nq ? row : Nq - 1;
+    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 32);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int c = col0 + 64 * s + 32 * hi;
+      const i32x4 lo = c < a.dcols ? src[4 * s] : i32x4{0, 0, 0, 0};
+      const i32x4 up = c + 16 < a.dcols ? src[4 * s + 1] : i32x4{0, 0, 0, 0};
+      qf[s] = i32x8{lo[0], lo[1], lo[2], lo[3], up[0], up[1], up[2], up[3]};
+    }
+  }
+  // the first stage's epochs are issued whether or not it exists (their tile index is clamped into
+  // the head, and the wait below completes them before anything else uses the LDS): a load on one
+  // path only would make the compiler wait for every load before the Q rows' use
   static_for<LA>([&](auto e_c) {
     constexpr int E = decltype(e_c)::value;
     static_for<NL>([&](auto q_c) {
-      issue_epoch_load(0, std::integral_constant<int, 0>{}, std::integral_constant<int, E>{}, q_c);
+      constexpr int Q = decltype(q_c)::value;
+      if constexpr (E < EPT)
+        issue_group(0, std::integral_constant<int, 0>{}, std::integral_constant<int, Q / BIW>{},
+                    std::integral_constant<int, E * BIW + Q % BIW>{});
+      else
+        issue_epoch_load(0, std::integral_constant<int, 0>{}, std::integral_constant<int, E>{}, q_c);
     });
   });
+  // complete here, and redefine through the assembler: the compiler then has no load of these
+  // registers to wait for inside the key loop
+#pragma unroll
+  for (int s = 0; s < NS; ++s) asm volatile("" : "+v"(qf[s]));
   wait_epoch(0);
   __builtin_amdgcn_s_barrier();
   static_for<NL>([&](auto q_c) {

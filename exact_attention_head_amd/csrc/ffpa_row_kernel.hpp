@@ -394,24 +394,6 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const int ntiles = (kv_end + BC - 1) / BC;
   const int total_epochs = ntiles * EPT;
 
-  // ---- this wave's Q rows (its DW columns), in VGPRs for the whole key loop
-  i32x4 qf[DW / 16];
-  {
-    const int qrow = row < Nq ? row : Nq - 1;
-    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 8);
-#pragma unroll
-    for (int k = 0; k < DW / 16; ++k) {
-      // runtime layouts may carry a padded head dim: columns from dcols on are not read and hold zero
-      if constexpr (VL) qf[k] = col0 + hi * 8 + 16 * k < a.dcols ? src[k * 2] : i32x4{0, 0, 0, 0};
-      else qf[k] = src[k * 2];
-    }
-    // complete here, and redefine through the assembler: the compiler then has no load of these
-    // registers to wait for inside the key loop (where it would drain the prefetch ring)
-    vm_wait<0>();
-#pragma unroll
-    for (int k = 0; k < DW / 16; ++k) asm volatile("" : "+v"(qf[k]));
-  }
-
   // ---- ring loads: wave w fills rows 8w .. 8w+7 of every sub-tile (its w-th KiB): lane t takes
   // row 8w + t/8 and stores physical chunk t%8, i.e. logical chunk (t%8) ^ pi((row >> 1) & 7).
   // One descriptor per tensor head (its size ends at key Nkv, so rows past it read as zero); the
@@ -554,13 +536,42 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   const uint32_t mrd = ring_addr + MASK_OFF + mr * MROWB;
   const int mswz = pi7((mr >> 1) & 7);
 
-  // ---- prologue: the first tile's mask rows and epochs 0 .. LA-1 in flight, epoch 0 (and the
-  // mask, issued before it) visible, the first PF fragments requested
+  // ---- prologue: this wave's Q rows (its DW columns, in VGPRs for the whole key loop), then the
+  // first tile's mask rows and epochs 0 .. LA-1 in flight behind them, so that the Q rows and the
+  // ring's first keys are fetched together; then Q, epoch 0 (and the mask, issued before it)
+  // visible, the first PF fragments requested
+  i32x4 qf[DW / 16];
+  {
+    const int qrow = row < Nq ? row : Nq - 1;
+    const i32x4* src = (const i32x4*)(qg + (int64_t)qrow * q_rs + col0 + hi * 8);
+#pragma unroll
+    for (int k = 0; k < DW / 16; ++k) {
+      // runtime layouts may carry a padded head dim: columns from dcols on are not read and hold zero
+      if constexpr (VL) qf[k] = col0 + hi * 8 + 16 * k < a.dcols ? src[k * 2] : i32x4{0, 0, 0, 0};
+      else qf[k] = src[k * 2];
+    }
+  }
   if constexpr (MASK_LDS) {
     issue_mask(0, 0);
     issue_mask(0, 1);
   }
-  static_for<LA>([&](auto e_c) { issue_epoch(0, voff_lane, e_c); });
+  // the first tile's epochs are issued whether or not the tile exists (with no key tile their rows
+  // land in the ring unread, and the wait below completes them before anything else uses the LDS):
+  // a load on one path only would make the compiler wait for every load before the Q rows' use
+  static_for<LA>([&](auto e_c) {
+    constexpr int E = decltype(e_c)::value;
+    if constexpr (E < EPT) {
+      static_for<BI>([&](auto i_c) {
+        issue_group(voff_lane, std::integral_constant<int, 0>{}, std::integral_constant<int, E * BI + decltype(i_c)::value>{});
+      });
+    } else {
+      issue_epoch(0, voff_lane, e_c);
+    }
+  });
+  // complete here, and redefine through the assembler: the compiler then has no load of these
+  // registers to wait for inside the key loop (where it would drain the prefetch ring)
+#pragma unroll
+  for (int k = 0; k < DW / 16; ++k) asm volatile("" : "+v"(qf[k]));
   wait_epoch(0);
   __builtin_amdgcn_s_barrier();
   issue_epoch(0, voff_lane, std::integral_constant<int, LA>{});
