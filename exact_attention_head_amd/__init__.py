@@ -306,6 +306,11 @@ def _mask_desc(attn_mask, B, Hq, Nq, Nkv):
     return desc, m
 
 
+def _records_grad(torch, tensors) -> bool:
+    """Whether autograd would record an operation on these tensors (None entries are skipped)."""
+    return torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in tensors)
+
+
 def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False,
          scale: Optional[float] = None, enable_gqa: bool = False, return_lse: bool = False, out=None,
          dropout_seed: Optional[int] = None, dropout_keep=None, return_dropout_keep: bool = False):
@@ -321,6 +326,11 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     offset 0, or taken from ``dropout_keep`` (int32 [B, Hq, Nq, ceil(Nkv / 32)] words, any bits;
     dropout_p then sets the scaling).  ``return_dropout_keep`` appends the keep words to the result.
     Dropout runs on contiguous tensors (others are copied first).
+
+    Autograd, as for SDPA: with grad mode on and query, key, value or a floating attn_mask requiring
+    grad, the call is recorded (``attn_with_grad``): the backward runs ffpa_bwd, ffpa_bwd_dropout or
+    ffpa_bwd_mask_grad, and the LSE is returned without a gradient.  ``out``, ``dropout_keep`` and
+    ``return_dropout_keep`` are not recorded and raise in that case.
     """
     import torch
 
@@ -330,6 +340,13 @@ def attn(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: b
     for name, t in (("query", query), ("key", key), ("value", value)):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
             raise ValueError(f"{name} must be a 4-D tensor [B, H, N, D]")
+    if _records_grad(torch, (query, key, value, attn_mask)):
+        if out is not None or dropout_keep is not None or return_dropout_keep:
+            raise ValueError("out, dropout_keep and return_dropout_keep are not recorded for autograd: call "
+                             "under torch.no_grad(), or leave them out")
+        o, lse = AttnFunction().apply(query, key, value, attn_mask, is_causal, scale, enable_gqa, float(dropout_p),
+                                      dropout_seed)
+        return (o, lse) if return_lse else o
     if query.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"query dtype {query.dtype} is neither bfloat16 nor float16")
     if key.dtype != query.dtype or value.dtype != query.dtype:
@@ -498,7 +515,8 @@ def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seql
     own, with the tail-aligned causal rule of its own lengths.
 
     Returns O [Tq, Hq, D], or (O, LSE [Hq, Tq] float32) with return_lse.  The offsets are checked on
-    a host copy (one device-to-host transfer) before the launch.
+    a host copy (one device-to-host transfer) before the launch.  There is no backward: with grad mode
+    on, inputs that require grad raise NotImplementedError.
     """
     import torch
 
@@ -513,6 +531,10 @@ def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seql
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dim() != 3:
             raise ValueError(f"{name} must be a 3-D tensor [T, H, D]")
+    if _records_grad(torch, (q, k, v)):
+        # a result without a gradient would drop the attention's share of it without a word
+        raise NotImplementedError("packed batches have no backward: call under torch.no_grad(), or run each "
+                                  "sequence through attn")
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise TypeError(f"q dtype {q.dtype} is neither bfloat16 nor float16")
     if k.dtype != q.dtype or v.dtype != q.dtype:

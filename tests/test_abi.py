@@ -226,6 +226,37 @@ def test_cu_seqlens_host_check():
     assert "max_seqlen" in detail()
 
 
+def test_attn_records_autograd_when_inputs_need_grad():
+    """With grad mode on and an input requiring grad, attn goes through the autograd function (here it
+    then stops at the device check inside it); out and the dropout-word options are refused there."""
+    import torch
+
+    qb = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16, requires_grad=True)
+    kb = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="autograd"):
+        ffpa.attn(qb, kb, kb, out=torch.empty(1, 2, 4, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="autograd"):
+        ffpa.attn(qb, kb, kb, dropout_p=0.1, return_dropout_keep=True)
+    with pytest.raises(ValueError, match="same GPU"):  # recorded, then the forward's own checks
+        ffpa.attn(qb, kb, kb)
+    with torch.no_grad(), pytest.raises(ValueError, match="same GPU"):  # nothing recorded: out is fine
+        ffpa.attn(qb, kb, kb, out=torch.empty(1, 2, 4, 64, dtype=torch.bfloat16))
+    # a floating mask that requires grad is recorded too
+    m = torch.zeros(1, 1, 4, 4, requires_grad=True)
+    with pytest.raises(ValueError, match="autograd"):
+        ffpa.attn(kb, kb, kb, attn_mask=m, out=torch.empty(1, 2, 4, 64, dtype=torch.bfloat16))
+
+
+def test_varlen_refuses_inputs_that_need_grad():
+    import torch
+
+    q = torch.zeros(10, 2, 64, dtype=torch.bfloat16, requires_grad=True)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(NotImplementedError, match="no backward"):
+        ffpa.attn_varlen(q, q, q, cu, cu, 6, 6)
+    with torch.no_grad(), pytest.raises(ValueError):  # nothing recorded: on to the device check
+        ffpa.attn_varlen(q, q, q, cu, None, 6, 6)
+
 def test_varlen_python_layer_rejects_before_the_library():
     import torch
 

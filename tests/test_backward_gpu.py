@@ -148,3 +148,21 @@ def test_autograd_function_matches():
     for g, w in zip(got, want):
         assert torch.equal(g, w)
     _log("autograd", _compare(got, q, k, v, do, is_causal=True))
+
+
+def test_attn_records_autograd_like_sdpa():
+    """attn on inputs that require grad records the call: the same gradients as attn_with_grad, bit for
+    bit, with the LSE returned beside O and no gradient of its own; under no_grad nothing is recorded."""
+    q, k, v, do = _case(1, 4, 2, 100, 120, 512, seed=12)
+    qd, kd, vd = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    o, lse = ffpa.attn(qd, kd, vd, is_causal=True, enable_gqa=True, return_lse=True)
+    assert o.grad_fn is not None and not lse.requires_grad
+    o.backward(do.to(DEV))
+    got = (qd.grad.cpu(), kd.grad.cpu(), vd.grad.cpu())
+    qw, kw, vw = (t.to(DEV).requires_grad_(True) for t in (q, k, v))
+    ffpa.attn_with_grad(qw, kw, vw, is_causal=True, enable_gqa=True).backward(do.to(DEV))
+    for g, w in zip(got, (qw.grad.cpu(), kw.grad.cpu(), vw.grad.cpu())):
+        assert torch.equal(g, w)
+    with torch.no_grad():
+        assert ffpa.attn(qd, kd, vd, is_causal=True, enable_gqa=True).grad_fn is None
+    _log("attn autograd", _compare(got, q, k, v, do, is_causal=True))
