@@ -51,13 +51,15 @@ struct RingPlan {
   int em, ng;
 };
 
-constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes) {
+// Epochs shorter than min_em are taken only where no plan with longer ones fits.
+constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes, int min_em = 0) {
   RingPlan best{0, 0};
   int best_score = -1;
   const int ems[4] = {32, 16, 8, 4};
   for (int i = 0; i < 4; ++i) {
     const int em = ems[i];
     if (em == 4 && best.em != 0) break;  // four-product epochs only where nothing longer fits (D = 64)
+    if (em < min_em && best.em != 0) break;
     if (MPT % em != 0) continue;
     const int bi = em / 4;  // groups per epoch (four products per wave per group)
     for (int ng = 40; ng >= bi; --ng) {
@@ -78,7 +80,11 @@ constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes) {
   return best;
 }
 
-template <int D>
+// STAGED: the staged-mask variants.  Above D = 512 they take 16-product epochs where a plan has them
+// (D = 1024: half the barriers per tile against 32 products of lookahead instead of 48), which
+// measured 1.4% faster on the fp32-mask cross-attention workload; the other variants keep the plan
+// that fits their registers (16-product epochs spill the general variant at D = 1024).
+template <int D, bool STAGED = false>
 struct RowTiling {
   static constexpr int DG = D <= 512 ? 1 : 2;
   static constexpr int DW = D / DG;             // output columns per wave
@@ -90,7 +96,7 @@ struct RowTiling {
   static constexpr int MPT = 8 * NSUB;          // products per wave per tile
   static constexpr int EXCH = DG == 2 ? 4 * 4096 : 0;  // partial-S exchange: [wave][4 KiB]
   static constexpr int MASKB = BR * 128 * 2;            // staged fp32 mask: [block][row][32 keys]
-  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH + MASKB);
+  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH + MASKB, STAGED && DG == 2 ? 16 : 0);
   static constexpr int EM = PLAN.em;
   static constexpr int NG = PLAN.ng;
   static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB % 2 == 0 && NSUB >= 2;
@@ -262,7 +268,7 @@ constexpr bool row_barrier_within(int first, int last, int EM, int PF) {
 // keeps them compile-time.
 template <typename T, int D, int MODE, bool VL, bool DROP = false>
 __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
-  using RT = RowTiling<D>;
+  using RT = RowTiling<D, MODE == kRowMaskF32 || MODE == kRowMaskU8>;
   using E = Elem<T>;
   static_assert(RT::OK, "no ring plan for this head dim");
   constexpr int DG = RT::DG, DW = RT::DW, NSUB = RT::NSUB, BR = RT::BR, GPP = RT::GPP;
