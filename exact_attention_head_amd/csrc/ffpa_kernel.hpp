@@ -1,8 +1,9 @@
 // Exact large-head-dim attention forward for gfx950 (MI355X, CDNA4): shared definitions (argument
 // block, matrix-core wrappers, logit and mask helpers, the staged O store), the launcher, and the
-// shared-staging kernel that serves the head dims the row-owner kernel (ffpa_row_kernel.hpp: 64,
-// 128, 192, ..., 512, 640, 768, 896, 1024) does not: the multiples of 64 above 512 whose half is an
-// odd number of 32-column steps (576, 704, 832, 960).
+// shared-staging kernel compiled for the head dims the row-owner kernel (ffpa_row_kernel.hpp: 64,
+// 128, 192, ..., 512, 640, 768, 896, 1024) does not take: the multiples of 64 above 512 whose half is
+// an odd number of 32-column steps (576, 704, 832, 960).  It serves them with dropout only; without
+// it the row kernel of the next head dim runs them padded, several times faster.
 //
 // Shared-staging kernel.  One workgroup = 4 wave64s = one (batch, query head, tile of BR query rows).
 // It loops over the keys in tiles of BC = 64 and keeps an online softmax, as

@@ -80,8 +80,9 @@ enum {
  *   lse  device, [B, Hq, Nq] float32, natural log; written; NULL skips it
  *   B, Hq, Hkv, Nq, Nkv >= 1; Hq % Hkv == 0; 8 <= D <= 1024 with D % 8 == 0
  *        (head dims divisible by 8, as the README's "End-to-End Inference"
- *        section allows; a D without a kernel of its own runs the next one up,
- *        see ffpa_kernel_head_dim; K and V must then hold finite values, since
+ *        section allows; a D other than 64, 128, 192, 256, 320, 384, 448,
+ *        512, 640, 768, 896 and 1024 runs the next of these up, see
+ *        ffpa_kernel_head_dim; K and V must then hold finite values, since
  *        the padding columns of one key row read the next row's first ones,
  *        multiplied by zero)
  *   scale   finite, or NaN for the default 1/sqrt(D)
@@ -303,10 +304,12 @@ const char* ffpa_last_error_detail(void);
  * use), or 0 for an unsupported D.  Host-only; for schedulers and tests. */
 int ffpa_rows_per_block(int64_t D);
 
-/* Head dim of the kernel that serves tensors of head dim D: D itself when
- * D % 64 == 0, else the smallest head dim above D among 64, 128, 192, 256,
- * 320, 384, 448, 512, 640, 768, 896 and 1024 (its columns past D are padding:
- * zeros in Q, never stored in O).  0 for an unsupported D.  Host-only. */
+/* Head dim of the kernel that serves tensors of head dim D in ffpa_fwd,
+ * ffpa_fwd_strided and ffpa_fwd_varlen: the smallest of 64, 128, 192, 256,
+ * 320, 384, 448, 512, 640, 768, 896 and 1024 at or above D (its columns past
+ * D are padding: zeros in Q, never stored in O).  576, 704, 832 and 960 thus
+ * run 640, 768, 896 and 1024; with dropout (ffpa_fwd_dropout) they run
+ * kernels of their own.  0 for an unsupported D.  Host-only. */
 int64_t ffpa_kernel_head_dim(int64_t D);
 
 /* Name of the GPU kernel that serves head dim D (as profilers list it, without
