@@ -120,6 +120,23 @@ def test_bool_mask_staged_shapes(shape, D):
     _log(f"staged bool mask shape {shape} D={D}", compare(o, l, q, k, v, mask=mask))
 
 
+@pytest.mark.parametrize("kind", ["bool", "f32"])
+@pytest.mark.parametrize("D", [512, 1024])
+@pytest.mark.parametrize("Nkv", [64, 128])
+def test_mask_staged_few_key_tiles(kind, D, Nkv):
+    """Staged masks over one or two key tiles: the ring's first epochs (issued together with the Q
+    rows) then cover most or all of the keys, and at D = 1024 the staged-mask variants advance the
+    ring in 16-product epochs."""
+    q, k, v = _case(2, 2, 2, 130, Nkv, D, seed=D + Nkv + (kind == "bool"))
+    bias = _bias((2, 1, 130, Nkv), seed=D * 7 + Nkv)
+    if kind == "bool":
+        mask = bias > -0.5
+        mask[..., 0] = True
+    else:
+        mask = bias
+    o, l = run_gpu(q, k, v, mask=mask)
+    _log(f"staged mask {kind} D={D} Nkv={Nkv}", compare(o, l, q, k, v, mask=mask))
+
 @pytest.mark.parametrize("D", [64, 512, 1024])
 def test_bool_mask_staged_dead_rows(D):
     """Rows whose mask admits no key get O = 0 and LSE = -inf on the staged path too."""
