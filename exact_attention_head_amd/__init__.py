@@ -26,7 +26,8 @@ __all__ = ["attn", "attn_varlen", "attn_fp8", "ffpa_fwd_fp8", "ffpa_check_fp8_ar
            "ffpa_check_cu_seqlens", "ffpa_fwd_strided", "ffpa_check_strided_args", "LayoutDesc", "ffpa_bwd",
            "ffpa_bwd_workspace_size", "ffpa_bwd_dropout", "ffpa_bwd_mask_grad", "ffpa_bwd_noalloc", "ffpa_dropout_keep", "ffpa_fwd_dropout", "ffpa_check_dropout_args",
            "dropout_keep", "attn_backward", "attn_with_grad", "AttnFunction", "library", "rows_per_block", "kernel_head_dim", "kernel_name", "FFPA_BF16", "FFPA_FP16",
-           "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc"]
+           "MASK_NONE", "MASK_BOOL_U8", "MASK_ADD_F32", "MASK_ADD_BF16", "MASK_ADD_FP16", "MaskDesc",
+           "ffpa_attn_func", "ffpa_attn_varlen_func"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libffpa.so")
@@ -503,6 +504,24 @@ def _attn_dropout(q, k, v, o, out, lse, desc, mask_keep, B, Hq, Hkv, Nq, Nkv, D,
 
 
 # keyword arguments of ffpa_attn_varlen_func that this forward rejects when given a non-default value
+# the page's extension keywords of ffpa_attn_func ("API Reference"): they choose among its NVIDIA
+# implementations; this library has one gfx950 path
+_BACKEND_KWARGS = ("backend", "forward_backend", "backward_backend")
+
+
+def ffpa_attn_func(query, key, value, attn_mask=None, dropout_p: float = 0.0, is_causal: bool = False,
+                   scale: Optional[float] = None, enable_gqa: bool = False, **kwargs):
+    """``attn`` under the name and SDPA-aligned signature of ffpa_attn_func ("API Reference"), for code
+    written against that page: returns O [B, Hq, Nq, D], recorded for autograd when an input requires
+    grad.  The page's backend keywords (backend, forward_backend, backward_backend) are accepted and
+    have no effect; any other keyword raises TypeError, as on the page."""
+    for name in kwargs:
+        if name not in _BACKEND_KWARGS:
+            raise TypeError(f"unexpected keyword argument {name!r}")
+    return attn(query, key, value, attn_mask=attn_mask, dropout_p=dropout_p, is_causal=is_causal, scale=scale,
+                enable_gqa=enable_gqa)
+
+
 _VARLEN_UNSUPPORTED = ("window_size", "softcap", "sink", "attention_mask", "attn_mask", "block_mask", "score_mod",
                        "aux_tensors", "seqused_k", "block_table", "num_splits", "alibi_slopes")
 
@@ -581,6 +600,10 @@ def attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seql
     if st != OK:
         _raise(st)
     return (o, lse) if return_lse else o
+
+
+# ffpa_attn_varlen_func ("API Reference") has attn_varlen's signature
+ffpa_attn_varlen_func = attn_varlen
 
 
 def ffpa_bwd(q, k, v, o, dout, lse, mask: Optional[MaskDesc], dq, dk, dv, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal,

@@ -248,6 +248,20 @@ def test_attn_records_autograd_when_inputs_need_grad():
         ffpa.attn(kb, kb, kb, attn_mask=m, out=torch.empty(1, 2, 4, 64, dtype=torch.bfloat16))
 
 
+def test_pages_function_names():
+    """ffpa_attn_func and ffpa_attn_varlen_func, the names and signatures of the "API Reference" page:
+    the backend keywords are accepted, any other raises TypeError, and the call goes through attn."""
+    import torch
+
+    qb = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ffpa.ffpa_attn_func(qb, qb, qb, acc="f32")
+    with pytest.raises(ValueError, match="same GPU"):  # accepted, then attn's own checks
+        ffpa.ffpa_attn_func(qb, qb, qb, backend="cutedsl", forward_backend=None, backward_backend=None)
+    with pytest.raises(TypeError):  # attn's dtype rule
+        ffpa.ffpa_attn_func(qb.float(), qb.float(), qb.float())
+    assert ffpa.ffpa_attn_varlen_func is ffpa.attn_varlen
+
 def test_varlen_refuses_inputs_that_need_grad():
     import torch
 

@@ -281,3 +281,16 @@ def test_head_dim_sweep_workload(D, dtype):
     o, l = run_gpu(q, k, v)
     rows = W.sample_rows(w.B, w.Hq, w.Nq, seed=w.seed, bucket=512)
     _log(w.name, compare(o, l, q, k, v, rows=rows))
+
+
+def test_pages_function_name_runs_attn():
+    """ffpa_attn_func (the "API Reference" name) gives attn's result bit for bit, backend keywords
+    and all."""
+    import exact_attention_head_amd as ffpa
+
+    q, k, v = _case(1, 4, 2, 100, 130, 512, seed=41)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    want = ffpa.attn(qd, kd, vd, is_causal=True, enable_gqa=True)
+    got = ffpa.ffpa_attn_func(qd, kd, vd, is_causal=True, enable_gqa=True, backend="triton")
+    assert torch.equal(got, want)
