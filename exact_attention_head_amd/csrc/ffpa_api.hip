@@ -58,10 +58,8 @@ int rows_for(int64_t D) {
   }
 }
 
-// Head dim of the kernel that serves tensors of head dim D: the smallest row-kernel head dim at or
-// above D (D a multiple of 8), whose columns past D are padding.  576, 704, 832 and 960 have
-// shared-staging kernels of their own, but the row kernel of the next head dim up runs them 2.5-3x
-// faster even with the padding; their own kernels serve only dropout (own_kernel_dim).  0 if none.
+// Head dim of the kernel that serves tensors of head dim D: the smallest compiled head dim at or
+// above D (D a multiple of 8), whose columns past D are padding.  0 if none.
 int64_t kernel_dim(int64_t D) {
   if (D < 8 || D % 8 != 0) return 0;
   int64_t best = 0;
@@ -71,10 +69,6 @@ int64_t kernel_dim(int64_t D) {
 #undef FFPA_PAD_CASE
   return best;
 }
-
-// The kernel compiled for D itself (dropout runs on the contiguous layout only, so it takes no
-// padding), 0 if none.
-int64_t own_kernel_dim(int64_t D) { return rows_for(D) > 0 ? D : 0; }
 
 // Elements from a tensor's first element to one past its last: (B-1)*sb + (H-1)*sh + (N-1)*sn + D.
 // (in 128-bit arithmetic: caller strides may be as large as int64_t allows)
@@ -259,7 +253,7 @@ int check_varlen(const void* q, const void* k, const void* v, const int32_t* cu_
   return FFPA_OK;
 }
 
-// Launches the kernel compiled for head dim kd (the caller's choice: kernel_dim or own_kernel_dim).
+// Launches the kernel compiled for head dim kd (kernel_dim of the tensors' head dim).
 template <typename T>
 hipError_t dispatch(int64_t kd, const ffpa::FwdArgs& a, hipStream_t s) {
   switch (kd) {
@@ -346,7 +340,7 @@ static int launch_dense(const void* q, const void* k, const void* v, const ffpa_
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
   const hipStream_t s = (hipStream_t)stream;
-  const int64_t kd = keep != nullptr ? own_kernel_dim(D) : kernel_dim(D);
+  const int64_t kd = kernel_dim(D);
   const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(kd, a, s) : dispatch<ffpa::Fp16>(kd, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FFPA_OK;
@@ -366,11 +360,6 @@ int ffpa_check_dropout_args(const void* q, const void* k, const void* v, const f
   const int st = check(q, k, v, mask, o, lse, B, Hq, Hkv, Nq, Nkv, D, scale, is_causal, dtype);
   if (st != FFPA_OK) return st;
   if (!(dropout_p >= 0.f && dropout_p < 1.f)) return fail(FFPA_ERR_VALUE, "dropout probability must lie in [0, 1)");
-  if (own_kernel_dim(D) != D)
-    return fail(FFPA_ERR_UNSUPPORTED, "dropout needs a head dim with a kernel of its own (D %% 64 == 0), not %lld",
-                (long long)D);
-  if (B * Hq * ((Nq + rows_for(D) - 1) / rows_for(D)) > 0x7fffffffLL)  // that kernel's own rows per workgroup
-    return fail(FFPA_ERR_UNSUPPORTED, "too many workgroups");
   if (keep == nullptr || ((uintptr_t)keep & 3)) return fail(FFPA_ERR_VALUE, "keep must be non-null and 4-byte aligned");
   if (B * Hq * Nq * ((Nkv + 31) / 32) >= (1LL << 40)) return fail(FFPA_ERR_UNSUPPORTED, "keep mask too large");
   const size_t kbytes = (size_t)(B * Hq * Nq * ((Nkv + 31) / 32)) * 4;

@@ -108,8 +108,8 @@ struct RowTiling {
   static constexpr int LDS_BYTES = RING + EXCH;  // + MASKB when the mask is staged
 };
 
-// The head dims that run the row kernel: every D with a ring plan and an even number of 32-column
-// steps per wave (576, 704, 832 and 960 keep the shared-staging kernel).
+// The head dims the row kernel compiles: every D with a ring plan and an even number of 32-column
+// steps per wave (576, 704, 832 and 960 run the next of them, padded).
 template <int D>
 constexpr bool use_row_kernel() {
   return RowTiling<D>::OK;
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void ffpa_fwd_row_kernel(FwdArgs a) {
   constexpr bool MASK_U8 = MODE == kRowMaskU8;
   constexpr int MESZ = MASK_U8 ? 1 : 4;  // bytes per staged mask element
   constexpr int MROWB = 32 * MESZ;       // bytes of one row's 32-key block
-  static_assert(!DROP || (!VL && !MASK_LDS), "dropout runs on the contiguous dense layout");
+  static_assert(!DROP || !MASK_LDS, "dropout runs without a staged mask");
   constexpr int LDS_MAIN = RT::LDS_BYTES + (MASK_LDS ? RT::MASKB : 0);
   // the epilogue stages each wave's O block through LDS once the ring is no longer read
   constexpr int LDS_BYTES = LDS_MAIN > 4 * o_stage_bytes<DW>() ? LDS_MAIN : 4 * o_stage_bytes<DW>();

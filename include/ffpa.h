@@ -174,9 +174,9 @@ int ffpa_dropout_keep(uint32_t* keep, int64_t B, int64_t Hq, int64_t Nq, int64_t
  * ffpa_dropout_keep, read only; any bits may be given).  The LSE is that of
  * the logits, as in ffpa_fwd: dropout does not change it.  Tensors are
  * contiguous as in ffpa_fwd; every other argument, rule and error is that of
- * ffpa_fwd, plus FFPA_ERR_VALUE for dropout_p outside [0, 1), a null or
- * misaligned keep, or o / lse overlapping keep, and FFPA_ERR_UNSUPPORTED for
- * a head dim without a kernel of its own (D % 64 != 0).
+ * ffpa_fwd (every head dim of ffpa_fwd included), plus FFPA_ERR_VALUE for
+ * dropout_p outside [0, 1), a null or misaligned keep, or o / lse
+ * overlapping keep.
  */
 int ffpa_fwd_dropout(const void* q, const void* k, const void* v, const ffpa_mask_t* mask, void* o, float* lse,
                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nkv, int64_t D, float scale,
@@ -308,8 +308,7 @@ int ffpa_rows_per_block(int64_t D);
  * ffpa_fwd_strided and ffpa_fwd_varlen: the smallest of 64, 128, 192, 256,
  * 320, 384, 448, 512, 640, 768, 896 and 1024 at or above D (its columns past
  * D are padding: zeros in Q, never stored in O).  576, 704, 832 and 960 thus
- * run 640, 768, 896 and 1024; with dropout (ffpa_fwd_dropout) they run
- * kernels of their own.  0 for an unsupported D.  Host-only. */
+ * run 640, 768, 896 and 1024.  0 for an unsupported D.  Host-only. */
 int64_t ffpa_kernel_head_dim(int64_t D);
 
 /* Name of the GPU kernel that serves head dim D (as profilers list it, without

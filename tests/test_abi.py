@@ -356,13 +356,14 @@ def test_dropout_valid_arguments_pass():
     assert dcheck(p=0.0) == ffpa.OK
     assert dcheck(p=0.999) == ffpa.OK
     assert dcheck(D=576) == ffpa.OK
+    assert dcheck(D=80) == ffpa.OK  # padded head dims take dropout too
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(p=1.0), ffpa.ERR_VALUE), (dict(p=-0.5), ffpa.ERR_VALUE), (dict(p=float("nan")), ffpa.ERR_VALUE),
     (dict(keep=None), ffpa.ERR_VALUE), (dict(keep=KEEP + 2), ffpa.ERR_VALUE),
     (dict(keep=O), ffpa.ERR_VALUE),            # o overlaps the keep words
-    (dict(dtype=5), ffpa.ERR_TYPE), (dict(D=80), ffpa.ERR_UNSUPPORTED), (dict(Hkv=3), ffpa.ERR_VALUE),
+    (dict(dtype=5), ffpa.ERR_TYPE), (dict(D=100), ffpa.ERR_UNSUPPORTED), (dict(Hkv=3), ffpa.ERR_VALUE),
 ])
 def test_dropout_argument_errors(kw, status):
     assert dcheck(**kw) == status

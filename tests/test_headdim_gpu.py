@@ -124,9 +124,3 @@ def test_padded_in_bounds_and_deterministic(D):
     assert torch.isnan(big[:pad].float()).all() and torch.isnan(big[pad + n:].float()).all(), "O guard band written"
     assert (lbig[:pad] == 12345.0).all() and (lbig[pad + B * Hq * Nq:] == 12345.0).all(), "LSE guard band written"
     _log(f"guard D={D}", compare(o.cpu(), lse.cpu(), q.cpu(), k.cpu(), v.cpu()))
-
-
-def test_padded_dropout_is_refused():
-    q, k, v = (t.cuda() for t in W.random_qkv(1, 1, 1, 64, 64, 80, seed=1))
-    with pytest.raises(NotImplementedError):
-        ffpa.attn(q, k, v, dropout_p=0.1)
