@@ -253,10 +253,9 @@ int check_varlen(const void* q, const void* k, const void* v, const int32_t* cu_
   return FFPA_OK;
 }
 
-// Launches the kernel compiled for head dim kd (kernel_dim of the tensors' head dim).
 template <typename T>
-hipError_t dispatch(int64_t kd, const ffpa::FwdArgs& a, hipStream_t s) {
-  switch (kd) {
+hipError_t dispatch(int64_t D, const ffpa::FwdArgs& a, hipStream_t s) {
+  switch (kernel_dim(D)) {
 #define FFPA_DISPATCH_CASE(Dv) \
   case Dv: return ffpa::launch_fwd<T, Dv>(a, s);
     FFPA_FOR_EACH_D(FFPA_DISPATCH_CASE)
@@ -340,8 +339,7 @@ static int launch_dense(const void* q, const void* k, const void* v, const ffpa_
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = is_causal;
   const hipStream_t s = (hipStream_t)stream;
-  const int64_t kd = kernel_dim(D);
-  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(kd, a, s) : dispatch<ffpa::Fp16>(kd, a, s);
+  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FFPA_OK;
 }
@@ -437,8 +435,7 @@ int ffpa_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* 
   a.q_sr = a.o_sr = (int)(Hq * D);
   a.kv_sr = (int)(Hkv * D);
   const hipStream_t s = (hipStream_t)stream;
-  const int64_t kd = kernel_dim(D);
-  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(kd, a, s) : dispatch<ffpa::Fp16>(kd, a, s);
+  const hipError_t e = dtype == FFPA_BF16 ? dispatch<ffpa::Bf16>(D, a, s) : dispatch<ffpa::Fp16>(D, a, s);
   if (e != hipSuccess) return fail(FFPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FFPA_OK;
 }
