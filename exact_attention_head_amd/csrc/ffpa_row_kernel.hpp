@@ -51,13 +51,16 @@ struct RingPlan {
   int em, ng;
 };
 
-// Epochs shorter than min_em are taken only where no plan with longer ones fits.
-constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes, int min_em = 0) {
+// Lookahead first, up to 32 products (beyond that fewer barriers measured faster: 16-product epochs
+// at D = 256 against 8-product ones with 48 products ahead, 5.6%), then fewer barriers.  Epochs
+// shorter than min_em are taken only where no plan with longer ones fits; none longer than max_em.
+constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes, int min_em = 0, int max_em = 32) {
   RingPlan best{0, 0};
   int best_score = -1;
   const int ems[4] = {32, 16, 8, 4};
   for (int i = 0; i < 4; ++i) {
     const int em = ems[i];
+    if (em > max_em) continue;
     if (em == 4 && best.em != 0) break;  // four-product epochs only where nothing longer fits (D = 64)
     if (em < min_em && best.em != 0) break;
     if (MPT % em != 0) continue;
@@ -69,7 +72,7 @@ constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes, int min_
       const int ne = ng / bi;
       if (ne < 4) continue;
       const int ahead = (ne - 2) * em;  // products of lookahead
-      const int capped = ahead < 48 ? ahead : 48;
+      const int capped = ahead < 32 ? ahead : 32;
       const int score = capped * 16 - MPT / em;  // enough lookahead first, then fewer barriers
       if (score > best_score) {
         best_score = score;
@@ -82,8 +85,9 @@ constexpr RingPlan choose_ring(int GT, int MPT, int DG, int exch_bytes, int min_
 
 // STAGED: the staged-mask variants.  Above D = 512 they take 16-product epochs where a plan has them
 // (D = 1024: half the barriers per tile against 32 products of lookahead instead of 48), which
-// measured 1.4% faster on the fp32-mask cross-attention workload; the other variants keep the plan
-// that fits their registers (16-product epochs spill the general variant at D = 1024).
+// measured 1.4% faster on the fp32-mask cross-attention workload; the other variants there keep
+// 8-product epochs, which fit their registers (16-product ones spill the general variant at
+// D = 1024, and measured no faster on the raw one).
 template <int D, bool STAGED = false>
 struct RowTiling {
   static constexpr int DG = D <= 512 ? 1 : 2;
@@ -96,7 +100,8 @@ struct RowTiling {
   static constexpr int MPT = 8 * NSUB;          // products per wave per tile
   static constexpr int EXCH = DG == 2 ? 4 * 4096 : 0;  // partial-S exchange: [wave][4 KiB]
   static constexpr int MASKB = BR * 128 * 2;            // staged fp32 mask: [block][row][32 keys]
-  static constexpr RingPlan PLAN = choose_ring(GT, MPT, DG, EXCH + MASKB, STAGED && DG == 2 ? 16 : 0);
+  static constexpr RingPlan PLAN =
+      choose_ring(GT, MPT, DG, EXCH + MASKB, STAGED && DG == 2 ? 16 : 0, DG == 2 && !STAGED ? 8 : 32);
   static constexpr int EM = PLAN.em;
   static constexpr int NG = PLAN.ng;
   static constexpr bool OK = PLAN.em != 0 && D % 64 == 0 && NSUB % 2 == 0 && NSUB >= 2;
