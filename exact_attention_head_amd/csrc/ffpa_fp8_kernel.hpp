@@ -77,9 +77,10 @@ struct Fp8Tiling {
   static constexpr int GTW = 4 * NCGW;         // 4 KiB groups per stage of one column group: K, then V
   static constexpr int GT = DG * GTW;          // groups per stage
   static constexpr int RS = DG == 2 ? 1 : (GT <= 4 ? 8 : (GT <= 8 ? 4 : 2));  // stages per turn of the ring
-  // products per epoch: 8 wherever the ring still holds four such epochs, two of them lookahead (every
-  // D but 768), else 4; at D = 1024, 8 (half the barriers) measured 7.5% faster than 4
-  static constexpr int EM = RS * GT / (DG * 4) >= 4 ? 8 : 4;
+  // products per epoch: the longest of 16, 8 and 4 that divides the stage and leaves the ring four
+  // epochs, two of them lookahead (16 at D = 256 and 512, 8 at 128, 384 and 1024, 4 at 768); halving
+  // the barriers measured 2.5% faster at D = 256, 4.5% at 512 and 7.5% at 1024
+  static constexpr int EM = (MPT % 16 == 0 && RS * GT / (DG * 8) >= 4) ? 16 : (RS * GT / (DG * 4) >= 4 ? 8 : 4);
   static constexpr int BIW = EM / 2;           // groups per epoch of one column group
   static constexpr int BI = DG * BIW;          // groups per epoch
   static constexpr int EPT = MPT / EM;         // epochs per stage
